@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise gated delta-rule backward on one MI355X.
+
+One step = one gdr_bwd call over one batch of seeded synthetic inputs already
+resident in HBM: chunk table, per-chunk preparation, both state sweeps and
+the chunk gradients (every step of the hot path). W untimed warmup steps,
+then K timed steps between two device synchronisations, timed with HIP
+events on the stream the kernels run on; the per-kernel times come from
+events recorded at the kernel boundaries inside the same timed steps.
+
+Prints one JSON line. `value` is tokens/s (B*T per second of the whole
+backward). `roofline` reports the dominant kernel against the HBM peak with
+its algorithmic bytes; `cpu_baseline` times the fp64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 / fp16 MFMA, datasheet
+MFMA_FP32_PEAK_TFS = 157.3
+METRIC = "gated-delta-rule bwd tokens/s (B*T) at H=16,K=V=128; % of MFMA/HBM roofline"
+
+
+def per_token_head_costs(w, n_chunks: int, n_seqs: int, tokens: int) -> dict:
+    """Algorithmic bytes and FLOPs of the method, per value token-head.
+
+    bytes: inputs read once + outputs written once + one write and one read of
+    the per-chunk state h in io precision + h0 / dht / dh0 per (sequence, head).
+    FLOPs: 8 K x V products of C rows per chunk (16 C K V), 14 C x C x D
+    products on the lower triangle, C^3 for the triangular inverse and its
+    gradient.
+    """
+    import torch
+    es = 4 if w.io_dtype == torch.float32 else 2
+    K, V, C, H, Hg = w.K, w.V, w.chunk, w.H, w.Hg
+    gbytes = K * 4 if w.gate == "kda" else 4
+    th = tokens * H
+    qk = 2 * K * es * Hg / H
+    inp = qk + 2 * V * es + gbytes + es
+    out = qk + V * es + gbytes + es
+    state = 2 * K * V * es * n_chunks * H / th          # h written once, read once
+    ends = 3 * K * V * 4 * n_seqs * H / th              # h0, dht, dh0
+    f = (C + 1) / (2 * C)
+    flops_chunk = 16 * C * K * V + 2 * C * C * f * (9 * K + 5 * V) + C ** 3
+    flops = flops_chunk * n_chunks * H / th
+    # the chunk-gradient kernel alone: its inputs, outputs and the two states it reads
+    k_bytes = inp + out + state
+    return dict(method_bytes=inp + out + state + ends, io_bytes=inp + out + ends,
+                flops=flops, chunk_bwd_bytes=k_bytes)
+
+
+def cpu_baseline(inp, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle on a bounded head sample of the same workload."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from gdr_workloads import head_subset
+    w = inp["workload"]
+    G = w.H // w.Hg
+    # probe: one q/k head group on the first sequence only gives the per-token cost
+    sub, _ = head_subset(inp, [0])
+    t0 = time.perf_counter()
+    oracle.run(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"], sub["h0"],
+               sub["dht"], sub["cu_seqlens"], inp["scale"], w.gate)
+    t_group = time.perf_counter() - t0
+    threads = oracle.threads()
+    n_groups = w.Hg
+    # groups run in parallel across threads (one task per (sequence, group))
+    est_all = t_group * max(1.0, n_groups * (w.B if not w.varlen else 1) / threads)
+    if est_all <= budget_s:
+        hks = list(range(n_groups))
+    else:
+        k = max(1, int(n_groups * budget_s / est_all))
+        hks = list(range(k))
+    sub, hv = head_subset(inp, hks)
+    t0 = time.perf_counter()
+    oracle.run(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"], sub["h0"],
+               sub["dht"], sub["cu_seqlens"], inp["scale"], w.gate)
+    t = time.perf_counter() - t0
+    frac = len(hv) / w.H
+    tokens = inp["tokens"]
+    return {"value": tokens * frac / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(hv)} of {w.H} value heads, all {tokens} tokens "
+                      f"({t:.1f} s fp64 on the host; value scaled to all heads)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="kda_fixed_h16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the backward shards by sequence / head with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import chunked_gated_delta_gdr_amd as gdr
+    from gdr_workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    tokens = int(inp["cu_seqlens"][-1]) if w.varlen else w.B * w.T
+    inp["tokens"] = tokens
+    dev = torch.device("cuda", 0)
+    t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    lens = (torch.diff(inp["cu_seqlens"]).tolist() if w.varlen else [w.T] * w.B)
+    n_chunks = sum((L + w.chunk - 1) // w.chunk for L in lens)
+    n_seqs = len(lens)
+
+    desc = gdr.make_desc(w.B, w.T, w.H, w.Hg, w.K, w.V, chunk=w.chunk, n_seqs=w.n_seqs,
+                         gate=0 if w.gate == "kda" else 1, io_dtype=w.io_dtype)
+    ws = torch.empty(gdr.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    out = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"]),
+           torch.empty_like(t["g"]), torch.empty_like(t["beta"]),
+           torch.empty_like(t["h0"]))
+
+    def step(events=None):
+        gdr.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], h0=t["h0"], dht=t["dht"],
+                cu_seqlens=t["cu_seqlens"], scale=inp["scale"], chunk_size=w.chunk,
+                workspace=ws, out=out, stage_events=events)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-step stage events (created by one record so their handles exist)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    kernel_ms = {}
+    for si, name in enumerate(gdr.STAGES):
+        kernel_ms[name] = sum(r[si].elapsed_time(r[si + 1]) for r in evs) / args.steps
+
+    costs = per_token_head_costs(w, n_chunks, n_seqs, tokens)
+    th = tokens * w.H
+    k_ms = kernel_ms["chunk_bwd"]
+    k_bytes = costs["chunk_bwd_bytes"] * th
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    fp32 = w.io_dtype == torch.float32
+    step_s = ms * 1e-3
+    res = {
+        "metric": METRIC,
+        "value": tokens / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[w.io_dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "tokens": tokens, "H": w.H, "Hg": w.Hg,
+                   "K": w.K, "V": w.V, "chunk": w.chunk, "sub_chunk": 16, "gate": w.gate,
+                   "n_seqs": n_seqs, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "gdr_chunk_bwd", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "algorithmic_bytes": k_bytes, "ms": k_ms},
+        "step_roofline": {
+            "method_bytes": costs["method_bytes"] * th,
+            "hbm_frac": costs["method_bytes"] * th / step_s / 1e9 / HBM_PEAK_GBS,
+            "io_floor_frac": costs["io_bytes"] * th / step_s / 1e9 / HBM_PEAK_GBS,
+            "flops": costs["flops"] * th,
+            "mfma_frac": costs["flops"] * th / step_s / 1e12 /
+                         (MFMA_FP32_PEAK_TFS if fp32 else MFMA_BF16_PEAK_TFS)},
+        "kernels_ms": kernel_ms,
+        "wall_ms_per_step": t_wall * 1e3 / args.steps,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+"""Python binding of libgdr.so: the MI355X chunkwise gated delta-rule backward.
+
+Argument marshalling only: every step of the backward runs in the HIP kernels
+behind the C ABI (include/gdr.h). torch supplies device memory and the current
+stream. There is no fallback: if the library is missing or the tensors are not
+on a ROCm device, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["bwd", "workspace_bytes", "workspace_offsets", "library_path", "Desc",
+           "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdr.so")
+_lib = None
+
+GATE_PER_CHANNEL, GATE_SCALAR = 0, 1
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+WS_NAMES = ("ctab", "seq_off", "sAqkT", "A", "AT", "w", "wT", "kt", "ktT", "uT", "qsT",
+            "glast", "h", "X", "dh", "T")
+
+
+class GdrError(RuntimeError):
+    pass
+
+
+class Desc(ctypes.Structure):
+    """Mirror of gdr_bwd_desc_t."""
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("H", ctypes.c_int32), ("Hg", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("sub_chunk", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise GdrError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(python -m chunked_gated_delta_gdr_amd.build)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, D = ctypes.c_void_p, ctypes.POINTER(Desc)
+        lib.gdr_bwd_check.restype = ctypes.c_int
+        lib.gdr_bwd_check.argtypes = [D]
+        lib.gdr_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdr_bwd_workspace_bytes.argtypes = [D]
+        lib.gdr_bwd_workspace_offsets.restype = ctypes.c_int
+        lib.gdr_bwd_workspace_offsets.argtypes = [D, ctypes.POINTER(ctypes.c_size_t), ctypes.c_int]
+        lib.gdr_bwd.restype = ctypes.c_int
+        lib.gdr_bwd.argtypes = [D] + [P] * 15 + [P, ctypes.c_size_t, P]
+        lib.gdr_bwd_with_events.restype = ctypes.c_int
+        lib.gdr_bwd_with_events.argtypes = [D] + [P] * 15 + [P, ctypes.c_size_t, P,
+                                                              ctypes.POINTER(ctypes.c_void_p)]
+        lib.gdr_strerror.restype = ctypes.c_char_p
+        lib.gdr_strerror.argtypes = [ctypes.c_int]
+        lib.gdr_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _err(rc: int) -> GdrError:
+    return GdrError(f"gdr error {rc}: {_load().gdr_strerror(rc).decode()}")
+
+
+def make_desc(B, T, H, Hg, K, V, chunk=64, n_seqs=0, gate=GATE_PER_CHANNEL,
+              io_dtype=torch.bfloat16, scale=0.0, sub_chunk=16) -> Desc:
+    return Desc(B=B, T=T, H=H, Hg=Hg, K=K, V=V, chunk=chunk, sub_chunk=sub_chunk,
+                n_seqs=n_seqs, gate=gate, io_dtype=_DTYPES.get(io_dtype, -1)
+                if isinstance(io_dtype, torch.dtype) else int(io_dtype), scale=scale)
+
+
+def check(desc: Desc) -> int:
+    return int(_load().gdr_bwd_check(ctypes.byref(desc)))
+
+
+def workspace_bytes(desc: Desc) -> int:
+    n = int(_load().gdr_bwd_workspace_bytes(ctypes.byref(desc)))
+    if n == 0:
+        raise _err(check(desc))
+    return n
+
+
+def workspace_offsets(desc: Desc) -> dict:
+    arr = (ctypes.c_size_t * (len(WS_NAMES) + 1))()
+    rc = _load().gdr_bwd_workspace_offsets(ctypes.byref(desc), arr, len(WS_NAMES) + 1)
+    if rc != 0:
+        raise _err(rc)
+    out = {n: int(arr[i]) for i, n in enumerate(WS_NAMES)}
+    out["total"] = int(arr[len(WS_NAMES)])
+    return out
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise GdrError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+STAGES = ("chunk_table", "prep", "sweep", "chunk_bwd")
+
+
+def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
+        chunk_size: int = 64, workspace: Optional[torch.Tensor] = None, out=None,
+        stage_events=None):
+    """Backward of the gated delta rule (see include/gdr.h for the definition).
+
+    q, k [B,T,Hg,K]; v, do [B,T,H,V]; beta [B,T,H] (all in one io dtype:
+    float32, bfloat16 or float16); g fp32 [B,T,H,K] (per-channel gate) or
+    [B,T,H] (scalar gate), raw per-token log2 gate; h0, dht fp32 [N,H,K,V] or
+    None; cu_seqlens int32 [N+1] on the device (varlen, B == 1) or None.
+    Returns (dq, dk, dv, dg, db, dh0). ``workspace`` (uint8, at least
+    workspace_bytes) may be passed to avoid an allocation per call; ``out``
+    may hold preallocated outputs in the same order. ``stage_events``: five
+    torch.cuda.Event(enable_timing=True), already recorded once, recorded at
+    the kernel boundaries (see gdr_bwd_with_events).
+    """
+    lib = _load()
+    io = q.dtype
+    if io not in _DTYPES:
+        raise TypeError(f"unsupported io dtype {io}")
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    gate = GATE_PER_CHANNEL if g.dim() == 4 else GATE_SCALAR
+    n_seqs = 0
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.shape[0],))
+        n_seqs = cu_seqlens.shape[0] - 1
+        N = n_seqs
+    _need(q, "q", io, (B, T, Hg, K))
+    _need(k, "k", io, (B, T, Hg, K))
+    _need(v, "v", io, (B, T, H, V))
+    _need(do, "do", io, (B, T, H, V))
+    _need(beta, "beta", io, (B, T, H))
+    _need(g, "g", torch.float32, (B, T, H, K) if gate == GATE_PER_CHANNEL else (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, H, K, V))
+    if dht is not None:
+        _need(dht, "dht", torch.float32, (N, H, K, V))
+    desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
+                     io_dtype=io, scale=float(scale) if scale is not None else 0.0)
+    rc = check(desc)
+    if rc != 0:
+        raise _err(rc)
+    nbytes = workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() < nbytes or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be uint8 with >= {nbytes} bytes")
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dg = torch.empty_like(g)
+        db = torch.empty_like(beta)
+        dh0 = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dg, db, dh0 = out
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(h0), _ptr(do), _ptr(dht), _ptr(cu_seqlens),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0),
+            _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if stage_events is None:
+        rc = lib.gdr_bwd(*args)
+    else:
+        if len(stage_events) != 5 or any(e.cuda_event == 0 for e in stage_events):
+            raise ValueError("stage_events: five created (recorded once) timing events")
+        evs = (ctypes.c_void_p * 5)(*[e.cuda_event for e in stage_events])
+        rc = lib.gdr_bwd_with_events(*args, evs)
+    if rc != 0:
+        raise _err(rc)
+    return dq, dk, dv, dg, db, dh0

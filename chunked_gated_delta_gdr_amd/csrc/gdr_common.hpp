@@ -1,0 +1,195 @@
+// gdr_common.hpp -- device building blocks shared by the gfx950 kernels of the
+// chunkwise gated delta-rule backward: MFMA traits for the three operand types,
+// fragment loads from LDS/global, fp32 <-> io conversions and the kernel
+// parameter block.
+//
+// MFMA lane layouts (gfx950, wave64), checked on the device:
+//   v_mfma_f32_16x16x32_{bf16,f16}: lane l holds A[l%16][8*(l/16) + 0..7] and
+//     B[8*(l/16) + 0..7][l%16]; the f32x4 result holds D[4*(l/16) + 0..3][l%16].
+//   v_mfma_f32_16x16x4_f32: A[l%16][l/16], B[l/16][l%16]; D as above.
+// Both are "16 rows x 16 cols, reduction in steps of 4*KL" with KL = 8 or 1.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+    static constexpr int KL = 8;
+    using frag = bf16x8;
+    using quad = bf16x4;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<_Float16> {
+    static constexpr int KL = 8;
+    using frag = f16x8;
+    using quad = f16x4;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<float> {
+    static constexpr int KL = 1;
+    using frag = float;
+    using quad = f32x4;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename T> constexpr int kstep() { return 4 * Mfma<T>::KL; }
+// Row padding (elements) that keeps 16-row fragment reads bank-conflict free.
+template <typename T> constexpr int pad() { return sizeof(T) == 4 ? 4 : 8; }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Fragment of a matrix stored with the reduction index contiguous: element
+// (i, kk) at p[i*ld + kk]; lane l gets i = i0 + l%16, kk = k0 + KL*(l/16) + [0,KL).
+// Works for LDS and global pointers; needs 16-byte alignment for 16-bit types.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag frag_kc(const T* p, int ld, int i0, int k0) {
+    const int l = lane_id();
+    const T* q = p + (long)(i0 + (l & 15)) * ld + k0 + (l >> 4) * Mfma<T>::KL;
+    return *reinterpret_cast<const typename Mfma<T>::frag*>(q);
+}
+
+// Same fragment of a matrix stored with the reduction index as the row:
+// element (i, kk) at p[kk*ld + i].
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, int i0, int k0) {
+    const int l = lane_id();
+    typename Mfma<T>::frag f;
+    if constexpr (Mfma<T>::KL == 1) {
+        f = p[(long)(k0 + (l >> 4)) * ld + i0 + (l & 15)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < Mfma<T>::KL; ++j)
+            f[j] = p[(long)(k0 + (l >> 4) * Mfma<T>::KL + j) * ld + i0 + (l & 15)];
+    }
+    return f;
+}
+
+// Row-panel product: acc[t] += A[i0..i0+16, 0..KD) * Bt[j0+16t .. +16, 0..KD)^T
+// with both operands stored reduction-contiguous (A[i*lda+kk], Bt[j*ldb+kk]).
+template <typename T, int NT, int KD>
+__device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda, int i0,
+                                          const T* Bt, int ldb, int j0) {
+#pragma unroll
+    for (int k0 = 0; k0 < KD; k0 += kstep<T>()) {
+        auto a = frag_kc(A, lda, i0, k0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0), acc[t]);
+    }
+}
+
+// Same with a run-time reduction length kd (a multiple of kstep<T>()).
+template <typename T, int NT>
+__device__ __forceinline__ void panel_mma_n(f32x4 (&acc)[NT], const T* A, int lda, int i0,
+                                            const T* Bt, int ldb, int j0, int kd) {
+    for (int k0 = 0; k0 < kd; k0 += kstep<T>()) {
+        auto a = frag_kc(A, lda, i0, k0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0), acc[t]);
+    }
+}
+
+// fp32 16x16 tile product on fp32 arrays, reduction length kd (multiple of 4):
+// acc += A[(ai0+i)*lda + ak0 + kk] * B[(bk0+kk)*ldb + bj0 + j].
+__device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* A, int lda, int ai0, int ak0,
+                                          const float* B, int ldb, int bk0, int bj0, int kd) {
+    const int l = lane_id();
+    for (int k = 0; k < kd; k += 4) {
+        float a = A[(ai0 + (l & 15)) * lda + ak0 + k + (l >> 4)];
+        float b = B[(bk0 + k + (l >> 4)) * ldb + bj0 + (l & 15)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row / column of element i (0..3) of an f32x4 accumulator tile held by this lane.
+__device__ __forceinline__ int acc_row(int i) { return 4 * (lane_id() >> 4) + i; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+// Store 4 consecutive values (accumulator rows r..r+3 of one column) to
+// p[0..3] (contiguous), converting to T.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+    } else {
+        typename Mfma<T>::quad v;
+        v[0] = (T)a; v[1] = (T)b; v[2] = (T)c; v[3] = (T)d;
+        *reinterpret_cast<typename Mfma<T>::quad*>(p) = v;
+    }
+}
+
+// 16-byte vector load / store helpers (8 x 16-bit or 4 x fp32).
+struct alignas(16) Vec16 { uint32_t w[4]; };
+__device__ __forceinline__ Vec16 ld16(const void* p) { return *reinterpret_cast<const Vec16*>(p); }
+__device__ __forceinline__ void st16(void* p, Vec16 v) { *reinterpret_cast<Vec16*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Kernel parameters (one struct passed by value to every kernel).
+// ---------------------------------------------------------------------------
+struct ChunkEntry {
+    int tok0;   // flattened token index (b*T + t) of the chunk's first token
+    int len;    // real tokens in the chunk (1..C)
+    int seq;    // sequence index n
+    int pad_;
+};
+
+struct Params {
+    // problem
+    int64_t B, T;
+    int H, Hg, G;        // G = H / Hg
+    int N;               // sequences
+    int nc_max;          // chunk-table capacity (grid size of chunk-parallel kernels)
+    int varlen;
+    float scale;
+    // inputs
+    const void* q; const void* k; const void* v; const float* g; const void* beta;
+    const float* h0; const void* dout; const float* dht; const int* cu;
+    // outputs
+    void* dq; void* dk; void* dv; float* dg; void* db; float* dh0;
+    // workspace
+    ChunkEntry* ctab;    // [nc_max]
+    int* seq_off;        // [N+1] first chunk of each sequence; seq_off[N] = chunk count
+    void* sAqkT;         // [nc][H][C][C]  scale * Aqk^T
+    void* Am;            // [nc][H][C][C]  A = (I + Akk)^-1
+    void* AT;            // [nc][H][C][C]  A^T
+    void* w;             // [nc][H][C][D]  w = A (beta k 2^G)
+    void* wT;            // [nc][H][D][C]
+    void* kt;            // [nc][H][C][D]  k 2^(G_last - G)
+    void* ktT;           // [nc][H][D][C]
+    void* uT;            // [nc][H][D][C]  u = A (beta v), transposed
+    void* qsT;           // [nc][H][D][C]  scale * (q 2^G - Aqk w), transposed
+    float* glast;        // [nc][H][D]     2^G_last
+    void* hbuf;          // [nc][H][D][D]  state before the chunk
+    void* xbuf;          // [nc][H][C][D]  X = u - w h
+    void* dhbuf;         // [nc][H][D][D]  dL/dS at the chunk end
+    void* tbuf;          // [nc][H][C][D]  k~ dh
+};
+
+}  // namespace gdr

@@ -1,0 +1,6 @@
+// Explicit instantiation: io dtype __bf16, chunk 64, K = V = 128, both gate forms.
+#include "gdr_launch.hpp"
+namespace gdr {
+template hipError_t launch_bwd<__bf16, 64, 128, false>(const Params&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_bwd<__bf16, 64, 128, true>(const Params&, hipStream_t, hipEvent_t const*);
+}  // namespace gdr

@@ -1,0 +1,37 @@
+// gdr_launch.hpp -- enqueues the four kernels of one backward pass on a stream.
+#pragma once
+#include "gdr_chunk_bwd.hpp"
+#include "gdr_prep.hpp"
+#include "gdr_sweep.hpp"
+
+namespace gdr {
+
+// ev: NULL, or GDR_STAGE_EVENTS hipEvent_t recorded on `stream` before the
+// first kernel and after each of the four kernels.
+using LaunchFn = hipError_t (*)(const Params&, hipStream_t, hipEvent_t const* ev);
+
+constexpr int kSweepBV = 32;  // V columns of the state per sweep workgroup
+
+template <typename T, int C, int D, bool SCALAR>
+hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
+    auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+    hipError_t e = mark(0);
+    // chunk table (device-side, so varlen needs no host sync)
+    gdr_chunk_table<C><<<dim3(1), dim3(256), 0, stream>>>(p);
+    if (e == hipSuccess) e = mark(1);
+    if (p.nc_max > 0)
+        gdr_prep<T, C, D, SCALAR><<<dim3(p.nc_max, p.H), dim3(64 * (C / 16)), 0, stream>>>(p);
+    if (e == hipSuccess) e = mark(2);
+    gdr_sweep<T, C, D, kSweepBV><<<dim3(2 * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
+    if (e == hipSuccess) e = mark(3);
+    if (p.nc_max > 0)
+        gdr_chunk_bwd<T, C, D, SCALAR><<<dim3(p.nc_max, p.Hg), dim3(64 * (C / 16)), 0, stream>>>(p);
+    if (e == hipSuccess) e = mark(4);
+    const hipError_t le = hipGetLastError();
+    return le != hipSuccess ? le : e;
+}
+
+// Instantiated in gdr_inst_*.hip; looked up by the C ABI.
+LaunchFn find_launcher(int io_dtype, int chunk, int dim, int scalar);
+
+}  // namespace gdr

@@ -1,0 +1,417 @@
+// gdr_prep.hpp -- chunk table and the chunk-parallel preparation kernel.
+//
+// gdr_prep computes, for one (chunk, value head), the WY factors of the chunk
+// form of the gated delta rule and the quantities the two state sweeps need:
+//   G     chunk-local inclusive cumsum of the raw log2 gate (fp32, in LDS only;
+//         the bwd_intra page takes this cumsum as its g input),
+//   Aqk   [r,s] = sum_d q_rd k_sd 2^(G_rd - G_sd),          s <= r,
+//   Akk   [r,s] = beta_r sum_d k_rd k_sd 2^(G_rd - G_sd),    s <  r,
+//   A     = (I + Akk)^-1 (unit lower triangular; the "Ar"/"Ag" factor of the
+//           FlashQLA page's CONSUMER_A steps),
+//   w     = A (beta k 2^G),  u = A (beta v),
+//   k~    = k 2^(G_last - G),  q~ = q 2^G - Aqk w,  2^G_last.
+// Diagonal 16x16 blocks of Aqk/Akk are formed per element, one decay per
+// (r, s, d), as the bwd_intra page's module docstring requires: the decay is
+// a running product of per-token factors 2^g <= 1 along s (never a
+// factorisation inside a diagonal block). Off-diagonal blocks use bf16/fp16
+// MFMA on operands prescaled through the block boundary rho = 16 i of the
+// target row block: q 2^(G_r - G_rho) and k 2^(G_rho - G_s), both exponents
+// <= 0 (the per-block-boundary form of the same page).
+#pragma once
+#include "gdr_common.hpp"
+
+namespace gdr {
+
+// ---------------------------------------------------------------------------
+// Chunk table: one workgroup. seq_off[n] = first global chunk of sequence n,
+// ctab[j] = {first token, length, sequence}. Fixed length: B sequences of T.
+// ---------------------------------------------------------------------------
+template <int C>
+__global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
+    __shared__ int s_scan[256];
+    __shared__ int s_base;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_base = 0;
+    __syncthreads();
+    for (int n0 = 0; n0 < p.N; n0 += 256) {
+        const int n = n0 + tid;
+        int len = 0, tok0 = 0;
+        if (n < p.N) {
+            if (p.varlen) {
+                tok0 = p.cu[n];
+                len = p.cu[n + 1] - p.cu[n];
+            } else {
+                tok0 = (int)(n * p.T);
+                len = (int)p.T;
+            }
+        }
+        const int nch = (len + C - 1) / C;
+        s_scan[tid] = nch;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
+            int v = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += v;
+            __syncthreads();
+        }
+        const int first = s_base + s_scan[tid] - nch;
+        if (n < p.N) {
+            p.seq_off[n] = first;
+            for (int c = 0; c < nch && first + c < p.nc_max; ++c) {
+                ChunkEntry e;
+                e.tok0 = tok0 + c * C;
+                e.len = min(C, len - c * C);
+                e.seq = n;
+                e.pad_ = c;
+                p.ctab[first + c] = e;
+            }
+        }
+        __syncthreads();
+        if (tid == 255) s_base += s_scan[255];
+        __syncthreads();
+    }
+    if (tid == 0) p.seq_off[p.N] = min(s_base, p.nc_max);
+}
+
+// ---------------------------------------------------------------------------
+// LDS plan of gdr_prep (byte offsets), see the phase comments in the kernel.
+// ---------------------------------------------------------------------------
+template <typename T, int C, int D>
+struct PrepLds {
+    static constexpr int NB = C / 16;
+    static constexpr int NT = 64 * NB;
+    static constexpr int LT = D + pad<T>();   // T  [*][D]
+    static constexpr int LC = C + pad<T>();   // T  [*][C]
+    static constexpr int LF = D + 4;          // f32 [*][D]
+    static constexpr int LCF = C + 4;         // f32 [*][C]
+    static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+    static constexpr size_t G_OFF = 0;
+    static constexpr size_t X_OFF = G_OFF + size_t(C) * LF * 4;
+    static constexpr size_t X_BYTES = cmax(cmax(size_t(C) * LF * 4, size_t(C + 16) * LT * sizeof(T)),
+                                           size_t(D) * LC * sizeof(T));
+    static constexpr size_t Q_OFF = X_OFF + X_BYTES;
+    static constexpr size_t K_OFF = Q_OFF + size_t(C) * LT * sizeof(T);
+    static constexpr size_t AQK_OFF = K_OFF + size_t(C) * LT * sizeof(T);
+    static constexpr size_t AKK_OFF = AQK_OFF + size_t(C) * LCF * 4;
+    static constexpr size_t AF_OFF = AKK_OFF + size_t(C) * LCF * 4;
+    static constexpr size_t SCR_OFF = AF_OFF + size_t(C) * LCF * 4;
+    static constexpr size_t BETA_OFF = SCR_OFF + size_t(NB) * 16 * 20 * 4;
+    static constexpr size_t TOTAL = BETA_OFF + size_t(C) * 4;
+    // after the inverse, the q/k region holds A and Aqk as MFMA operands
+    static constexpr size_t AT_OFF = Q_OFF;                                  // T [C][LC]
+    static constexpr size_t AQKT_OFF = Q_OFF + size_t(C) * LC * sizeof(T);   // T [C][LC]
+    static_assert(2 * size_t(C) * LC * sizeof(T) <= 2 * size_t(C) * LT * sizeof(T), "A/Aqk alias");
+    static_assert(TOTAL <= 163840, "LDS budget of gdr_prep");
+};
+
+template <typename T, int C, int D, bool SCALAR>
+__global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
+    using L = PrepLds<T, C, D>;
+    constexpr int NB = L::NB, NT = L::NT, LT = L::LT, LC = L::LC, LF = L::LF, LCF = L::LCF;
+    constexpr int NTD = D / 16;  // column tiles of a [C][D] product
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    float* Gs = reinterpret_cast<float*>(smem + L::G_OFF);
+    float* At = reinterpret_cast<float*>(smem + L::X_OFF);    // phase 1-2: 2^g per token
+    T* Xb = reinterpret_cast<T*>(smem + L::X_OFF);            // later phases
+    T* qL = reinterpret_cast<T*>(smem + L::Q_OFF);
+    T* kL = reinterpret_cast<T*>(smem + L::K_OFF);
+    float* AqkF = reinterpret_cast<float*>(smem + L::AQK_OFF);
+    float* AkkF = reinterpret_cast<float*>(smem + L::AKK_OFF);
+    float* AF = reinterpret_cast<float*>(smem + L::AF_OFF);
+    float* scr = reinterpret_cast<float*>(smem + L::SCR_OFF);
+    float* bs = reinterpret_cast<float*>(smem + L::BETA_OFF);
+
+    const int j = blockIdx.x, h = blockIdx.y;
+    if (j >= p.seq_off[p.N]) return;
+    const ChunkEntry ce = p.ctab[j];
+    const int tok0 = ce.tok0, len = ce.len;
+    const int hk = h / p.G;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const T* q = static_cast<const T*>(p.q);
+    const T* k = static_cast<const T*>(p.k);
+    const T* v = static_cast<const T*>(p.v);
+    const T* beta = static_cast<const T*>(p.beta);
+    const size_t jh = size_t(j) * p.H + h;
+
+    // ---- phase 1: raw gate -> 2^g table and chunk-local cumsum G; q, k, beta ----
+    for (int e = tid; e < C * (D / 4); e += NT) {
+        const int r = e / (D / 4), d0 = (e % (D / 4)) * 4;
+        f32x4 gv = zero4();
+        if (r < len) {
+            if constexpr (SCALAR) {
+                float s = p.g[(size_t)(tok0 + r) * p.H + h];
+                gv = f32x4{s, s, s, s};
+            } else {
+                gv = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + r) * p.H + h) * D + d0);
+            }
+        }
+        *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = gv;
+        *reinterpret_cast<f32x4*>(At + r * LF + d0) =
+            f32x4{fast_exp2(gv[0]), fast_exp2(gv[1]), fast_exp2(gv[2]), fast_exp2(gv[3])};
+    }
+    constexpr int V8 = 16 / sizeof(T);  // elements per 16-byte vector
+    for (int e = tid; e < C * (D / V8); e += NT) {
+        const int r = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        Vec16 qv{}, kv{};
+        if (r < len) {
+            qv = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
+            kv = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
+        }
+        st16(qL + r * LT + d0, qv);
+        st16(kL + r * LT + d0, kv);
+    }
+    for (int r = tid; r < C; r += NT) bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
+    for (int e = tid; e < C * LCF; e += NT) { AqkF[e] = 0.f; AkkF[e] = 0.f; AF[e] = 0.f; }
+    __syncthreads();
+    for (int d = tid; d < D; d += NT) {  // column cumsum
+        float s = 0.f;
+        for (int r = 0; r < C; ++r) { s += Gs[r * LF + d]; Gs[r * LF + d] = s; }
+    }
+    __syncthreads();
+
+    // ---- phase 2: diagonal 16x16 blocks of Aqk / Akk (VALU, per element) ----
+    // lane -> (block m, mirror row pair pr, d-part e8); the pair (16m+pr,
+    // 16m+15-pr) gives every lane 17 (r, s) steps. Partial dot products over
+    // the d-part are summed across the 8 parts with xor shuffles.
+    {
+        constexpr int PW = D / 8;
+        const int m = tid >> 6, pr = (tid & 63) >> 3, e8 = tid & 7, d0 = e8 * PW;
+        float qr[PW], kr[PW], E[PW];
+        int r = 16 * m + pr, s = r;
+        auto load_row = [&](int rr) {
+#pragma unroll
+            for (int i = 0; i < PW; ++i) {
+                qr[i] = to_f32(qL[rr * LT + d0 + i]);
+                kr[i] = to_f32(kL[rr * LT + d0 + i]);
+                E[i] = 1.f;
+            }
+        };
+        load_row(r);
+        for (int it = 0; it < 17; ++it) {
+            if (it == pr + 1) {  // switch to the mirror row
+                r = 16 * m + 15 - pr;
+                s = r;
+                load_row(r);
+            }
+            float pq = 0.f, pk = 0.f;
+#pragma unroll
+            for (int i = 0; i < PW; ++i) {
+                const float t = to_f32(kL[s * LT + d0 + i]) * E[i];
+                pq += qr[i] * t;
+                pk += kr[i] * t;
+            }
+            pq += __shfl_xor(pq, 1); pk += __shfl_xor(pk, 1);
+            pq += __shfl_xor(pq, 2); pk += __shfl_xor(pk, 2);
+            pq += __shfl_xor(pq, 4); pk += __shfl_xor(pk, 4);
+            if (e8 == 0) {
+                AqkF[r * LCF + s] = pq;
+                if (s < r) AkkF[r * LCF + s] = bs[r] * pk;
+            }
+            // E(r, s-1) = E(r, s) * 2^g_s
+#pragma unroll
+            for (int i = 0; i < PW; ++i) E[i] *= At[s * LF + d0 + i];
+            --s;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: off-diagonal blocks through the boundary rho = 16 i (MFMA) ----
+    for (int ib = 1; ib < NB; ++ib) {
+        const int rho = 16 * ib;
+        T* qb = Xb;                 // [16][LT]  q_r 2^(G_r - G_rho), r in block ib
+        T* kqb = Xb + 16 * LT;      // [16][LT]  k_r 2^(G_r - G_rho)
+        T* kb = Xb + 32 * LT;       // [rho][LT] k_s 2^(G_rho - G_s), s < rho
+        for (int e = tid; e < (32 + rho) * D; e += NT) {
+            const int rr = e / D, d = e % D;
+            const float grho = Gs[rho * LF + d];
+            if (rr < 16) {
+                const int r = rho + rr;
+                const float f = fast_exp2(Gs[r * LF + d] - grho);
+                qb[rr * LT + d] = from_f32<T>(to_f32(qL[r * LT + d]) * f);
+            } else if (rr < 32) {
+                const int r = rho + rr - 16;
+                const float f = fast_exp2(Gs[r * LF + d] - grho);
+                kqb[(rr - 16) * LT + d] = from_f32<T>(to_f32(kL[r * LT + d]) * f);
+            } else {
+                const int s = rr - 32;
+                const float f = fast_exp2(grho - Gs[s * LF + d]);
+                kb[s * LT + d] = from_f32<T>(to_f32(kL[s * LT + d]) * f);
+            }
+        }
+        __syncthreads();
+        // tiles: (which in {Aqk, Akk}) x (rho/16 column tiles)
+        const int ntile = 2 * ib;
+        for (int t = w; t < ntile; t += NB) {
+            const int which = t / ib, ct = t % ib;
+            f32x4 acc[1] = {zero4()};
+            panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rho + acc_row(i), s = 16 * ct + acc_col();
+                if (which) AkkF[r * LCF + s] = bs[r] * acc[0][i];
+                else AqkF[r * LCF + s] = acc[0][i];
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: A = (I + Akk)^-1 ----
+    // 4a: diagonal blocks by forward substitution, one column per lane
+    if (tid < C) {
+        const int m = tid >> 4, jj = tid & 15, b0 = 16 * m;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == jj) ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) acc -= AkkF[(b0 + r) * LCF + b0 + s2] * x[s2];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) AF[(b0 + r) * LCF + b0 + jj] = x[r];
+    }
+    __syncthreads();
+    // 4b: block rows: A_ij = -A_ii * sum_{kb=j}^{i-1} L_i,kb A_kb,j  (fp32 MFMA)
+    for (int bi = 1; bi < NB; ++bi) {
+        float* sc = scr + w * 16 * 20;
+        if (w < bi) {
+            const int bj = w;
+            f32x4 acc = zero4();
+            acc = tile_f32(acc, AkkF, LCF, 16 * bi, 16 * bj, AF, LCF, 16 * bj, 16 * bj, 16 * (bi - bj));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[acc_row(i) * 20 + acc_col()] = acc[i];
+        }
+        __syncthreads();
+        if (w < bi) {
+            const int bj = w;
+            f32x4 acc = zero4();
+            acc = tile_f32(acc, AF, LCF, 16 * bi, 16 * bi, sc, 20, 0, 0, 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) AF[(16 * bi + acc_row(i)) * LCF + 16 * bj + acc_col()] = -acc[i];
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 5: A, Aqk to the workspace and into LDS as MFMA operands ----
+    {
+        T* gA = static_cast<T*>(p.Am) + jh * C * C;
+        T* gAT = static_cast<T*>(p.AT) + jh * C * C;
+        T* gSq = static_cast<T*>(p.sAqkT) + jh * C * C;
+        for (int e = tid; e < C * C; e += NT) {
+            const int r = e / C, s = e % C;
+            gA[e] = from_f32<T>(AF[r * LCF + s]);
+            gAT[e] = from_f32<T>(AF[s * LCF + r]);         // AT[r][s] = A[s][r]
+            gSq[e] = from_f32<T>(p.scale * AqkF[s * LCF + r]);
+        }
+    }
+    T* AtL = reinterpret_cast<T*>(smem + L::AT_OFF);     // A   [C][LC]
+    T* AqkL = reinterpret_cast<T*>(smem + L::AQKT_OFF);  // Aqk [C][LC]
+    // q/k in LDS are no longer needed: re-read from global below.
+    for (int e = tid; e < C * C; e += NT) {
+        const int r = e / C, s = e % C;
+        AtL[r * LC + s] = from_f32<T>(AF[r * LCF + s]);
+        AqkL[r * LC + s] = from_f32<T>(AqkF[r * LCF + s]);
+    }
+    // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^)
+    T* khT = Xb;  // [D][LC]
+    for (int e = tid; e < C * (D / V8); e += NT) {
+        const int s = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        Vec16 kv{};
+        if (s < len) kv = ld16(k + ((size_t)(tok0 + s) * p.Hg + hk) * D + d0);
+        const T* kk = reinterpret_cast<const T*>(&kv);
+#pragma unroll
+        for (int i = 0; i < V8; ++i)
+            khT[(d0 + i) * LC + s] = from_f32<T>(bs[s] * to_f32(kk[i]) * fast_exp2(Gs[s * LF + d0 + i]));
+    }
+    __syncthreads();
+
+    // ---- phase 6: w = A k^ (wave w owns rows 16w..16w+15 of every [C][D] product) ----
+    const int r0 = 16 * w;
+    f32x4 acc[NTD];
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
+    panel_mma<T, NTD, C>(acc, AtL, LC, r0, khT, LC, 0);
+    __syncthreads();  // khT is about to be overwritten by w^T
+    {
+        T* gw = static_cast<T*>(p.w) + jh * C * D;
+        T* gwT = static_cast<T*>(p.wT) + jh * D * C;
+        T* wTL = Xb;  // [D][LC]
+#pragma unroll
+        for (int t = 0; t < NTD; ++t) {
+            const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gw[(rb + i) * D + c] = from_f32<T>(acc[t][i]);
+            store4<T>(gwT + c * C + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+            store4<T>(wTL + c * LC + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 7: q~ = q 2^G - Aqk w, stored as scale * q~^T ----
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
+    panel_mma<T, NTD, C>(acc, AqkL, LC, r0, Xb, LC, 0);
+    {
+        T* gq = static_cast<T*>(p.qsT) + jh * D * C;
+#pragma unroll
+        for (int t = 0; t < NTD; ++t) {
+            const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rb + i;
+                const float qv = r < len ? to_f32(q[((size_t)(tok0 + r) * p.Hg + hk) * D + c]) : 0.f;
+                o[i] = p.scale * (qv * fast_exp2(Gs[r * LF + c]) - acc[t][i]);
+            }
+            store4<T>(gq + c * C + rb, o[0], o[1], o[2], o[3]);
+        }
+    }
+    __syncthreads();  // Xb (w^T) -> v^T
+
+    // ---- phase 8: u = A (beta v) ----
+    T* vhT = Xb;  // [D][LC]
+    for (int e = tid; e < C * (D / V8); e += NT) {
+        const int s = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        Vec16 vv{};
+        if (s < len) vv = ld16(v + ((size_t)(tok0 + s) * p.H + h) * D + d0);
+        const T* vp = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+        for (int i = 0; i < V8; ++i) vhT[(d0 + i) * LC + s] = from_f32<T>(bs[s] * to_f32(vp[i]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
+    panel_mma<T, NTD, C>(acc, AtL, LC, r0, vhT, LC, 0);
+    {
+        T* gu = static_cast<T*>(p.uT) + jh * D * C;
+#pragma unroll
+        for (int t = 0; t < NTD; ++t) {
+            const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+            store4<T>(gu + c * C + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        }
+    }
+
+    // ---- phase 9: k~ = k 2^(G_last - G) (row-major and transposed), 2^G_last ----
+    {
+        T* gkt = static_cast<T*>(p.kt) + jh * C * D;
+        T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
+        for (int e = tid; e < C * (D / V8); e += NT) {
+            const int r = e / (D / V8), d0 = (e % (D / V8)) * V8;
+            Vec16 kv{};
+            if (r < len) kv = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
+            const T* kk = reinterpret_cast<const T*>(&kv);
+            Vec16 o;
+            T* op = reinterpret_cast<T*>(&o);
+#pragma unroll
+            for (int i = 0; i < V8; ++i) {
+                const float x = to_f32(kk[i]) * fast_exp2(Gs[(C - 1) * LF + d0 + i] - Gs[r * LF + d0 + i]);
+                op[i] = from_f32<T>(x);
+                gktT[(d0 + i) * C + r] = op[i];
+            }
+            st16(gkt + r * D + d0, o);
+        }
+        for (int d = tid; d < D; d += NT) p.glast[jh * D + d] = fast_exp2(Gs[(C - 1) * LF + d]);
+    }
+}
+
+}  // namespace gdr

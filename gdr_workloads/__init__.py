@@ -17,7 +17,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "varlen_lengths", "scaled"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "varlen_lengths", "scaled", "head_subset"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -141,3 +141,20 @@ def make_inputs(w: Workload, device: Optional[str] = None) -> dict:
             if out[key] is not None:
                 out[key] = out[key].to(device)
     return out
+
+
+def head_subset(inp: dict, hks: list) -> tuple:
+    """Inputs restricted to q/k heads ``hks`` and the value heads of their GQA
+    groups (head h reads q/k head h // (H / Hg)). Returns (inputs, value heads).
+    Every (sequence, head) is independent, so this is an exact sub-problem."""
+    w = inp["workload"]
+    G = w.H // w.Hg
+    hv = [hk * G + j for hk in hks for j in range(G)]
+    out = dict(inp)
+    out["q"] = inp["q"][:, :, hks]
+    out["k"] = inp["k"][:, :, hks]
+    for key in ("v", "do", "beta", "g"):
+        out[key] = inp[key][:, :, hv]
+    out["h0"] = inp["h0"][:, hv]
+    out["dht"] = inp["dht"][:, hv]
+    return out, hv

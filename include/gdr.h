@@ -1,0 +1,165 @@
+/*
+ * gdr.h -- C ABI of the MI355X (gfx950) chunkwise backward pass of gated
+ * delta-rule linear attention.
+ *
+ * The operation. Per sequence n and value head h, tokens t = 1..T_n, the
+ * forward recurrence (the one the "kernel_fun kda bwd_intra" page and the
+ * FlashQLA issue #30 page both take apart chunk by chunk) is
+ *     S_t = (I - beta_t k_t k_t^T) Diag(2^{g_t}) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,          S_0 = h0,
+ * with the gate g_t either per channel (g_t in R^K, the KDA form of the
+ * bwd_intra page) or one scalar per token and head (the GDN form of the
+ * FlashQLA page's fused_bwd.py). Given do = dL/do and dht = dL/dS_T, gdr_bwd
+ * returns dq, dk, dv, dg, db (= dL/dbeta) and dh0 = dL/dS_0. g is the raw
+ * per-token log2 gate (the kernels form its chunk-local cumulative sum
+ * themselves, as the bwd_intra page's inputs assume), and dg is the gradient
+ * with respect to that raw g. Value head h reads q/k head h / (H / Hg) (GQA,
+ * as in fused_bwd.py's head map); dq and dk are summed over each group.
+ *
+ * Conventions shared by every call:
+ *  - All pointers other than the descriptor are DEVICE pointers (HBM),
+ *    contiguous row-major, owned by the caller. The library allocates nothing,
+ *    frees nothing, keeps no pointer after returning, and only enqueues work
+ *    on `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *    Calls return without synchronising the host.
+ *  - Return value: GDR_OK (0) or a negative gdr_status_t. Nothing is printed
+ *    and no C++ exception crosses the ABI. gdr_strerror() describes a code;
+ *    for GDR_EHIP it also holds the HIP error text of the failing call
+ *    (thread-local, until the next failing call on the same host thread).
+ *  - Preconditions that are documented but not checked: g <= 0 elementwise
+ *    (every exp2 argument the kernels form is then <= 0), finite inputs,
+ *    non-overlapping output buffers, cu_seqlens non-decreasing on device.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_EINVAL = -1,        /* bad shape, null required pointer, misaligned buffer */
+    GDR_EUNSUPPORTED = -2,  /* valid but not built: K, V not in {64,128}, K != V, fp32 with K != 64, chunk not in {32,64} */
+    GDR_EWORKSPACE = -3,    /* workspace NULL or smaller than gdr_bwd_workspace_bytes() */
+    GDR_EHIP = -4           /* a HIP launch or query failed */
+} gdr_status_t;
+
+typedef enum {
+    GDR_GATE_PER_CHANNEL = 0, /* KDA: g [B,T,H,K] fp32 */
+    GDR_GATE_SCALAR = 1       /* GDN: g [B,T,H]   fp32 */
+} gdr_gate_t;
+
+typedef enum {
+    GDR_DTYPE_F32 = 0,
+    GDR_DTYPE_BF16 = 1,
+    GDR_DTYPE_F16 = 2
+} gdr_dtype_t;
+
+/*
+ * Problem descriptor (host memory; read during the call only).
+ *   B, T      batch and tokens per sequence; varlen: B == 1 and T = packed total
+ *   H, Hg     value heads and q/k heads, H % Hg == 0
+ *   K, V      key and value head dims; supported: K == V in {64, 128} (64 only for fp32 io)
+ *   chunk     chunk length C in {32, 64} (the chunk of the chunkwise form)
+ *   sub_chunk diagonal sub-block of the intra-chunk gradient; must be 16
+ *   n_seqs    0 = fixed length (B sequences of T tokens);
+ *             > 0 = varlen: cu_seqlens holds n_seqs + 1 offsets, B must be 1
+ *   gate      gdr_gate_t
+ *   io_dtype  gdr_dtype_t of q, k, v, beta, do and of dq, dk, dv, db
+ *   scale     readout scale; <= 0 means K^-0.5
+ */
+typedef struct {
+    int64_t B, T;
+    int32_t H, Hg, K, V;
+    int32_t chunk, sub_chunk;
+    int32_t n_seqs;
+    int32_t gate;
+    int32_t io_dtype;
+    float scale;
+} gdr_bwd_desc_t;
+
+/*
+ * Checks a descriptor without touching the GPU.
+ * Returns GDR_OK, GDR_EINVAL or GDR_EUNSUPPORTED.
+ */
+int gdr_bwd_check(const gdr_bwd_desc_t* d);
+
+/*
+ * Bytes of device workspace gdr_bwd needs for descriptor d (0 if d is invalid).
+ * The workspace holds the per-chunk intermediates of the chunkwise form (the
+ * WY factors, the per-chunk states h_c and state gradients dh_c) and, for
+ * varlen, the chunk table built on the device. Touches no GPU state.
+ */
+size_t gdr_bwd_workspace_bytes(const gdr_bwd_desc_t* d);
+
+/*
+ * The backward pass. Inputs (device, read only):
+ *   q, k        [B,T,Hg,K] io_dtype
+ *   v, do_      [B,T,H,V]  io_dtype
+ *   g           [B,T,H,K] (per channel) or [B,T,H] (scalar) fp32, raw log2 gate
+ *   beta        [B,T,H]    io_dtype
+ *   h0          [N,H,K,V]  fp32 initial states, N = n_seqs or B; NULL = zero
+ *   dht         [N,H,K,V]  fp32 gradient of the final states; NULL = zero
+ *   cu_seqlens  int32 [n_seqs+1] (varlen) or NULL (fixed length)
+ * Outputs (device, fully overwritten, never accumulated into):
+ *   dq, dk      [B,T,Hg,K] io_dtype (fp32 group sum, then one rounding)
+ *   dv          [B,T,H,V]  io_dtype
+ *   dg          same shape as g, fp32 (w.r.t. the raw per-token gate)
+ *   db          [B,T,H]    io_dtype
+ *   dh0         [N,H,K,V]  fp32, always written (zero-state gradient included)
+ * workspace:    device buffer of at least gdr_bwd_workspace_bytes(d) bytes,
+ *               256-byte aligned; contents on entry are ignored.
+ * Every buffer must be 16-byte aligned. Varlen tokens outside
+ * [cu_seqlens[0], cu_seqlens[n_seqs]) are not written.
+ */
+int gdr_bwd(const gdr_bwd_desc_t* d,
+            const void* q, const void* k, const void* v, const float* g,
+            const void* beta, const float* h0, const void* do_, const float* dht,
+            const int32_t* cu_seqlens,
+            void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdr_bwd plus a measurement hook: stage_events is NULL or an array of
+ * GDR_STAGE_EVENTS hipEvent_t (created by the caller, passed as void*) that
+ * are recorded on `stream` before the first kernel and after each of the four
+ * kernels (chunk table, per-chunk preparation, state sweeps, chunk gradients),
+ * so that a caller can time every kernel on the stream it runs on. The events
+ * add no synchronisation. Same arguments, ownership and errors as gdr_bwd.
+ */
+#define GDR_STAGE_EVENTS 5
+int gdr_bwd_with_events(const gdr_bwd_desc_t* d,
+                        const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* h0, const void* do_, const float* dht,
+                        const int32_t* cu_seqlens,
+                        void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* stage_events);
+
+/*
+ * Byte offsets of the workspace regions for descriptor d, in this order:
+ *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A, 4 A^T,
+ *   5 w, 6 w^T, 7 k~, 8 k~^T, 9 u^T, 10 scale*q~^T, 11 2^G_last,
+ *   12 h (state before each chunk), 13 X, 14 dh (state gradient at each
+ *   chunk end), 15 T = k~ dh, 16 = total bytes.
+ * Per-chunk regions are [chunks][H][..] in io_dtype (2^G_last in fp32).
+ * For inspecting intermediates in tests; n must be >= 17.
+ * Returns GDR_OK, GDR_EINVAL or GDR_EUNSUPPORTED. Touches no GPU state.
+ */
+int gdr_bwd_workspace_offsets(const gdr_bwd_desc_t* d, size_t* offsets, int n);
+
+/* Static description of a status code (plus the HIP message for GDR_EHIP). */
+const char* gdr_strerror(int status);
+
+/* Library version as "major.minor.patch". */
+const char* gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

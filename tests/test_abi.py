@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gdr.h declares, and validates descriptors / arguments before touching
+the device (every call below returns from the host-side checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+gdr = pytest.importorskip("chunked_gated_delta_gdr_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdr.library_path()):
+        import chunked_gated_delta_gdr_amd.build as b
+        b.build()
+    return gdr._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gdr_bwd", "gdr_bwd_workspace_bytes", "gdr_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gdr.h but not exported"
+
+
+def test_version_and_strerror(lib):
+    assert lib.gdr_version().decode().count(".") == 2
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.gdr_strerror(code), bytes)
+
+
+def desc(**kw):
+    base = dict(B=2, T=4096, H=16, Hg=16, K=128, V=128, chunk=64, n_seqs=0, gate=0,
+                io_dtype=1, scale=0.0, sub_chunk=16)
+    base.update(kw)
+    return gdr.Desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(H=32, Hg=16, chunk=32, io_dtype=2, gate=1), 0),
+    (dict(K=64, V=64, io_dtype=0, T=256, B=1, H=2, Hg=2), 0),
+    (dict(B=1, T=32768, n_seqs=24), 0),
+    (dict(H=16, Hg=5), -1),
+    (dict(B=0), -1),
+    (dict(T=-1), -1),
+    (dict(gate=2), -1),
+    (dict(io_dtype=7), -1),
+    (dict(n_seqs=3), -1),            # varlen needs B == 1
+    (dict(K=96, V=96), -2),
+    (dict(K=128, V=64), -2),
+    (dict(chunk=16), -2),
+    (dict(sub_chunk=8), -2),
+    (dict(io_dtype=0), -2),          # fp32 io is built for K = 64 only
+])
+def test_check_codes(lib, kw, code):
+    assert gdr.check(desc(**kw)) == code
+
+
+def test_workspace_bytes(lib):
+    d = desc()
+    n = gdr.workspace_bytes(d)
+    offs = gdr.workspace_offsets(d)
+    assert offs["total"] == n
+    order = [offs[k] for k in gdr.WS_NAMES]
+    assert order == sorted(order) and all(o % 256 == 0 for o in order)
+    # the per-chunk states: 128 chunks x 16 heads x 128 x 128 bf16
+    assert offs["X"] - offs["h"] >= 128 * 16 * 128 * 128 * 2
+    assert lib.gdr_bwd_workspace_bytes(ctypes.byref(desc(K=96, V=96))) == 0
+    # varlen capacity: floor(T / C) + n_seqs chunks
+    dv = desc(B=1, T=1000, n_seqs=7)
+    o = gdr.workspace_offsets(dv)
+    assert o["seq_off"] - o["ctab"] >= (1000 // 64 + 7) * 16
+
+
+def _call(lib, d, ptrs=None, ws=None, wsb=0, **over):
+    names = ["q", "k", "v", "g", "beta", "h0", "do", "dht", "cu", "dq", "dk", "dv", "dg", "db", "dh0"]
+    p = {n: ctypes.c_void_p(0x100000 * (i + 1)) for i, n in enumerate(names)}
+    p["h0"] = p["dht"] = p["cu"] = None
+    if ptrs:
+        p.update(ptrs)
+    return lib.gdr_bwd(ctypes.byref(d), *[p[n] for n in names],
+                       ws, ctypes.c_size_t(wsb), None)
+
+
+def test_bwd_argument_errors_before_any_launch(lib):
+    d = desc()
+    need = gdr.workspace_bytes(d)
+    big = ctypes.c_void_p(0x7F0000000000)
+    assert _call(lib, desc(K=96, V=96)) == -2
+    assert _call(lib, d, {"q": None}, big, need) == -1            # null input
+    assert _call(lib, d, {"dg": ctypes.c_void_p(0x100008)}, big, need) == -1  # misaligned
+    assert _call(lib, d, None, None, need) == -3                  # no workspace
+    assert _call(lib, d, None, big, need - 1) == -3               # too small
+    assert _call(lib, d, None, ctypes.c_void_p(0x7F0000000010), need) == -1  # not 256-aligned
+    dvl = desc(B=1, T=1000, n_seqs=4)
+    assert _call(lib, dvl, None, big, gdr.workspace_bytes(dvl)) == -1  # varlen without cu_seqlens
+    assert _call(lib, d, {"cu": ctypes.c_void_p(0x200000)}, big, need) == -1  # cu without varlen

@@ -1,0 +1,176 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (from the method description): per output tensor, max|gpu - ref| /
+max|ref| over real tokens <= 1e-4 for fp32 io and <= 2e-2 for bf16 / fp16 io.
+Small cases compare every element; the full-size workloads run in the launch
+configuration the benchmark times and compare sampled heads (the oracle is
+per (sequence, head), so a head subset is an exact sub-problem).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gdr_workloads import WORKLOADS, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+tu = pytest.importorskip("gdr_testutil")
+
+
+def _check(errs, tol, label=""):
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, f"{label} over tolerance {tol}: {bad} (all: {errs})"
+
+
+KDA16 = WORKLOADS["kda_fixed_h16"]
+GDN = WORKLOADS["gdn_gqa_fp16"]
+VARLEN = WORKLOADS["kda_varlen"]
+TINY = WORKLOADS["tiny_kda_fp32"]
+
+SMALL = {
+    # the tiny workload at its full size
+    "tiny_kda_fp32": TINY,
+    "tiny_fp32_h0_dht": scaled(TINY, T=200, h0_std=0.1, dht_std=0.1),
+    "fp32_gdn_c32_ragged": scaled(TINY, T=150, gate="gdn", chunk=32, h0_std=0.1, dht_std=0.1),
+    "fp32_kda_c32_gqa": scaled(TINY, T=97, H=4, Hg=2, chunk=32, dht_std=0.1, seed=3),
+    # several chunks and a ragged tail at K = V = 128
+    "bf16_kda_ragged": scaled(KDA16, B=2, T=200, H=2, Hg=2, dht_std=0.1),
+    "bf16_kda_gqa": scaled(KDA16, B=1, T=130, H=4, Hg=1, seed=1),
+    "bf16_kda_d64": scaled(KDA16, B=1, T=190, H=3, Hg=3, K=64, V=64, seed=2),
+    "bf16_gdn_c64": scaled(GDN, B=1, T=160, H=2, Hg=1, chunk=64, io_dtype=torch.bfloat16),
+    "f16_gdn_gqa_c32": scaled(GDN, B=2, T=100, H=4, Hg=2),
+    "f16_kda_c32": scaled(KDA16, B=1, T=75, H=2, Hg=2, chunk=32, io_dtype=torch.float16, seed=5),
+    "bf16_varlen": scaled(VARLEN, T=300, H=2, Hg=2, n_seqs=5),
+    "bf16_varlen_many_short": scaled(VARLEN, T=700, H=2, Hg=2, n_seqs=30, seed=7),
+    "f16_gdn_varlen_c32": scaled(GDN, B=1, T=333, H=2, Hg=1, n_seqs=6, seed=9),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_compare(name):
+    w = SMALL[name]
+    _check(tu.parity(w), tu.tolerance(w), name)
+
+
+@pytest.mark.parametrize("with_h0,with_dht", [(False, False), (True, False), (False, True)])
+def test_optional_states(with_h0, with_dht):
+    """h0 / dht passed as NULL behave as zero; dh0 is always written."""
+    w = scaled(KDA16, B=1, T=140, H=2, Hg=2, h0_std=0.2, dht_std=0.2, seed=11)
+    _check(tu.parity(w, with_h0=with_h0, with_dht=with_dht), tu.tolerance(w))
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 63, 64, 65])
+def test_short_sequences(T):
+    """Shorter than one chunk, exactly one, one plus a single token."""
+    w = scaled(KDA16, B=2, T=T, H=2, Hg=2, dht_std=0.1, seed=T)
+    _check(tu.parity(w), tu.tolerance(w), f"T={T}")
+
+
+def test_varlen_lengths_1_to_17():
+    """17 packed sequences of lengths 1, 2, ..., 17 (every partial-chunk size)."""
+    cu = np.cumsum([0] + list(range(1, 18)))
+    w = scaled(VARLEN, T=int(cu[-1]), H=2, Hg=2, n_seqs=9, seed=13)  # 9 x 17 = 153 fits the draw
+    inp = make_inputs(w)
+    inp["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32)
+    gen = torch.Generator().manual_seed(14)
+    inp["h0"] = torch.randn(17, w.H, w.K, w.V, generator=gen) * 0.1
+    inp["dht"] = torch.randn(17, w.H, w.K, w.V, generator=gen) * 0.1
+    gpu = tu.run_gpu(inp)
+    ref = tu.run_oracle(inp)
+    _check(tu.rel_errors(gpu, ref, tu.real_token_mask(inp)), tu.tolerance(w))
+
+
+@pytest.mark.parametrize("beta_val", [0.0, 1.0])
+def test_beta_extremes(beta_val):
+    w = scaled(KDA16, B=1, T=150, H=2, Hg=2, dht_std=0.1, seed=17)
+    inp = make_inputs(w)
+    inp["beta"] = torch.full_like(inp["beta"], beta_val)
+    gpu = tu.run_gpu(inp)
+    ref = tu.run_oracle(inp)
+    errs = tu.rel_errors(gpu, ref)
+    if beta_val == 0.0:  # frozen state: dk = dv = 0 exactly
+        assert gpu["dk"].abs().max() == 0 and gpu["dv"].abs().max() == 0
+        errs.pop("dk"), errs.pop("dv")
+    _check(errs, tu.tolerance(w))
+
+
+def test_large_gates_x16():
+    """Gates x16 (the exponent-law guard arm): decays underflow, nothing overflows."""
+    w = scaled(KDA16, B=1, T=200, H=2, Hg=2, gate_mult=8.0, dht_std=0.1, seed=19)
+    errs = tu.parity(w)
+    _check(errs, tu.tolerance(w))
+
+
+def test_fp32_large_gates_x16():
+    w = scaled(TINY, T=130, gate_mult=8.0, h0_std=0.1, dht_std=0.1, seed=23)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
+def test_stage_states_match_oracle():
+    """Per-chunk states h_c and state gradients dh_{c+1} in the workspace
+    match the oracle's chunk-boundary states."""
+    import chunked_gated_delta_gdr_amd as gdr
+    w = scaled(VARLEN, T=300, H=2, Hg=2, n_seqs=5, dht_std=0.1)
+    inp = make_inputs(w)
+    desc = gdr.make_desc(w.B, w.T, w.H, w.Hg, w.K, w.V, chunk=w.chunk, n_seqs=w.n_seqs,
+                         io_dtype=w.io_dtype)
+    offs = gdr.workspace_offsets(desc)
+    ws = torch.zeros(offs["total"], dtype=torch.uint8, device="cuda")
+    tu.run_gpu(inp, workspace=ws)
+    ref = tu.run_oracle(inp, chunk=w.chunk)
+    nch, D = ref["h_chunks"].shape[0], w.K
+    for name, key in (("h", "h_chunks"), ("dh", "dh_chunks")):
+        raw = ws[offs[name]: offs[name] + nch * w.H * D * D * 2].cpu()
+        got = raw.view(torch.bfloat16).double().numpy().reshape(nch, w.H, D, D)
+        err = np.abs(got - ref[key]).max() / np.abs(ref[key]).max()
+        assert err < 2e-2, f"{name}: {err}"
+
+
+def test_deterministic_and_workspace_reuse():
+    w = scaled(GDN, B=1, T=300, H=4, Hg=2, seed=29)
+    inp = make_inputs(w)
+    import chunked_gated_delta_gdr_amd as gdr
+    desc = gdr.make_desc(w.B, w.T, w.H, w.Hg, w.K, w.V, chunk=w.chunk, gate=1, io_dtype=w.io_dtype)
+    ws = torch.full((gdr.workspace_bytes(desc),), 255, dtype=torch.uint8, device="cuda")
+    a = tu.run_gpu(inp, workspace=ws)
+    b = tu.run_gpu(inp, workspace=ws)
+    for n in tu.OUTS:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_linear_in_output_gradients():
+    """All six gradients are jointly linear in (do, dht): an oracle-free check."""
+    w = scaled(TINY, T=160, h0_std=0.1, dht_std=0.1, seed=31)
+    i1, i2 = make_inputs(w), make_inputs(scaled(w, seed=32))
+    i3 = dict(i1)
+    i3["do"] = 0.5 * i1["do"] - 2.0 * i2["do"]
+    i3["dht"] = 0.5 * i1["dht"] - 2.0 * i2["dht"]
+    i2 = dict(i1, do=i2["do"], dht=i2["dht"])
+    r1, r2, r3 = tu.run_gpu(i1), tu.run_gpu(i2), tu.run_gpu(i3)
+    for n in tu.OUTS:
+        comb = 0.5 * r1[n].double() - 2.0 * r2[n].double()
+        assert (r3[n].double() - comb).abs().max() <= 1e-4 * comb.abs().max(), n
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled heads
+# ---------------------------------------------------------------------------
+
+def test_full_tiny_kda_fp32():
+    _check(tu.parity(TINY), 1e-4)
+
+
+def test_full_kda_fixed_h16():
+    _check(tu.parity(KDA16, hks=[0, 9]), 2e-2)
+
+
+def test_full_gdn_gqa_fp16():
+    _check(tu.parity(GDN, hks=[5]), 2e-2)
+
+
+def test_full_kda_varlen():
+    _check(tu.parity(VARLEN, hks=[3, 12]), 2e-2)
+
+
+def test_full_kda_long():
+    _check(tu.parity(WORKLOADS["kda_long"], hks=[7, 30]), 2e-2)
