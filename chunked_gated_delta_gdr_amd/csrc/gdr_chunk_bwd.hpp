@@ -1,8 +1,10 @@
 // gdr_chunk_bwd.hpp -- chunk-parallel gradient kernel.
 //
 // One workgroup per (chunk, q/k head); it loops over the value heads of the
-// GQA group and sums dq / dk over them in fp32. Wave w owns rows 16w..16w+15
-// (diagonal block w) of every [C][*] product. With h = h_c, dh' = dh_{c+1},
+// GQA group and sums dq / dk over them in fp32. 2 C/16 waves: wave w owns
+// rows 16 (w % NB) .. +16 (diagonal block w % NB) and the column half w / NB
+// of every [C][*] product, which keeps each wave's accumulators small enough
+// for two waves per SIMD. With h = h_c, dh' = dh_{c+1},
 // X = u - w h (forward sweep) and T = k~ dh' (reverse sweep):
 //   dX  = scale Aqk^T do + T
 //   dAqk = scale Lower_incl(do X^T)          (the FlashQLA page's dP step)
@@ -31,7 +33,7 @@ namespace gdr {
 template <typename T, int C, int D>
 struct BwdLds {
     static constexpr int NB = C / 16;
-    static constexpr int BVS = sizeof(T) == 4 ? 16 : 32;  // V slice of the state products
+    static constexpr int BVS = 32;  // V slice of the state products
     static constexpr int LT = D + pad<T>();
     static constexpr int LC = C + pad<T>();
     static constexpr int LB = BVS + pad<T>();
@@ -44,11 +46,11 @@ struct BwdLds {
     static constexpr size_t Q_OFF = 0;
     static constexpr size_t K_OFF = Q_OFF + sz(C, LT, sizeof(T));
     static constexpr size_t BETA_OFF = K_OFF + sz(C, LT, sizeof(T));        // f32 [C]
-    static constexpr size_t DB_OFF = BETA_OFF + C * 4;                       // f32 [C]
-    static constexpr size_t GL_OFF = DB_OFF + C * 4;                         // f32 [D] dG_last
+    static constexpr size_t DB_OFF = BETA_OFF + C * 4;                       // f32 [4][C] db partials
+    static constexpr size_t GL_OFF = DB_OFF + 4 * C * 4;                     // f32 [D] dG_last
     static constexpr size_t GLW_OFF = GL_OFF + D * 4;                        // f32 [NB][D] per-wave dG_last
-    static constexpr size_t BT_OFF = GLW_OFF + size_t(NB) * D * 4;           // f32 [NB][D] block totals
-    static constexpr size_t DIAG_OFF = BT_OFF + size_t(NB) * D * 4;          // f32 [2][NB][16][16]
+    static constexpr size_t BT_OFF = GLW_OFF + size_t(NB) * D * 4;           // f32 [NB][D] block totals + [2][C]
+    static constexpr size_t DIAG_OFF = BT_OFF + (size_t(NB) * D + 2 * C) * 4; // f32 [2][NB][16][16]
     static constexpr size_t U_OFF = DIAG_OFF + size_t(2) * NB * 256 * 4;     // union region
     // phase 1 (state products, one V slice)
     static constexpr size_t P1_DOT = 0;                                      // T [BVS][LC]
@@ -96,8 +98,8 @@ struct BwdLds {
 // Fragment of rows [i0, i0+16) of a global token-major matrix: element
 // (i, kk) at p[i*ld + kk]; rows >= nrows (past the sequence end) read as zero.
 template <typename T>
-__device__ __forceinline__ typename Mfma<T>::frag frag_rows(const T* p, long ld, int i0, int k0, int nrows) {
-    const int l = lane_id();
+__device__ __forceinline__ typename Mfma<T>::frag frag_rows(const T* p, long ld, int i0, int k0, int nrows,
+                                                            int l = lane_id()) {
     const int i = i0 + (l & 15);
     typename Mfma<T>::frag f;
     if (i < nrows) {
@@ -112,31 +114,35 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_rows(const T* p, long ld,
     return f;
 }
 
-template <typename T, int C, int D, bool SCALAR>
-__global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
+template <typename T, int C, int D, bool SCALAR, bool GROUPED>
+__global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     using L = BwdLds<T, C, D>;
-    constexpr int NB = L::NB, NT = 64 * NB, BVS = L::BVS;
+    constexpr int NB = L::NB, NW = 2 * NB, NT = 64 * NW, BVS = L::BVS;
     constexpr int LT = L::LT, LC = L::LC, LB = L::LB, LF = L::LF;
-    constexpr int NTD = D / 16, NTC = C / 16, NTV = BVS / 16;
+    constexpr int DH2 = D / 2, CH2 = C / 2, VH2 = BVS / 2;    // column halves
+    constexpr int NTD = DH2 / 16, NTC = CH2 / 16, NTV = VH2 / 16;
     constexpr int V8 = 16 / sizeof(T);
+    static_assert(NTD >= 1 && NTC >= 1 && NTV >= 1 && D <= NT, "tiling");
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    T* qL = reinterpret_cast<T*>(smem + L::Q_OFF);
-    T* kL = reinterpret_cast<T*>(smem + L::K_OFF);
+    T* const qL0 = reinterpret_cast<T*>(smem + L::Q_OFF);
+    T* const kL0 = reinterpret_cast<T*>(smem + L::K_OFF);
     float* bs = reinterpret_cast<float*>(smem + L::BETA_OFF);
-    float* dbS = reinterpret_cast<float*>(smem + L::DB_OFF);
+    float* dbS = reinterpret_cast<float*>(smem + L::DB_OFF);     // [4][C]: MFMA halves, diagonal halves
     float* dGl = reinterpret_cast<float*>(smem + L::GL_OFF);
     float* dGlw = reinterpret_cast<float*>(smem + L::GLW_OFF);
     float* btot = reinterpret_cast<float*>(smem + L::BT_OFF);
     float* dqD = reinterpret_cast<float*>(smem + L::DIAG_OFF);   // [NB][16 s][16 r] dAqk
     float* dkD = dqD + NB * 256;                                   // [NB][16 s][16 r] dAkk
-    char* U = smem + L::U_OFF;
+    char* const U0 = smem + L::U_OFF;
 
     const int j = blockIdx.x, hk = blockIdx.y;
     if (j >= p.seq_off[p.N]) return;
     const ChunkEntry ce = p.ctab[j];
     const int tok0 = ce.tok0, len = ce.len;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-    const int r0 = 16 * w;  // this wave's rows
+    const int rb = w % NB, ch = w / NB;
+    const int r0 = 16 * rb;                   // this wave's rows
+    const int cd0 = ch * DH2, cc0 = ch * CH2, cv0 = ch * VH2;  // its column halves
     const T* q = static_cast<const T*>(p.q);
     const T* k = static_cast<const T*>(p.k);
     const T* v = static_cast<const T*>(p.v);
@@ -151,20 +157,29 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             qv = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
             kv = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
         }
-        st16(qL + r * LT + d0, qv);
-        st16(kL + r * LT + d0, kv);
+        st16(qL0 + r * LT + d0, qv);
+        st16(kL0 + r * LT + d0, kv);
     }
 
-    // fp32 group sums of dq, dk in the diagonal pass layout: lane owns
-    // columns d = l + 64 cc, all 16 rows of block w
-    constexpr int NCOL = D / 64;
-    float dq_tot[NCOL][16], dk_tot[NCOL][16];
+    // diagonal-pass layout: lane owns column dcol (when lane < D/2) and the
+    // 16 rows of block rb; GROUPED keeps fp32 group sums of dq, dk there
+    const bool colact = l < DH2;
+    const int dcol = cd0 + (colact ? l : 0);
+    float dq_tot[GROUPED ? 16 : 1], dk_tot[GROUPED ? 16 : 1];
+    if constexpr (GROUPED) {
 #pragma unroll
-    for (int cc = 0; cc < NCOL; ++cc)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { dq_tot[cc][r] = 0.f; dk_tot[cc][r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { dq_tot[r] = 0.f; dk_tot[r] = 0.f; }
+    }
 
-    for (int gi = 0; gi < p.G; ++gi) {
+    // One value head per call of `head`. With G == 1 there is no loop at all:
+    // a loop around this body lets the compiler hoist the (lane-dependent)
+    // address arithmetic of every unrolled LDS access out of it and keep it
+    // live across iterations, which costs hundreds of registers.
+    auto head = [&](const int gi) __attribute__((always_inline)) {
+        const int l = opaque_lane_id();  // fresh per head: see above
+        char* U = U0;
+        T* qL = qL0;
+        T* kL = kL0;
         const int h = hk * p.G + gi;
         const size_t jh = (size_t)j * p.H + h;
         const T* AT = static_cast<const T*>(p.AT) + jh * C * C;
@@ -178,11 +193,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
         const long ldo = (long)p.H * D;
 
         __syncthreads();  // previous head's LDS use is over
-        for (int r = tid; r < C; r += NT) {
-            bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
-            dbS[r] = 0.f;
-        }
-        for (int d = tid; d < D; d += NT) dGl[d] = 0.f;
+        for (int r = tid; r < C; r += NT) bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
 
         // ================= phase 1: state products over V slices =================
         f32x4 dqh[NTD], dkt_[NTD], dwP[NTD], dAq[NTC], dAp[NTC];
@@ -190,8 +201,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
         for (int t = 0; t < NTD; ++t) { dqh[t] = zero4(); dkt_[t] = zero4(); dwP[t] = zero4(); }
 #pragma unroll
         for (int t = 0; t < NTC; ++t) { dAq[t] = zero4(); dAp[t] = zero4(); }
-        float dbp[4] = {0.f, 0.f, 0.f, 0.f};   // partial db of rows r0 + acc_row(i)
-        float hdh = 0.f;                        // partial rowsum(h dh') of column tid % D
+        float dbp[4] = {0.f, 0.f, 0.f, 0.f};   // partial db of rows r0 + acc_row(i, l)
+        float hdh = 0.f;                        // partial rowsum(h dh') of column tid
 
         T* doT = reinterpret_cast<T*>(U + L::P1_DOT);
         T* XL = reinterpret_cast<T*>(U + L::P1_XL);
@@ -223,69 +234,66 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 st16(dhL + d * LB + c, ld16(dhb + (size_t)d * D + v0 + c));
             }
             __syncthreads();
-            // dX = T + sAqkT do  (own rows, [16][BVS])
+            // dX = T + sAqkT do  (own rows, own half of the slice)
             f32x4 dX[NTV];
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dX[t][i] = to_f32(tb[(size_t)(r0 + acc_row(i)) * D + v0 + 16 * t + acc_col()]);
+                    dX[t][i] = to_f32(tb[(size_t)(r0 + acc_row(i, l)) * D + v0 + cv0 + 16 * t + acc_col(l)]);
             }
-            panel_mma<T, NTV, C>(dX, sAqkT, C, r0, doT, LC, 0);
+            panel_mma<T, NTV, C>(dX, sAqkT, C, r0, doT, LC, cv0, l);
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
-                const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+                const int c = cv0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dXL[(rb + i) * LB + c] = from_f32<T>(dX[t][i]);
-                store4<T>(dXT + c * LC + rb, dX[t][0], dX[t][1], dX[t][2], dX[t][3]);
+                for (int i = 0; i < 4; ++i) dXL[(rr + i) * LB + c] = from_f32<T>(dX[t][i]);
+                store4<T>(dXT + c * LC + rr, dX[t][0], dX[t][1], dX[t][2], dX[t][3]);
             }
-            // rowsum(h dh') over this slice, column d = tid % D
-            for (int d = tid; d < D; d += NT) {
-                float s = 0.f;
+            // rowsum(h dh') over this slice, column d = tid
+            if (tid < D) {
+                float s2 = 0.f;
 #pragma unroll 8
-                for (int c = 0; c < BVS; ++c) s += to_f32(hL[d * LB + c]) * to_f32(dhL[d * LB + c]);
-                hdh += s;
+                for (int c = 0; c < BVS; ++c) s2 += to_f32(hL[tid * LB + c]) * to_f32(dhL[tid * LB + c]);
+                hdh += s2;
             }
             __syncthreads();
 #pragma unroll
             for (int k0 = 0; k0 < BVS; k0 += kstep<T>()) {
-                const auto a_do = frag_rows(dorow, ldo, r0, v0 + k0, len);
-                const auto a_x = frag_kc(xb + v0, D, r0, k0);
-                const auto a_dx = frag_kc(dXL, LB, r0, k0);
+                const auto a_do = frag_rows(dorow, ldo, r0, v0 + k0, len, l);
+                const auto a_x = frag_kc(xb + v0, D, r0, k0, l);
+                const auto a_dx = frag_kc(dXL, LB, r0, k0, l);
 #pragma unroll
                 for (int t = 0; t < NTC; ++t) {
-                    dAq[t] = Mfma<T>::mma(a_do, frag_kc(XL, LB, 16 * t, k0), dAq[t]);
-                    dAp[t] = Mfma<T>::mma(a_dx, frag_kc(vL, LB, 16 * t, k0), dAp[t]);
+                    dAq[t] = Mfma<T>::mma(a_do, frag_kc(XL, LB, cc0 + 16 * t, k0, l), dAq[t]);
+                    dAp[t] = Mfma<T>::mma(a_dx, frag_kc(vL, LB, cc0 + 16 * t, k0, l), dAp[t]);
                 }
 #pragma unroll
                 for (int t = 0; t < NTD; ++t) {
-                    const auto bh = frag_kc(hL, LB, 16 * t, k0);
+                    const auto bh = frag_kc(hL, LB, cd0 + 16 * t, k0, l);
                     dqh[t] = Mfma<T>::mma(a_do, bh, dqh[t]);
                     dwP[t] = Mfma<T>::mma(a_dx, bh, dwP[t]);
-                    dkt_[t] = Mfma<T>::mma(a_x, frag_kc(dhL, LB, 16 * t, k0), dkt_[t]);
+                    dkt_[t] = Mfma<T>::mma(a_x, frag_kc(dhL, LB, cd0 + 16 * t, k0, l), dkt_[t]);
                 }
             }
             // dv^ = A^T dX; dv = beta dv^; db += rowsum(dv^ v)
             f32x4 dvh[NTV];
 #pragma unroll
             for (int t = 0; t < NTV; ++t) dvh[t] = zero4();
-            panel_mma<T, NTV, C>(dvh, AT, C, r0, dXT, LC, 0);
+            panel_mma<T, NTV, C>(dvh, AT, C, r0, dXT, LC, cv0, l);
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
-                const int c = 16 * t + acc_col();
+                const int c = cv0 + 16 * t + acc_col(l);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + acc_row(i);
+                    const int r = r0 + acc_row(i, l);
                     dbp[i] += dvh[t][i] * to_f32(vL[r * LB + c]);
                     if (r < len) dvout[(size_t)r * ldo + v0 + c] = from_f32<T>(bs[r] * dvh[t][i]);
                 }
             }
         }
         // dG_last, part 1: ln2 2^G_last rowsum_v(h dh')  (glast of this chunk)
-        {
-            const float* gl = p.glast + jh * D;
-            for (int d = tid; d < D; d += NT) dGl[d] = kLn2 * gl[d] * hdh;
-        }
+        if (tid < D) dGl[tid] = kLn2 * p.glast[jh * D + tid] * hdh;
         __syncthreads();  // phase-1 LDS is dead from here
 
         // ================= phase 2 =================
@@ -295,8 +303,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             f32x4 gv = zero4();
             if (r < len) {
                 if constexpr (SCALAR) {
-                    const float s = p.g[(size_t)(tok0 + r) * p.H + h];
-                    gv = f32x4{s, s, s, s};
+                    const float s2 = p.g[(size_t)(tok0 + r) * p.H + h];
+                    gv = f32x4{s2, s2, s2, s2};
                 } else {
                     gv = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + r) * p.H + h) * D + d0);
                 }
@@ -304,9 +312,9 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = gv;
         }
         __syncthreads();
-        for (int d = tid; d < D; d += NT) {
-            float s = 0.f;
-            for (int r = 0; r < C; ++r) { s += Gs[r * LF + d]; Gs[r * LF + d] = s; }
+        if (tid < D) {
+            float s2 = 0.f;
+            for (int r = 0; r < C; ++r) { s2 += Gs[r * LF + tid]; Gs[r * LF + tid] = s2; }
         }
         __syncthreads();
 
@@ -317,12 +325,12 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
         f32x4 Pq[NTD], Pk[NTD], PG[NTD];
 #pragma unroll
         for (int t = 0; t < NTD; ++t) {
-            const int c = 16 * t + acc_col();
+            const int c = cd0 + 16 * t + acc_col(l);
             const float gls = Gs[(C - 1) * LF + c];
             float colk = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = r0 + acc_row(i);
+                const int r = r0 + acc_row(i, l);
                 const float G = Gs[r * LF + c];
                 const float dqi = p.scale * dqh[t][i] * fast_exp2(G);
                 const float dki = dkt_[t][i] * fast_exp2(gls - G);
@@ -335,11 +343,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             // sum over the 16 rows of this wave (4 in-lane, 4 lane groups)
             colk += __shfl_xor(colk, 16);
             colk += __shfl_xor(colk, 32);
-            if (l < 16) dGlw[w * D + c] = kLn2 * colk;  // summed in wave order later
-            const int rb = r0 + acc_row(0);
-            store4<T>(dwT + c * LC + rb, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
+            if (l < 16) dGlw[rb * D + c] = kLn2 * colk;  // summed in block order later
+            const int rr = r0 + acc_row(0, l);
+            store4<T>(dwT + c * LC + rr, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dwL[(rb + i) * LT + c] = from_f32<T>(-dwP[t][i]);
+            for (int i = 0; i < 4; ++i) dwL[(rr + i) * LT + c] = from_f32<T>(-dwP[t][i]);
         }
         for (int e = tid; e < C * D; e += NT) {
             const int r = e / D, d = e % D;
@@ -351,40 +359,41 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             f32x4 dkh[NTD];
 #pragma unroll
             for (int t = 0; t < NTD; ++t) dkh[t] = zero4();
-            panel_mma<T, NTD, C>(dkh, AT, C, r0, dwT, LC, 0);
+            panel_mma<T, NTD, C>(dkh, AT, C, r0, dwT, LC, cd0, l);
 #pragma unroll
             for (int t = 0; t < NTD; ++t) {
-                const int c = 16 * t + acc_col();
+                const int c = cd0 + 16 * t + acc_col(l);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + acc_row(i);
-                    const float kgv = to_f32(kL[r * LT + c]) * fast_exp2(Gs[r * LF + c]);
-                    Pk[t][i] += bs[r] * fast_exp2(Gs[r * LF + c]) * dkh[t][i];
+                    const int r = r0 + acc_row(i, l);
+                    const float gam = fast_exp2(Gs[r * LF + c]);
+                    const float kgv = to_f32(kL[r * LT + c]) * gam;
+                    Pk[t][i] += bs[r] * gam * dkh[t][i];
                     PG[t][i] += kLn2 * bs[r] * kgv * dkh[t][i];
                     dbp[i] += dkh[t][i] * kgv;
                 }
             }
         }
-        panel_mma<T, NTC, D>(dAp, dwL, LT, r0, kgL, LT, 0);
+        panel_mma<T, NTC, D>(dAp, dwL, LT, r0, kgL, LT, cc0, l);
         // dA = dA' Diag(beta); T1 = dA A^T
         T* dAL = reinterpret_cast<T*>(U + L::P2_DAL);
         T* T1T = reinterpret_cast<T*>(U + L::P2_T1T);
 #pragma unroll
         for (int t = 0; t < NTC; ++t) {
-            const int c = 16 * t + acc_col();
+            const int c = cc0 + 16 * t + acc_col(l);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dAL[(r0 + acc_row(i)) * LC + c] = from_f32<T>(dAp[t][i] * bs[c]);
+            for (int i = 0; i < 4; ++i) dAL[(r0 + acc_row(i, l)) * LC + c] = from_f32<T>(dAp[t][i] * bs[c]);
         }
         __syncthreads();
         {
             f32x4 t1[NTC];
 #pragma unroll
             for (int t = 0; t < NTC; ++t) t1[t] = zero4();
-            panel_mma<T, NTC, C>(t1, dAL, LC, r0, Am, C, 0);
+            panel_mma<T, NTC, C>(t1, dAL, LC, r0, Am, C, cc0, l);
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
-                const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
-                store4<T>(T1T + c * LC + rb, t1[t][0], t1[t][1], t1[t][2], t1[t][3]);
+                const int c = cc0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
+                store4<T>(T1T + c * LC + rr, t1[t][0], t1[t][1], t1[t][2], t1[t][3]);
             }
         }
         __syncthreads();
@@ -397,30 +406,32 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             f32x4 dAk[NTC];
 #pragma unroll
             for (int t = 0; t < NTC; ++t) dAk[t] = zero4();
-            panel_mma<T, NTC, C>(dAk, AT, C, r0, T1T, LC, 0);
+            panel_mma<T, NTC, C>(dAk, AT, C, r0, T1T, LC, cc0, l);
+            __syncthreads();  // T1T reads done before the dA operands overwrite dead buffers
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
-                const int s = 16 * t + acc_col(), rb = r0 + acc_row(0);
+                const int s = cc0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
                 float aq[4], ak[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = rb + i;
+                    const int r = rr + i;
                     aq[i] = s <= r ? p.scale * dAq[t][i] : 0.f;
                     ak[i] = s < r ? -dAk[t][i] : 0.f;
                     dAqL[r * LC + s] = from_f32<T>(aq[i]);
                     dAkL[r * LC + s] = from_f32<T>(ak[i]);
-                    if (t == w) {  // diagonal block, fp32 for the VALU pass: [s][r]
-                        dqD[w * 256 + (s - r0) * 16 + (r - r0)] = aq[i];
-                        dkD[w * 256 + (s - r0) * 16 + (r - r0)] = ak[i];
+                    if (s >= r0 && s < r0 + 16) {  // diagonal block, fp32 for the VALU pass: [s][r]
+                        dqD[rb * 256 + (s - r0) * 16 + (r - r0)] = aq[i];
+                        dkD[rb * 256 + (s - r0) * 16 + (r - r0)] = ak[i];
                     }
                 }
-                store4<T>(dAqT + s * LC + rb, aq[0], aq[1], aq[2], aq[3]);
-                store4<T>(dAkT + s * LC + rb, ak[0], ak[1], ak[2], ak[3]);
+                store4<T>(dAqT + s * LC + rr, aq[0], aq[1], aq[2], aq[3]);
+                store4<T>(dAkT + s * LC + rr, ak[0], ak[1], ak[2], ak[3]);
             }
         }
         __syncthreads();
 
-        // 2f: cross-block terms through each boundary rho = 16 ib, DH columns at a time
+        // 2f: cross-block terms through each boundary rho = 16 ib, DH columns
+        // at a time (the waves of the matching column half do the MFMA work)
         constexpr int NTH = L::DH / 16;
         for (int ib = 1; ib < NB; ++ib) {
             const int rho = 16 * ib;
@@ -433,10 +444,10 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
             T* kbbT = qbT + L::DH * lkc;                  // [DH][lkc]  beta_r k_r 2^(G_r - G_rho)
             for (int dh0 = 0; dh0 < D; dh0 += L::DH) {
                 for (int e = tid; e < L::DH * kbn; e += NT) {
-                    const int dd = e / kbn, s = e % kbn, d = dh0 + dd;
+                    const int dd = e / kbn, s2 = e % kbn, d = dh0 + dd;
                     float x = 0.f;
-                    if (s < rho) x = to_f32(kL[s * LT + d]) * fast_exp2(Gs[rho * LF + d] - Gs[s * LF + d]);
-                    kbT[dd * lkb + s] = from_f32<T>(x);
+                    if (s2 < rho) x = to_f32(kL[s2 * LT + d]) * fast_exp2(Gs[rho * LF + d] - Gs[s2 * LF + d]);
+                    kbT[dd * lkb + s2] = from_f32<T>(x);
                 }
                 for (int e = tid; e < L::DH * kcn; e += NT) {
                     const int dd = e / kcn, rr = e % kcn, r = kcb + rr, d = dh0 + dd;
@@ -450,72 +461,76 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     kbbT[dd * lkc + rr] = from_f32<T>(xk);
                 }
                 __syncthreads();
-                const int tb0 = dh0 / 16;   // first accumulator tile of this D chunk
-                if (w == ib) {  // row side of target block ib
-                    f32x4 aq[NTH], ak[NTH];
+                // a wave's column half lies entirely inside or outside the D chunk
+                static_assert(L::DH % DH2 == 0, "column halves must tile the D chunks");
+                if (cd0 >= dh0 && cd0 < dh0 + L::DH) {
+                    const int bt0 = cd0 - dh0;   // operand row of this wave's first tile
+                    if (rb == ib) {  // row side of target block ib
+                        f32x4 aq[NTD], ak[NTD];
 #pragma unroll
-                    for (int t = 0; t < NTH; ++t) { aq[t] = zero4(); ak[t] = zero4(); }
-                    for (int k0 = 0; k0 < kbn; k0 += kstep<T>()) {
-                        const auto fq = frag_kc(dAqL, LC, r0, k0);
-                        const auto fk = frag_kc(dAkL, LC, r0, k0);
+                        for (int t = 0; t < NTD; ++t) { aq[t] = zero4(); ak[t] = zero4(); }
+                        for (int k0 = 0; k0 < kbn; k0 += kstep<T>()) {
+                            const auto fq = frag_kc(dAqL, LC, r0, k0, l);
+                            const auto fk = frag_kc(dAkL, LC, r0, k0, l);
 #pragma unroll
-                        for (int t = 0; t < NTH; ++t) {
-                            const auto b = frag_kc(kbT, lkb, 16 * t, k0);
-                            aq[t] = Mfma<T>::mma(fq, b, aq[t]);
-                            ak[t] = Mfma<T>::mma(fk, b, ak[t]);
+                            for (int t = 0; t < NTD; ++t) {
+                                const auto b = frag_kc(kbT, lkb, bt0 + 16 * t, k0, l);
+                                aq[t] = Mfma<T>::mma(fq, b, aq[t]);
+                                ak[t] = Mfma<T>::mma(fk, b, ak[t]);
+                            }
+                        }
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int r = r0 + acc_row(i, l);
+                                const float f = fast_exp2(Gs[r * LF + c] - Gs[rho * LF + c]);
+                                const float xq = f * aq[t][i], xk = f * ak[t][i];
+                                const float qv = to_f32(qL[r * LT + c]), kv = to_f32(kL[r * LT + c]);
+                                Pq[t][i] += xq;
+                                Pk[t][i] += bs[r] * xk;
+                                PG[t][i] += kLn2 * (qv * xq + bs[r] * kv * xk);
+                                dbp[i] += kv * xk;
+                            }
                         }
                     }
+                    if (rb == ib - 1) {  // column side of source block ib-1
+                        f32x4 dk[NTD];
 #pragma unroll
-                    for (int t = 0; t < NTH; ++t) {
-                        const int c = dh0 + 16 * t + acc_col();
+                        for (int t = 0; t < NTD; ++t) dk[t] = zero4();
+                        for (int k0 = 0; k0 < kcn; k0 += kstep<T>()) {
+                            const auto fq = frag_kc(dAqT, LC, r0, kcb + k0, l);
+                            const auto fk = frag_kc(dAkT, LC, r0, kcb + k0, l);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = r0 + acc_row(i);
-                            const float f = fast_exp2(Gs[r * LF + c] - Gs[rho * LF + c]);
-                            const float xq = f * aq[t][i], xk = f * ak[t][i];
-                            const float qv = to_f32(qL[r * LT + c]), kv = to_f32(kL[r * LT + c]);
-                            Pq[tb0 + t][i] += xq;
-                            Pk[tb0 + t][i] += bs[r] * xk;
-                            PG[tb0 + t][i] += kLn2 * (qv * xq + bs[r] * kv * xk);
-                            dbp[i] += kv * xk;
+                            for (int t = 0; t < NTD; ++t) {
+                                dk[t] = Mfma<T>::mma(fq, frag_kc(qbT, lkc, bt0 + 16 * t, k0, l), dk[t]);
+                                dk[t] = Mfma<T>::mma(fk, frag_kc(kbbT, lkc, bt0 + 16 * t, k0, l), dk[t]);
+                            }
                         }
-                    }
-                }
-                if (w == ib - 1) {  // column side of source block ib-1
-                    f32x4 dk[NTH];
 #pragma unroll
-                    for (int t = 0; t < NTH; ++t) dk[t] = zero4();
-                    for (int k0 = 0; k0 < kcn; k0 += kstep<T>()) {
-                        const auto fq = frag_kc(dAqT, LC, r0, kcb + k0);
-                        const auto fk = frag_kc(dAkT, LC, r0, kcb + k0);
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
 #pragma unroll
-                        for (int t = 0; t < NTH; ++t) {
-                            dk[t] = Mfma<T>::mma(fq, frag_kc(qbT, lkc, 16 * t, k0), dk[t]);
-                            dk[t] = Mfma<T>::mma(fk, frag_kc(kbbT, lkc, 16 * t, k0), dk[t]);
-                        }
-                    }
-#pragma unroll
-                    for (int t = 0; t < NTH; ++t) {
-                        const int c = dh0 + 16 * t + acc_col();
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int s = r0 + acc_row(i);
-                            const float x = fast_exp2(Gs[rho * LF + c] - Gs[s * LF + c]) * dk[t][i];
-                            Pk[tb0 + t][i] += x;
-                            PG[tb0 + t][i] -= kLn2 * to_f32(kL[s * LT + c]) * x;
+                            for (int i = 0; i < 4; ++i) {
+                                const int s2 = r0 + acc_row(i, l);
+                                const float x = fast_exp2(Gs[rho * LF + c] - Gs[s2 * LF + c]) * dk[t][i];
+                                Pk[t][i] += x;
+                                PG[t][i] -= kLn2 * to_f32(kL[s2 * LT + c]) * x;
+                            }
                         }
                     }
                 }
                 __syncthreads();
             }
         }
-        // row sums of db over the 16 lanes of each row group
+        // row sums of db over the 16 lanes of each row group (this column half)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float x = dbp[i];
             x += __shfl_xor(x, 1); x += __shfl_xor(x, 2);
             x += __shfl_xor(x, 4); x += __shfl_xor(x, 8);
-            if ((l & 15) == 0) dbS[r0 + acc_row(i)] += x;
+            if ((l & 15) == 0) dbS[ch * C + r0 + acc_row(i, l)] = x;
         }
         __syncthreads();  // Gs and the cross operands are dead from here
 
@@ -525,144 +540,129 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_chunk_bwd(Params p) {
         float* exg = exk + C * LF;
 #pragma unroll
         for (int t = 0; t < NTD; ++t) {
-            const int c = 16 * t + acc_col();
+            const int c = cd0 + 16 * t + acc_col(l);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = r0 + acc_row(i);
+                const int r = r0 + acc_row(i, l);
                 exq[r * LF + c] = Pq[t][i];
                 exk[r * LF + c] = Pk[t][i];
                 exg[r * LF + c] = PG[t][i];
             }
         }
         __syncthreads();
-        const float* gsrc = p.g;
-        float dGc[NCOL][16];
-        float dbd[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dbd[r] = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < NCOL; ++cc) {
-            const int d = l + 64 * cc;
-            float qr[16], kr[16], ar[16], br[16];
+        {
+            const int d = dcol;
+            float qr[16], kr[16], ar[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rr = r0 + r;
                 qr[r] = to_f32(qL[rr * LT + d]);
                 kr[r] = to_f32(kL[rr * LT + d]);
-                br[r] = bs[rr];
                 float gv = 0.f;
                 if (rr < len) {
-                    if constexpr (SCALAR) gv = gsrc[(size_t)(tok0 + rr) * p.H + h];
-                    else gv = gsrc[((size_t)(tok0 + rr) * p.H + h) * D + d];
+                    if constexpr (SCALAR) gv = p.g[(size_t)(tok0 + rr) * p.H + h];
+                    else gv = p.g[((size_t)(tok0 + rr) * p.H + h) * D + d];
                 }
                 ar[r] = fast_exp2(gv);
             }
             float accq[16], acck[16], dkt[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) { accq[r] = 0.f; acck[r] = 0.f; }
-            const float* aqD = dqD + w * 256;
-            const float* akD = dkD + w * 256;
+            // the fp32 16x16 blocks of dAqk / dAkk, spread over the wave: lane L
+            // holds entries 4L..4L+3 of [s][r]; each (r, s) value is fetched with
+            // v_readlane into a scalar register (wave-uniform operand)
+            const f32x4 aqv = *reinterpret_cast<const f32x4*>(dqD + rb * 256 + 4 * l);
+            const f32x4 akv = *reinterpret_cast<const f32x4*>(dkD + rb * 256 + 4 * l);
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
+            for (int s2 = 0; s2 < 16; ++s2) {
+                // keep each source row's loads and math together (no hoisting of
+                // the whole 16x16 block's loads into registers)
                 float E = 1.f, acc = 0.f;
-                const float ks = kr[s];
+                const float ks = kr[s2];
 #pragma unroll
-                for (int r = s; r < 16; ++r) {
-                    if (r > s) E *= ar[r];          // E = 2^(G_r - G_s)
-                    const float aq = aqD[s * 16 + r], ak = akD[s * 16 + r];
-                    const float t = ks * E;
-                    accq[r] += aq * t;
-                    acck[r] += ak * t;
-                    acc += (aq * qr[r] + ak * br[r] * kr[r]) * E;
+                for (int r = s2; r < 16; ++r) {
+                    if (r > s2) E *= ar[r];          // E = 2^(G_r - G_s)
+                    const float aq = lane_value(aqv, s2 * 16 + r), ak = lane_value(akv, s2 * 16 + r);
+                    const float tq = ks * E;
+                    accq[r] += aq * tq;
+                    acck[r] += ak * tq;
+                    acc += (aq * qr[r] + ak * bs[r0 + r] * kr[r]) * E;
                 }
-                dkt[s] = acc;
+                dkt[s2] = acc;
             }
+            // combine with the MFMA partials; dG in place in exg; the diagonal
+            // db terms k_r . acck_r in place in exq (summed per row below)
+            float gsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rr = r0 + r;
-                dq_tot[cc][r] += exq[rr * LF + d] + accq[r];
-                dk_tot[cc][r] += exk[rr * LF + d] + br[r] * acck[r] + dkt[r];
-                dGc[cc][r] = exg[rr * LF + d] +
-                             kLn2 * (qr[r] * accq[r] + kr[r] * (br[r] * acck[r] - dkt[r]));
-                dbd[r] += kr[r] * acck[r];
+                const float br = bs[rr];
+                const float dqv = exq[rr * LF + d] + accq[r];
+                const float dkv = exk[rr * LF + d] + br * acck[r] + dkt[r];
+                float dG = exg[rr * LF + d] + kLn2 * (qr[r] * accq[r] + kr[r] * (br * acck[r] - dkt[r]));
+                if (rb == NB - 1 && r == 15) {  // dG_last joins the last row of the chunk
+                    float sl = dGl[d];
+                    for (int b2 = 0; b2 < NB; ++b2) sl += dGlw[b2 * D + d];
+                    dG += sl;
+                }
+                if constexpr (GROUPED) {
+                    dq_tot[r] += dqv;
+                    dk_tot[r] += dkv;
+                } else if (colact && rr < len) {
+                    const size_t o = ((size_t)(tok0 + rr) * p.Hg + hk) * D + d;
+                    static_cast<T*>(p.dq)[o] = from_f32<T>(dqv);
+                    static_cast<T*>(p.dk)[o] = from_f32<T>(dkv);
+                }
+                gsum += dG;
+                if (colact) {
+                    exg[rr * LF + d] = dG;
+                    exq[rr * LF + d] = kr[r] * acck[r];
+                }
             }
-        }
-        // dG_last joins the last row of the chunk; local suffix sums per block
-#pragma unroll
-        for (int cc = 0; cc < NCOL; ++cc) {
-            const int d = l + 64 * cc;
-            if (w == NB - 1) {
-                float s = dGl[d];
-                for (int b2 = 0; b2 < NB; ++b2) s += dGlw[b2 * D + d];
-                dGc[cc][15] += s;
-            }
-            float s = 0.f;
-#pragma unroll
-            for (int r = 15; r >= 0; --r) { s += dGc[cc][r]; dGc[cc][r] = s; }
-            btot[w * D + d] = s;
-        }
-        // db: diagonal part summed over the wave's columns
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = dbd[r];
-            x += __shfl_xor(x, 1); x += __shfl_xor(x, 2); x += __shfl_xor(x, 4);
-            x += __shfl_xor(x, 8); x += __shfl_xor(x, 16); x += __shfl_xor(x, 32);
-            dbd[r] = x;
+            if (colact) btot[rb * D + d] = gsum;
         }
         __syncthreads();
-        {
-            T* dbo = static_cast<T*>(p.db);
-            if (l < 16) {
-                const int r = r0 + l;
-                float x = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) x = (i == l) ? dbd[i] : x;
-                if (r < len) dbo[(size_t)(tok0 + r) * p.H + h] = from_f32<T>(dbS[r] + x);
+        // reverse cumsum of dG over the chunk, per column: in place in exg
+        if (colact) {
+            const int d = dcol;
+            float suf = 0.f;
+            for (int b2 = rb + 1; b2 < NB; ++b2) suf += btot[b2 * D + d];
+            for (int r = 15; r >= 0; --r) {
+                const int rr = r0 + r;
+                suf += exg[rr * LF + d];
+                if constexpr (SCALAR) exg[rr * LF + d] = suf;
+                else if (rr < len) p.dg[((size_t)(tok0 + rr) * p.H + h) * D + d] = suf;
             }
         }
-#pragma unroll
-        for (int cc = 0; cc < NCOL; ++cc) {
-            const int d = l + 64 * cc;
-            float later = 0.f;
-            for (int b2 = w + 1; b2 < NB; ++b2) later += btot[b2 * D + d];
+        if constexpr (SCALAR) __syncthreads();
+        // per-row sums: db = MFMA partials + sum_d k . acck (diagonal);
+        // scalar gate: dg = sum over channels of the per-channel suffix sums
+        if (tid < C && tid < len) {
+            float x = dbS[tid] + dbS[C + tid];
+            for (int d = 0; d < D; ++d) x += exq[tid * LF + d];
+            static_cast<T*>(p.db)[(size_t)(tok0 + tid) * p.H + h] = from_f32<T>(x);
             if constexpr (SCALAR) {
-                // scalar gate: dg is the sum over channels of the per-channel gradient
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dGc[cc][r] += later;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rr = r0 + r;
-                    if (rr < len) p.dg[((size_t)(tok0 + rr) * p.H + h) * D + d] = dGc[cc][r] + later;
-                }
+                float gsum2 = 0.f;
+                for (int d = 0; d < D; ++d) gsum2 += exg[tid * LF + d];
+                p.dg[(size_t)(tok0 + tid) * p.H + h] = gsum2;
             }
         }
-        if constexpr (SCALAR) {
+    };
+    if constexpr (GROUPED) {
+        for (int gi = 0; gi < p.G; ++gi) head(gi);
+    } else {
+        head(0);
+    }
+    if constexpr (GROUPED) {
+        if (colact) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < NCOL; ++cc) x += dGc[cc][r];
-                x += __shfl_xor(x, 1); x += __shfl_xor(x, 2); x += __shfl_xor(x, 4);
-                x += __shfl_xor(x, 8); x += __shfl_xor(x, 16); x += __shfl_xor(x, 32);
                 const int rr = r0 + r;
-                if (l == 0 && rr < len) p.dg[(size_t)(tok0 + rr) * p.H + h] = x;
-            }
-        }
-    }
-    // dq, dk (group sums) in the io dtype
-    T* dqo = static_cast<T*>(p.dq);
-    T* dko = static_cast<T*>(p.dk);
-#pragma unroll
-    for (int cc = 0; cc < NCOL; ++cc) {
-        const int d = l + 64 * cc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rr = r0 + r;
-            if (rr < len) {
-                const size_t o = ((size_t)(tok0 + rr) * p.Hg + hk) * D + d;
-                dqo[o] = from_f32<T>(dq_tot[cc][r]);
-                dko[o] = from_f32<T>(dk_tot[cc][r]);
+                if (rr < len) {
+                    const size_t o = ((size_t)(tok0 + rr) * p.Hg + hk) * D + dcol;
+                    static_cast<T*>(p.dq)[o] = from_f32<T>(dq_tot[r]);
+                    static_cast<T*>(p.dk)[o] = from_f32<T>(dk_tot[r]);
+                }
             }
         }
     }

@@ -66,9 +66,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Fragment of a matrix stored with the reduction index contiguous: element
 // (i, kk) at p[i*ld + kk]; lane l gets i = i0 + l%16, kk = k0 + KL*(l/16) + [0,KL).
 // Works for LDS and global pointers; needs 16-byte alignment for 16-bit types.
+// Every lane-dependent helper takes the lane index as its last argument
+// (default: the hardware lane id) so that a kernel can pass an opaque copy.
 template <typename T>
-__device__ __forceinline__ typename Mfma<T>::frag frag_kc(const T* p, int ld, int i0, int k0) {
-    const int l = lane_id();
+__device__ __forceinline__ typename Mfma<T>::frag frag_kc(const T* p, int ld, int i0, int k0,
+                                                          int l = lane_id()) {
     const T* q = p + (long)(i0 + (l & 15)) * ld + k0 + (l >> 4) * Mfma<T>::KL;
     return *reinterpret_cast<const typename Mfma<T>::frag*>(q);
 }
@@ -76,8 +78,8 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_kc(const T* p, int ld, in
 // Same fragment of a matrix stored with the reduction index as the row:
 // element (i, kk) at p[kk*ld + i].
 template <typename T>
-__device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, int i0, int k0) {
-    const int l = lane_id();
+__device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, int i0, int k0,
+                                                          int l = lane_id()) {
     typename Mfma<T>::frag f;
     if constexpr (Mfma<T>::KL == 1) {
         f = p[(long)(k0 + (l >> 4)) * ld + i0 + (l & 15)];
@@ -93,23 +95,23 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, in
 // with both operands stored reduction-contiguous (A[i*lda+kk], Bt[j*ldb+kk]).
 template <typename T, int NT, int KD>
 __device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda, int i0,
-                                          const T* Bt, int ldb, int j0) {
+                                          const T* Bt, int ldb, int j0, int l = lane_id()) {
 #pragma unroll
     for (int k0 = 0; k0 < KD; k0 += kstep<T>()) {
-        auto a = frag_kc(A, lda, i0, k0);
+        auto a = frag_kc(A, lda, i0, k0, l);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0), acc[t]);
+        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0, l), acc[t]);
     }
 }
 
 // Same with a run-time reduction length kd (a multiple of kstep<T>()).
 template <typename T, int NT>
 __device__ __forceinline__ void panel_mma_n(f32x4 (&acc)[NT], const T* A, int lda, int i0,
-                                            const T* Bt, int ldb, int j0, int kd) {
+                                            const T* Bt, int ldb, int j0, int kd, int l = lane_id()) {
     for (int k0 = 0; k0 < kd; k0 += kstep<T>()) {
-        auto a = frag_kc(A, lda, i0, k0);
+        auto a = frag_kc(A, lda, i0, k0, l);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0), acc[t]);
+        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0, l), acc[t]);
     }
 }
 
@@ -126,11 +128,31 @@ __device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* A, int lda, in
     return acc;
 }
 
+// Value idx (0..255) of a 256-float block spread over a wave as lane L ->
+// entries 4L..4L+3, read into a scalar register with v_readlane; idx must be
+// a compile-time constant after unrolling.
+// (The element is picked with an explicit select: indexing the vector inside
+// the readlane argument returned wrong values for elements 1..3 on the device.)
+__device__ __forceinline__ float lane_value(f32x4 v, int idx) {
+    const int j = idx & 3;
+    const float x = j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), idx >> 2));
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Row / column of element i (0..3) of an f32x4 accumulator tile held by this lane.
-__device__ __forceinline__ int acc_row(int i) { return 4 * (lane_id() >> 4) + i; }
-__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+__device__ __forceinline__ int acc_row(int i, int l = lane_id()) { return 4 * (l >> 4) + i; }
+__device__ __forceinline__ int acc_col(int l = lane_id()) { return l & 15; }
+
+// The hardware lane id behind an empty asm: each call yields a value the
+// compiler cannot prove equal to any other, so lane-dependent arithmetic
+// derived from it is neither hoisted out of loops nor merged across copies.
+__device__ __forceinline__ int opaque_lane_id() {
+    int l = static_cast<int>(threadIdx.x & 63);
+    asm volatile("" : "+v"(l));
+    return l;
+}
 
 // Store 4 consecutive values (accumulator rows r..r+3 of one column) to
 // p[0..3] (contiguous), converting to T.

@@ -24,8 +24,11 @@ hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
     if (e == hipSuccess) e = mark(2);
     gdr_sweep<T, C, D, kSweepBV><<<dim3(2 * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(3);
-    if (p.nc_max > 0)
-        gdr_chunk_bwd<T, C, D, SCALAR><<<dim3(p.nc_max, p.Hg), dim3(64 * (C / 16)), 0, stream>>>(p);
+    if (p.nc_max > 0) {
+        const dim3 grid(p.nc_max, p.Hg), block(128 * (C / 16));
+        if (p.G > 1) gdr_chunk_bwd<T, C, D, SCALAR, true><<<grid, block, 0, stream>>>(p);
+        else gdr_chunk_bwd<T, C, D, SCALAR, false><<<grid, block, 0, stream>>>(p);
+    }
     if (e == hipSuccess) e = mark(4);
     const hipError_t le = hipGetLastError();
     return le != hipSuccess ? le : e;
