@@ -97,12 +97,44 @@ struct PrepLds {
     static constexpr size_t SCR_OFF = AF_OFF + size_t(C) * LCF * 4;
     static constexpr size_t BETA_OFF = SCR_OFF + size_t(NB) * 16 * 20 * 4;
     static constexpr size_t TOTAL = BETA_OFF + size_t(C) * 4;
-    // after the inverse, the q/k region holds A and Aqk as MFMA operands
-    static constexpr size_t AT_OFF = Q_OFF;                                  // T [C][LC]
-    static constexpr size_t AQKT_OFF = Q_OFF + size_t(C) * LC * sizeof(T);   // T [C][LC]
-    static_assert(2 * size_t(C) * LC * sizeof(T) <= 2 * size_t(C) * LT * sizeof(T), "A/Aqk alias");
+    // after the inverse, A and Aqk are converted in place to MFMA operands
+    static_assert(size_t(C) * LC * sizeof(T) <= size_t(C) * LCF * 4, "A/Aqk in place");
+    static_assert(size_t(NB) * 16 * 20 >= size_t(NT > D ? NT : D) * 1, "cumsum scratch");
     static_assert(TOTAL <= 163840, "LDS budget of gdr_prep");
 };
+
+// Eight consecutive elements of a T row at p (16 bytes for 16-bit T, 32 for fp32).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const Vec16 v = ld16(p);
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = to_f32(e[i]);
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[i + 4] = b[i]; }
+    }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        Vec16 v;
+        T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = from_f32<T>(x[i]);
+        st16(p, v);
+    } else {
+        *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+}
+__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[i + 4] = b[i]; }
+}
 
 template <typename T, int C, int D, bool SCALAR>
 __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
@@ -126,20 +158,21 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     const ChunkEntry ce = p.ctab[j];
     const int tok0 = ce.tok0, len = ce.len;
     const int hk = h / p.G;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int tid = threadIdx.x, w = wave_id();
     const T* q = static_cast<const T*>(p.q);
     const T* k = static_cast<const T*>(p.k);
     const T* v = static_cast<const T*>(p.v);
     const T* beta = static_cast<const T*>(p.beta);
     const size_t jh = size_t(j) * p.H + h;
+    constexpr int V8 = 16 / sizeof(T);  // elements per 16-byte vector
 
-    // ---- phase 1: raw gate -> 2^g table and chunk-local cumsum G; q, k, beta ----
+    // ---- phase 1: raw gate -> 2^g table and G; q, k, beta ----
     for (int e = tid; e < C * (D / 4); e += NT) {
         const int r = e / (D / 4), d0 = (e % (D / 4)) * 4;
         f32x4 gv = zero4();
         if (r < len) {
             if constexpr (SCALAR) {
-                float s = p.g[(size_t)(tok0 + r) * p.H + h];
+                const float s = p.g[(size_t)(tok0 + r) * p.H + h];
                 gv = f32x4{s, s, s, s};
             } else {
                 gv = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + r) * p.H + h) * D + d0);
@@ -149,7 +182,6 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         *reinterpret_cast<f32x4*>(At + r * LF + d0) =
             f32x4{fast_exp2(gv[0]), fast_exp2(gv[1]), fast_exp2(gv[2]), fast_exp2(gv[3])};
     }
-    constexpr int V8 = 16 / sizeof(T);  // elements per 16-byte vector
     for (int e = tid; e < C * (D / V8); e += NT) {
         const int r = e / (D / V8), d0 = (e % (D / V8)) * V8;
         Vec16 qv{}, kv{};
@@ -163,11 +195,24 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     for (int r = tid; r < C; r += NT) bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
     for (int e = tid; e < C * LCF; e += NT) { AqkF[e] = 0.f; AkkF[e] = 0.f; AF[e] = 0.f; }
     __syncthreads();
-    for (int d = tid; d < D; d += NT) {  // column cumsum
-        float s = 0.f;
-        for (int r = 0; r < C; ++r) { s += Gs[r * LF + d]; Gs[r * LF + d] = s; }
+    {   // column cumsum in NSEG segments of SR rows: local scans, then segment offsets
+        constexpr int NSEG = NT / D > 0 ? NT / D : 1, SR = C / NSEG;
+        static_assert(NT % D == 0 || NT < D, "cumsum split");
+        float* segtot = scr;  // [NSEG][D]
+        const int d = tid % D, sg = tid / D;
+        if (sg < NSEG) {
+            float s = 0.f;
+            for (int r = sg * SR; r < (sg + 1) * SR; ++r) { s += Gs[r * LF + d]; Gs[r * LF + d] = s; }
+            segtot[sg * D + d] = s;
+        }
+        __syncthreads();
+        if (sg < NSEG && sg > 0) {
+            float off = 0.f;
+            for (int s2 = 0; s2 < sg; ++s2) off += segtot[s2 * D + d];
+            for (int r = sg * SR; r < (sg + 1) * SR; ++r) Gs[r * LF + d] += off;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- phase 2: diagonal 16x16 blocks of Aqk / Akk (VALU, per element) ----
     // lane -> (block m, mirror row pair pr, d-part e8); the pair (16m+pr,
@@ -175,15 +220,18 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     // the d-part are summed across the 8 parts with xor shuffles.
     {
         constexpr int PW = D / 8;
+        static_assert(PW % 8 == 0, "d-part of whole 8-element vectors");
         const int m = tid >> 6, pr = (tid & 63) >> 3, e8 = tid & 7, d0 = e8 * PW;
         float qr[PW], kr[PW], E[PW];
         int r = 16 * m + pr, s = r;
         auto load_row = [&](int rr) {
 #pragma unroll
-            for (int i = 0; i < PW; ++i) {
-                qr[i] = to_f32(qL[rr * LT + d0 + i]);
-                kr[i] = to_f32(kL[rr * LT + d0 + i]);
-                E[i] = 1.f;
+            for (int i0 = 0; i0 < PW; i0 += 8) {
+                float x[8], y[8];
+                load8<T>(qL + rr * LT + d0 + i0, x);
+                load8<T>(kL + rr * LT + d0 + i0, y);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { qr[i0 + i] = x[i]; kr[i0 + i] = y[i]; E[i0 + i] = 1.f; }
             }
         };
         load_row(r);
@@ -195,10 +243,17 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
             }
             float pq = 0.f, pk = 0.f;
 #pragma unroll
-            for (int i = 0; i < PW; ++i) {
-                const float t = to_f32(kL[s * LT + d0 + i]) * E[i];
-                pq += qr[i] * t;
-                pk += kr[i] * t;
+            for (int i0 = 0; i0 < PW; i0 += 8) {
+                float ks[8], as[8];
+                load8<T>(kL + s * LT + d0 + i0, ks);
+                load8f(At + s * LF + d0 + i0, as);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float t = ks[i] * E[i0 + i];
+                    pq += qr[i0 + i] * t;
+                    pk += kr[i0 + i] * t;
+                    E[i0 + i] *= as[i];   // E(r, s-1) = E(r, s) * 2^g_s
+                }
             }
             pq += __shfl_xor(pq, 1); pk += __shfl_xor(pk, 1);
             pq += __shfl_xor(pq, 2); pk += __shfl_xor(pk, 2);
@@ -207,9 +262,6 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
                 AqkF[r * LCF + s] = pq;
                 if (s < r) AkkF[r * LCF + s] = bs[r] * pk;
             }
-            // E(r, s-1) = E(r, s) * 2^g_s
-#pragma unroll
-            for (int i = 0; i < PW; ++i) E[i] *= At[s * LF + d0 + i];
             --s;
         }
     }
@@ -221,22 +273,24 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         T* qb = Xb;                 // [16][LT]  q_r 2^(G_r - G_rho), r in block ib
         T* kqb = Xb + 16 * LT;      // [16][LT]  k_r 2^(G_r - G_rho)
         T* kb = Xb + 32 * LT;       // [rho][LT] k_s 2^(G_rho - G_s), s < rho
-        for (int e = tid; e < (32 + rho) * D; e += NT) {
-            const int rr = e / D, d = e % D;
-            const float grho = Gs[rho * LF + d];
-            if (rr < 16) {
-                const int r = rho + rr;
-                const float f = fast_exp2(Gs[r * LF + d] - grho);
-                qb[rr * LT + d] = from_f32<T>(to_f32(qL[r * LT + d]) * f);
-            } else if (rr < 32) {
-                const int r = rho + rr - 16;
-                const float f = fast_exp2(Gs[r * LF + d] - grho);
-                kqb[(rr - 16) * LT + d] = from_f32<T>(to_f32(kL[r * LT + d]) * f);
+        for (int e = tid; e < (32 + rho) * (D / 8); e += NT) {
+            const int rr = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            float gr[8], gx[8], x[8];
+            load8f(Gs + rho * LF + d0, gr);
+            if (rr < 32) {
+                const int r = rho + (rr & 15);
+                load8f(Gs + r * LF + d0, gx);
+                load8<T>((rr < 16 ? qL : kL) + r * LT + d0, x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gx[i] - gr[i]);
             } else {
-                const int s = rr - 32;
-                const float f = fast_exp2(grho - Gs[s * LF + d]);
-                kb[s * LT + d] = from_f32<T>(to_f32(kL[s * LT + d]) * f);
+                const int s2 = rr - 32;
+                load8f(Gs + s2 * LF + d0, gx);
+                load8<T>(kL + s2 * LT + d0, x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gr[i] - gx[i]);
             }
+            store8<T>(Xb + rr * LT + d0, x);
         }
         __syncthreads();
         // tiles: (which in {Aqk, Akk}) x (rho/16 column tiles)
@@ -247,9 +301,9 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
             panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = rho + acc_row(i), s = 16 * ct + acc_col();
-                if (which) AkkF[r * LCF + s] = bs[r] * acc[0][i];
-                else AqkF[r * LCF + s] = acc[0][i];
+                const int r = rho + acc_row(i), s2 = 16 * ct + acc_col();
+                if (which) AkkF[r * LCF + s2] = bs[r] * acc[0][i];
+                else AqkF[r * LCF + s2] = acc[0][i];
             }
         }
         __syncthreads();
@@ -292,36 +346,41 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         __syncthreads();
     }
 
-    // ---- phase 5: A, Aqk to the workspace and into LDS as MFMA operands ----
+    // ---- phase 5: A, Aqk to the workspace; in place as MFMA operands in LDS ----
+    constexpr int PER = C * C / NT;   // elements of a C x C matrix per thread
+    float av[PER], qv[PER];
     {
         T* gA = static_cast<T*>(p.Am) + jh * C * C;
         T* gAT = static_cast<T*>(p.AT) + jh * C * C;
         T* gSq = static_cast<T*>(p.sAqkT) + jh * C * C;
-        for (int e = tid; e < C * C; e += NT) {
-            const int r = e / C, s = e % C;
-            gA[e] = from_f32<T>(AF[r * LCF + s]);
-            gAT[e] = from_f32<T>(AF[s * LCF + r]);         // AT[r][s] = A[s][r]
-            gSq[e] = from_f32<T>(p.scale * AqkF[s * LCF + r]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + i * NT, r = e / C, s2 = e % C;
+            av[i] = AF[r * LCF + s2];
+            qv[i] = AqkF[r * LCF + s2];
+            gA[e] = from_f32<T>(av[i]);
+            gAT[e] = from_f32<T>(AF[s2 * LCF + r]);         // AT[r][s] = A[s][r]
+            gSq[e] = from_f32<T>(p.scale * AqkF[s2 * LCF + r]);
         }
     }
-    T* AtL = reinterpret_cast<T*>(smem + L::AT_OFF);     // A   [C][LC]
-    T* AqkL = reinterpret_cast<T*>(smem + L::AQKT_OFF);  // Aqk [C][LC]
-    // q/k in LDS are no longer needed: re-read from global below.
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, s = e % C;
-        AtL[r * LC + s] = from_f32<T>(AF[r * LCF + s]);
-        AqkL[r * LC + s] = from_f32<T>(AqkF[r * LCF + s]);
-    }
-    // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^)
-    T* khT = Xb;  // [D][LC]
-    for (int e = tid; e < C * (D / V8); e += NT) {
-        const int s = e / (D / V8), d0 = (e % (D / V8)) * V8;
-        Vec16 kv{};
-        if (s < len) kv = ld16(k + ((size_t)(tok0 + s) * p.Hg + hk) * D + d0);
-        const T* kk = reinterpret_cast<const T*>(&kv);
+    __syncthreads();
+    T* AtL = reinterpret_cast<T*>(smem + L::AF_OFF);    // A   [C][LC], over the dead fp32 A
+    T* AqkL = reinterpret_cast<T*>(smem + L::AQK_OFF);  // Aqk [C][LC], over the dead fp32 Aqk
 #pragma unroll
-        for (int i = 0; i < V8; ++i)
-            khT[(d0 + i) * LC + s] = from_f32<T>(bs[s] * to_f32(kk[i]) * fast_exp2(Gs[s * LF + d0 + i]));
+    for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * NT, r = e / C, s2 = e % C;
+        AtL[r * LC + s2] = from_f32<T>(av[i]);
+        AqkL[r * LC + s2] = from_f32<T>(qv[i]);
+    }
+    // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^): 8 consecutive s per item
+    T* khT = Xb;  // [D][LC]
+    for (int e = tid; e < D * (C / 8); e += NT) {
+        const int d = e / (C / 8), s0 = (e % (C / 8)) * 8;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            x[i] = bs[s0 + i] * to_f32(kL[(s0 + i) * LT + d]) * fast_exp2(Gs[(s0 + i) * LF + d]);
+        store8<T>(khT + d * LC + s0, x);
     }
     __syncthreads();
 
@@ -332,25 +391,35 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     for (int t = 0; t < NTD; ++t) acc[t] = zero4();
     panel_mma<T, NTD, C>(acc, AtL, LC, r0, khT, LC, 0);
     __syncthreads();  // khT is about to be overwritten by w^T
-    {
-        T* gw = static_cast<T*>(p.w) + jh * C * D;
-        T* gwT = static_cast<T*>(p.wT) + jh * D * C;
-        T* wTL = Xb;  // [D][LC]
+    T* wTL = Xb;  // [D][LC]
 #pragma unroll
-        for (int t = 0; t < NTD; ++t) {
-            const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gw[(rb + i) * D + c] = from_f32<T>(acc[t][i]);
-            store4<T>(gwT + c * C + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-            store4<T>(wTL + c * LC + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-        }
+    for (int t = 0; t < NTD; ++t) {
+        const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+        store4<T>(wTL + c * LC + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     }
     __syncthreads();
+    {   // w^T rows out (16-byte pieces), w out through transposing LDS reads
+        T* gw = static_cast<T*>(p.w) + jh * C * D;
+        T* gwT = static_cast<T*>(p.wT) + jh * D * C;
+        for (int e = tid; e < D * (C / 8); e += NT) {
+            const int d = e / (C / 8), s0 = (e % (C / 8)) * 8;
+            float x[8];
+            load8<T>(wTL + d * LC + s0, x);
+            store8<T>(gwT + d * C + s0, x);
+        }
+        for (int e = tid; e < C * (D / 8); e += NT) {
+            const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = to_f32(wTL[(d0 + i) * LC + r]);
+            store8<T>(gw + r * D + d0, x);
+        }
+    }
 
     // ---- phase 7: q~ = q 2^G - Aqk w, stored as scale * q~^T ----
 #pragma unroll
     for (int t = 0; t < NTD; ++t) acc[t] = zero4();
-    panel_mma<T, NTD, C>(acc, AqkL, LC, r0, Xb, LC, 0);
+    panel_mma<T, NTD, C>(acc, AqkL, LC, r0, wTL, LC, 0);
     {
         T* gq = static_cast<T*>(p.qsT) + jh * D * C;
 #pragma unroll
@@ -360,8 +429,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
-                const float qv = r < len ? to_f32(q[((size_t)(tok0 + r) * p.Hg + hk) * D + c]) : 0.f;
-                o[i] = p.scale * (qv * fast_exp2(Gs[r * LF + c]) - acc[t][i]);
+                o[i] = p.scale * (to_f32(qL[r * LT + c]) * fast_exp2(Gs[r * LF + c]) - acc[t][i]);
             }
             store4<T>(gq + c * C + rb, o[0], o[1], o[2], o[3]);
         }
@@ -371,12 +439,12 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     // ---- phase 8: u = A (beta v) ----
     T* vhT = Xb;  // [D][LC]
     for (int e = tid; e < C * (D / V8); e += NT) {
-        const int s = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        const int s2 = e / (D / V8), d0 = (e % (D / V8)) * V8;
         Vec16 vv{};
-        if (s < len) vv = ld16(v + ((size_t)(tok0 + s) * p.H + h) * D + d0);
+        if (s2 < len) vv = ld16(v + ((size_t)(tok0 + s2) * p.H + h) * D + d0);
         const T* vp = reinterpret_cast<const T*>(&vv);
 #pragma unroll
-        for (int i = 0; i < V8; ++i) vhT[(d0 + i) * LC + s] = from_f32<T>(bs[s] * to_f32(vp[i]));
+        for (int i = 0; i < V8; ++i) vhT[(d0 + i) * LC + s2] = from_f32<T>(bs[s2] * to_f32(vp[i]));
     }
     __syncthreads();
 #pragma unroll
@@ -395,20 +463,24 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     {
         T* gkt = static_cast<T*>(p.kt) + jh * C * D;
         T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
-        for (int e = tid; e < C * (D / V8); e += NT) {
-            const int r = e / (D / V8), d0 = (e % (D / V8)) * V8;
-            Vec16 kv{};
-            if (r < len) kv = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-            const T* kk = reinterpret_cast<const T*>(&kv);
-            Vec16 o;
-            T* op = reinterpret_cast<T*>(&o);
+        for (int e = tid; e < C * (D / 8); e += NT) {
+            const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            float x[8], gl[8], g[8];
+            load8<T>(kL + r * LT + d0, x);
+            load8f(Gs + (C - 1) * LF + d0, gl);
+            load8f(Gs + r * LF + d0, g);
 #pragma unroll
-            for (int i = 0; i < V8; ++i) {
-                const float x = to_f32(kk[i]) * fast_exp2(Gs[(C - 1) * LF + d0 + i] - Gs[r * LF + d0 + i]);
-                op[i] = from_f32<T>(x);
-                gktT[(d0 + i) * C + r] = op[i];
-            }
-            st16(gkt + r * D + d0, o);
+            for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
+            store8<T>(gkt + r * D + d0, x);
+        }
+        for (int e = tid; e < D * (C / 8); e += NT) {
+            const int d = e / (C / 8), r0b = (e % (C / 8)) * 8;
+            const float gl = Gs[(C - 1) * LF + d];
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                x[i] = to_f32(kL[(r0b + i) * LT + d]) * fast_exp2(gl - Gs[(r0b + i) * LF + d]);
+            store8<T>(gktT + d * C + r0b, x);
         }
         for (int d = tid; d < D; d += NT) p.glast[jh * D + d] = fast_exp2(Gs[(C - 1) * LF + d]);
     }
