@@ -91,6 +91,124 @@ def cpu_baseline(inp, budget_s: float = 20.0) -> dict:
                       f"({t:.1f} s fp64 on the host; value scaled to all heads)"}
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel from rocprofv3 counters
+# ---------------------------------------------------------------------------
+# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the same counters
+# read for a plain elementwise copy of known size (`--copy-probe`), so the
+# result is in true bytes. The figures live in a text summary under profiles/
+# together with a hash of the kernel's sources; once the sources change the
+# stored figure no longer describes the kernel and `traffic` is reported null.
+KERNEL_SOURCES = ("chunked_gated_delta_gdr_amd/csrc/gdr_chunk_bwd.hpp",
+                  "chunked_gated_delta_gdr_amd/csrc/gdr_common.hpp")
+COPY_KERNEL_KEY = "neg_kernel"   # torch.neg(out=...): reads N bytes, writes N bytes
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gdr_chunk_bwd_{workload}_traffic.md")
+
+
+def stored_traffic(workload: str):
+    """Bytes per launch from the committed counter summary, or None if there is
+    none or it was taken on other sources of the kernel."""
+    p = traffic_summary_path(workload)
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        parts = line.strip().split("=")
+        if len(parts) == 2 and parts[0].strip().isidentifier():
+            kv[parts[0].strip()] = parts[1].strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _read_counter_csv(path: str, counter: str) -> dict:
+    """{kernel name: [value per dispatch in KiB]} from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(d: dict, key: str):
+    names = [n for n in d if key in n]
+    if len(names) != 1:
+        raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
+    return d[names[0]]
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: float, workload: str) -> str:
+    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * 2 ** 20
+    cf, cw = _pick(fetch, COPY_KERNEL_KEY), _pick(write, COPY_KERNEL_KEY)
+    f_copy = copy_bytes / (sum(cf) / len(cf) * 1024)
+    w_copy = copy_bytes / (sum(cw) / len(cw) * 1024)
+    kf, kw = _pick(fetch, "gdr_chunk_bwd"), _pick(write, "gdr_chunk_bwd")
+    rd = sum(kf) / len(kf) * 1024 * f_copy
+    wr = sum(kw) / len(kw) * 1024 * w_copy
+    lines = [
+        f"# gdr_chunk_bwd HBM traffic, workload {workload}",
+        "",
+        "rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one pass each, scaled by the",
+        f"same counters on a plain copy of {copy_mib:g} MiB (torch.neg, reads and writes "
+        f"{copy_mib:g} MiB).",
+        "",
+        "```",
+        f"workload = {workload}",
+        f"kernel_source_sha256 = {kernel_source_hash()}",
+        f"copy_fetch_kib = {sum(cf) / len(cf):.1f}",
+        f"copy_write_kib = {sum(cw) / len(cw):.1f}",
+        f"fetch_scale = {f_copy:.4f}",
+        f"write_scale = {w_copy:.4f}",
+        f"kernel_fetch_kib = {sum(kf) / len(kf):.1f}",
+        f"kernel_write_kib = {sum(kw) / len(kw):.1f}",
+        f"read_bytes_per_launch = {rd:.0f}",
+        f"write_bytes_per_launch = {wr:.0f}",
+        f"traffic_bytes_per_launch = {rd + wr:.0f}",
+        "```",
+        "",
+        "Per dispatch (KiB, raw):",
+        "",
+        "| kernel | FETCH_SIZE | WRITE_SIZE |",
+        "|---|---|---|",
+    ]
+    for name in sorted(set(fetch) | set(write)):
+        fv, wv = fetch.get(name, [0.0]), write.get(name, [0.0])
+        lines.append(f"| `{name[:90]}` | {sum(fv) / len(fv):.1f} | {sum(wv) / len(wv):.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_kernel_stats(stats_csv: str) -> str:
+    """Markdown table from a rocprofv3 --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["| kernel | calls | average (us) | min (us) | max (us) | share (%) |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,12 +216,25 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="kda_fixed_h16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
+                    help="after the timed steps, run a plain copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="print a table of a rocprofv3 --stats kernel_stats.csv and exit")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, args.copy_probe or 1024.0, args.workload),
+              end="")
+        return 0
+    if args.summarize_stats:
+        print(summarize_kernel_stats(args.summarize_stats), end="")
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the backward shards by sequence / head with no exchange; see DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path here (the backward "
+              "shards by sequence or head with no exchange, so N GPUs run N independent "
+              "copies of this step). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
@@ -176,7 +307,7 @@ def main() -> int:
                    "n_seqs": n_seqs, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "gdr_chunk_bwd", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": stored_traffic(w.name),
                      "algorithmic_bytes": k_bytes, "ms": k_ms},
         "step_roofline": {
             "method_bytes": costs["method_bytes"] * th,
@@ -188,6 +319,14 @@ def main() -> int:
         "kernels_ms": kernel_ms,
         "wall_ms_per_step": t_wall * 1e3 / args.steps,
     }
+    if args.copy_probe > 0:
+        n = int(args.copy_probe * 2 ** 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(res), flush=True)
