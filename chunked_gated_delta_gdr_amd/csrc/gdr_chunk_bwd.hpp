@@ -19,11 +19,18 @@
 //   dkt_s  = sum_{r>=s} (dAqk[r,s] q_r + dAkk[r,s] beta_r k_r) 2^(G_r-G_s)
 //   dq += accq, dk += beta acck + dkt, db += k . acck,
 //   dG += ln2 [q accq + k (beta acck - dkt)],
-// cross-block terms on MFMA through the block boundary rho (q/k prescaled by
-// 2^(G - G_rho) or 2^(G_rho - G), post-factors 2^(G_r - G_rho) and
-// 2^(G_rho - G_s), every exponent <= 0), the diagonal 16x16 blocks on VALU
-// with one running decay per (r, s, d). Finally dg = reverse cumsum of dG in
-// the chunk (the page's fold_dg), dG_last collecting
+// all on MFMA, one 16x16x16 product per pair of 16-row blocks. With block b =
+// rows 16b..16b+15, Ein_r = 2^(G_r - G_16b(r)) and Eout_s = 2^(G_16(b(s)+1) - G_s)
+// (both <= 1) and phi_j = 2^(G_16(j+1) - G_16j), the decay between a row r of
+// block b and a source s of an earlier block b' factors as
+//   2^(G_r - G_s) = Ein_r * phi_{b'+1} ... phi_{b-1} * Eout_s,
+// so the operands k Eout, q Ein, beta k Ein are scaled once per chunk and the
+// phi are applied to the accumulators between blocks (Horner); every exponent
+// is <= 0. Inside a diagonal block the source side needs 2^(G_16b - G_s) >= 1;
+// the MFMA form is used there when the block's gate range |G_r - G_16b| stays
+// within 2^64 for every column of the wave, else an exact VALU pass with one
+// exp2 per (r, s, d) (never reached at ordinary gate magnitudes). Finally
+// dg = reverse cumsum of dG in the chunk (the page's fold_dg), dG_last collecting
 //   ln2 [2^G_last rowsum_v(h dh') + sum_r k_r dk~_r 2^(G_last - G_r)].
 #pragma once
 #include "gdr_common.hpp"
@@ -46,12 +53,12 @@ struct BwdLds {
     static constexpr size_t Q_OFF = 0;
     static constexpr size_t K_OFF = Q_OFF + sz(C, LT, sizeof(T));
     static constexpr size_t BETA_OFF = K_OFF + sz(C, LT, sizeof(T));        // f32 [C]
-    static constexpr size_t DB_OFF = BETA_OFF + C * 4;                       // f32 [4][C] db partials
-    static constexpr size_t GL_OFF = DB_OFF + 4 * C * 4;                     // f32 [D] dG_last
+    static constexpr size_t DB_OFF = BETA_OFF + C * 4;                       // f32 [2][C] db row partials
+    static constexpr size_t DGR_OFF = DB_OFF + 2 * C * 4;                    // f32 [2][C] scalar-gate dg rows
+    static constexpr size_t GL_OFF = DGR_OFF + 2 * C * 4;                    // f32 [D] dG_last
     static constexpr size_t GLW_OFF = GL_OFF + D * 4;                        // f32 [NB][D] per-wave dG_last
-    static constexpr size_t BT_OFF = GLW_OFF + size_t(NB) * D * 4;           // f32 [NB][D] block totals + [2][C]
-    static constexpr size_t DIAG_OFF = BT_OFF + (size_t(NB) * D + 2 * C) * 4; // f32 [2][NB][16][16]
-    static constexpr size_t U_OFF = DIAG_OFF + size_t(2) * NB * 256 * 4;     // union region
+    static constexpr size_t BT_OFF = GLW_OFF + size_t(NB) * D * 4;           // f32 [NB][D] block totals
+    static constexpr size_t U_OFF = BT_OFF + size_t(NB) * D * 4;             // union region
     // phase 1 (state products, one V slice)
     static constexpr size_t P1_DOT = 0;                                      // T [BVS][LC]
     static constexpr size_t P1_XL = P1_DOT + sz(BVS, LC, sizeof(T));         // T [C][LB]
@@ -61,37 +68,35 @@ struct BwdLds {
     static constexpr size_t P1_DXT = P1_DXL + sz(C, LB, sizeof(T));          // T [BVS][LC]
     static constexpr size_t P1_VL = P1_DXT + sz(BVS, LC, sizeof(T));         // T [C][LB]
     static constexpr size_t P1_END = P1_VL + sz(C, LB, sizeof(T));
-    // phase 2: Gs lives from 2a to the end of the cross terms
+    // phase 2: Gs lives from 2a to the end of 2f
     static constexpr size_t P2_GS = 0;                                       // f32 [C][LF]
     static constexpr size_t P2_A = P2_GS + sz(C, LF, 4);
-    //   2b-2e
+    //   2a-2e
     static constexpr size_t P2_DWT = P2_A;                                   // T [D][LC]
     static constexpr size_t P2_DWL = P2_DWT + sz(D, LC, sizeof(T));          // T [C][LT]
     static constexpr size_t P2_KG = P2_DWL + sz(C, LT, sizeof(T));           // T [C][LT]
     static constexpr size_t P2_DAL = P2_KG + sz(C, LT, sizeof(T));           // T [C][LC]
     static constexpr size_t P2_T1T = P2_DAL + sz(C, LC, sizeof(T));          // T [C][LC]
     static constexpr size_t P2_B_END = P2_T1T + sz(C, LC, sizeof(T));
-    //   2e-2f: dAqk / dAkk operands (row-major and transposed) over the dead
-    //   dw / k 2^G / dA buffers; they must stay clear of T1T, still read in 2e
-    static constexpr size_t P2_DAQ = P2_A;                                   // T [C][LC] x4
-    static constexpr size_t P2_DA_END = P2_DAQ + 4 * sz(C, LC, sizeof(T));
-    //   2f: prescaled cross operands for one boundary and one D chunk of DH
-    //   columns: k^T [DH][rup(rho)], q^T and (beta k)^T [DH][rup(C-rho)]
-    static constexpr int DH = sizeof(T) == 4 ? 32 : 64;
-    static constexpr int cross_cols(int rho) { return rup(rho) + 2 * rup(C - rho) + 3 * pad<T>(); }
-    static constexpr int max_cross_cols() {
-        int m = 0;
-        for (int rho = 16; rho < C; rho += 16) m = cross_cols(rho) > m ? cross_cols(rho) : m;
-        return m;
-    }
+    //   2a: cumsum segment totals f32 [NT/D][D] in the dw region (written in 2b)
+    static constexpr size_t P2_SEG = P2_DWT;
+    //   2e-2f: dAqk / dAkk [C][LC] each, over the dead dw / k 2^G / dA buffers;
+    //   they must stay clear of T1T, still read in 2e
+    static constexpr size_t P2_DAQ = P2_A;
+    static constexpr size_t P2_DA_END = P2_DAQ + 2 * sz(C, LC, sizeof(T));
+    //   2f: scaled operands of one column half, transposed: k Eout, k / Ein,
+    //   q Ein, beta k Ein, each [D/2][LC]
     static constexpr size_t P2_X = P2_DA_END;
-    static constexpr size_t P2_X_END = P2_X + sz(DH, max_cross_cols(), sizeof(T));
-    // phase 3: three fp32 exchange buffers [C][LF] for the diagonal pass
-    static constexpr size_t P3_EX = 0;
-    static constexpr size_t P3_END = 3 * sz(C, LF, 4);
-    static constexpr size_t U_BYTES = cmax(cmax(P1_END, cmax(P2_B_END, P2_X_END)), P3_END);
+    static constexpr size_t P2_X_END = P2_X + 4 * sz(D / 2, LC, sizeof(T));
+    // epilogue: dq, dk [C][LT] and dg f32 [C][LF] staged for row-contiguous stores
+    static constexpr size_t E_DQ = 0;
+    static constexpr size_t E_DK = E_DQ + sz(C, LT, sizeof(T));
+    static constexpr size_t E_DG = E_DK + sz(C, LT, sizeof(T));
+    static constexpr size_t E_END = E_DG + sz(C, LF, 4);
+    static constexpr size_t U_BYTES = cmax(cmax(P1_END, P2_B_END), cmax(P2_X_END, E_END));
     static constexpr size_t TOTAL = U_OFF + U_BYTES;
     static_assert(P2_DA_END <= P2_T1T, "dAqk/dAkk operands must not overlap T1T");
+    static_assert(size_t(4) * C * 16 <= sz(D, LC, sizeof(T)), "cumsum segment totals fit the dw region");
     static_assert(TOTAL <= 163840, "LDS budget of gdr_chunk_bwd");
 };
 
@@ -114,6 +119,25 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_rows(const T* p, long ld,
     return f;
 }
 
+// Rows 0..len-1 of the staged dq, dk tiles ([C][D + pad] in LDS) to the
+// token-major outputs, 16 bytes per access.
+template <typename T, int C, int D, int NT>
+__device__ __forceinline__ void store_rows(const Params& p, const T* dqS, const T* dkS, int tok0, int len,
+                                           int hk, int tid) {
+    constexpr int V8 = 16 / sizeof(T), LT = D + pad<T>();
+    for (int e = tid; e < C * (D / V8); e += NT) {
+        const int r = e / (D / V8), c = (e % (D / V8)) * V8;
+        if (r < len) {
+            const size_t o = ((size_t)(tok0 + r) * p.Hg + hk) * D + c;
+            st16(static_cast<T*>(p.dq) + o, ld16(dqS + r * LT + c));
+            st16(static_cast<T*>(p.dk) + o, ld16(dkS + r * LT + c));
+        }
+    }
+}
+
+// Diagonal blocks use the MFMA form while |G_r - G_16b| <= this bound (log2).
+constexpr float kDiagGuard = 64.f;
+
 template <typename T, int C, int D, bool SCALAR, bool GROUPED>
 __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     using L = BwdLds<T, C, D>;
@@ -127,12 +151,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     T* const qL0 = reinterpret_cast<T*>(smem + L::Q_OFF);
     T* const kL0 = reinterpret_cast<T*>(smem + L::K_OFF);
     float* bs = reinterpret_cast<float*>(smem + L::BETA_OFF);
-    float* dbS = reinterpret_cast<float*>(smem + L::DB_OFF);     // [4][C]: MFMA halves, diagonal halves
+    float* dbS = reinterpret_cast<float*>(smem + L::DB_OFF);     // [2][C] per column half
+    float* dgR = reinterpret_cast<float*>(smem + L::DGR_OFF);    // [2][C] per column half
     float* dGl = reinterpret_cast<float*>(smem + L::GL_OFF);
     float* dGlw = reinterpret_cast<float*>(smem + L::GLW_OFF);
     float* btot = reinterpret_cast<float*>(smem + L::BT_OFF);
-    float* dqD = reinterpret_cast<float*>(smem + L::DIAG_OFF);   // [NB][16 s][16 r] dAqk
-    float* dkD = dqD + NB * 256;                                   // [NB][16 s][16 r] dAkk
     char* const U0 = smem + L::U_OFF;
 
     const int j = blockIdx.x, hk = blockIdx.y;
@@ -161,14 +184,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         st16(kL0 + r * LT + d0, kv);
     }
 
-    // diagonal-pass layout: lane owns column dcol (when lane < D/2) and the
-    // 16 rows of block rb; GROUPED keeps fp32 group sums of dq, dk there
-    const bool colact = l < DH2;
-    const int dcol = cd0 + (colact ? l : 0);
-    float dq_tot[GROUPED ? 16 : 1], dk_tot[GROUPED ? 16 : 1];
+    // GROUPED: fp32 group sums of dq, dk in this wave's accumulator tiles
+    f32x4 dq_tot[GROUPED ? NTD : 1], dk_tot[GROUPED ? NTD : 1];
     if constexpr (GROUPED) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { dq_tot[r] = 0.f; dk_tot[r] = 0.f; }
+        for (int t = 0; t < NTD; ++t) { dq_tot[t] = zero4(); dk_tot[t] = zero4(); }
     }
 
     // One value head per call of `head`. With G == 1 there is no loop at all:
@@ -297,31 +317,45 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         __syncthreads();  // phase-1 LDS is dead from here
 
         // ================= phase 2 =================
+        // 2a: G = chunk-local inclusive cumsum of g, one column and NT/D row
+        // segments per thread, and k 2^G
         float* Gs = reinterpret_cast<float*>(U + L::P2_GS);
-        for (int e = tid; e < C * (D / 4); e += NT) {
-            const int r = e / (D / 4), d0 = (e % (D / 4)) * 4;
-            f32x4 gv = zero4();
-            if (r < len) {
-                if constexpr (SCALAR) {
-                    const float s2 = p.g[(size_t)(tok0 + r) * p.H + h];
-                    gv = f32x4{s2, s2, s2, s2};
-                } else {
-                    gv = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + r) * p.H + h) * D + d0);
+        T* kgL = reinterpret_cast<T*>(U + L::P2_KG);
+        {
+            constexpr int NSEG = NT / D, SR = C / NSEG;
+            static_assert(NT % D == 0 && C % NSEG == 0, "cumsum segments");
+            float* segt = reinterpret_cast<float*>(U + L::P2_SEG);
+            const int d = tid % D, sg = tid / D, rs0 = sg * SR;
+            float gl[SR];
+            float run = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < SR; ++jj) {
+                const int r = rs0 + jj;
+                float gv = 0.f;
+                if (r < len) {
+                    if constexpr (SCALAR) gv = p.g[(size_t)(tok0 + r) * p.H + h];
+                    else gv = p.g[((size_t)(tok0 + r) * p.H + h) * D + d];
                 }
+                run += gv;
+                gl[jj] = run;
             }
-            *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = gv;
-        }
-        __syncthreads();
-        if (tid < D) {
-            float s2 = 0.f;
-            for (int r = 0; r < C; ++r) { s2 += Gs[r * LF + tid]; Gs[r * LF + tid] = s2; }
+            segt[sg * D + d] = run;
+            __syncthreads();
+            float off = 0.f;
+            for (int s2 = 0; s2 < sg; ++s2) off += segt[s2 * D + d];
+#pragma unroll
+            for (int jj = 0; jj < SR; ++jj) {
+                const int r = rs0 + jj;
+                const float G = gl[jj] + off;
+                Gs[r * LF + d] = G;
+                kgL[r * LT + d] = from_f32<T>(to_f32(kL[r * LT + d]) * fast_exp2(G));
+            }
         }
         __syncthreads();
 
-        // 2b: post-factors, dw -> LDS, k 2^G -> LDS
+        // 2b: post-factors, dw -> LDS
         T* dwT = reinterpret_cast<T*>(U + L::P2_DWT);
         T* dwL = reinterpret_cast<T*>(U + L::P2_DWL);
-        T* kgL = reinterpret_cast<T*>(U + L::P2_KG);
         f32x4 Pq[NTD], Pk[NTD], PG[NTD];
 #pragma unroll
         for (int t = 0; t < NTD; ++t) {
@@ -348,10 +382,6 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             store4<T>(dwT + c * LC + rr, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dwL[(rr + i) * LT + c] = from_f32<T>(-dwP[t][i]);
-        }
-        for (int e = tid; e < C * D; e += NT) {
-            const int r = e / D, d = e % D;
-            kgL[r * LT + d] = from_f32<T>(to_f32(kL[r * LT + d]) * fast_exp2(Gs[r * LF + d]));
         }
         __syncthreads();
         // 2c: dk^ = A^T dw ; dA' += dw (k 2^G)^T
@@ -397,11 +427,10 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             }
         }
         __syncthreads();
-        // 2e: dAkk = -StrictLower(A^T T1); dAqk = scale Lower_incl(...)
+        // 2e: dAkk = -StrictLower(A^T T1); dAqk = scale Lower_incl(do X^T), both
+        // row-major [r][s] for the intra-chunk products
         T* dAqL = reinterpret_cast<T*>(U + L::P2_DAQ);
-        T* dAqT = dAqL + C * LC;
-        T* dAkL = dAqT + C * LC;
-        T* dAkT = dAkL + C * LC;
+        T* dAkL = dAqL + C * LC;
         {
             f32x4 dAk[NTC];
 #pragma unroll
@@ -411,241 +440,316 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
                 const int s = cc0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
-                float aq[4], ak[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rr + i;
-                    aq[i] = s <= r ? p.scale * dAq[t][i] : 0.f;
-                    ak[i] = s < r ? -dAk[t][i] : 0.f;
-                    dAqL[r * LC + s] = from_f32<T>(aq[i]);
-                    dAkL[r * LC + s] = from_f32<T>(ak[i]);
-                    if (s >= r0 && s < r0 + 16) {  // diagonal block, fp32 for the VALU pass: [s][r]
-                        dqD[rb * 256 + (s - r0) * 16 + (r - r0)] = aq[i];
-                        dkD[rb * 256 + (s - r0) * 16 + (r - r0)] = ak[i];
-                    }
+                    dAqL[r * LC + s] = from_f32<T>(s <= r ? p.scale * dAq[t][i] : 0.f);
+                    dAkL[r * LC + s] = from_f32<T>(s < r ? -dAk[t][i] : 0.f);
                 }
-                store4<T>(dAqT + s * LC + rr, aq[0], aq[1], aq[2], aq[3]);
-                store4<T>(dAkT + s * LC + rr, ak[0], ak[1], ak[2], ak[3]);
             }
         }
-        __syncthreads();
 
-        // 2f: cross-block terms through each boundary rho = 16 ib, DH columns
-        // at a time (the waves of the matching column half do the MFMA work)
-        constexpr int NTH = L::DH / 16;
-        for (int ib = 1; ib < NB; ++ib) {
-            const int rho = 16 * ib;
-            const int kbn = L::rup(rho);                  // row-side reduction length
-            const int kcn = L::rup(C - rho);              // col-side reduction length
-            const int kcb = C - kcn;                      // col-side reduction start
-            const int lkb = kbn + pad<T>(), lkc = kcn + pad<T>();
-            T* kbT = reinterpret_cast<T*>(U + L::P2_X);   // [DH][lkb]  k_s 2^(G_rho - G_s), s < rho
-            T* qbT = kbT + L::DH * lkb;                   // [DH][lkc]  q_r 2^(G_r - G_rho), r >= rho
-            T* kbbT = qbT + L::DH * lkc;                  // [DH][lkc]  beta_r k_r 2^(G_r - G_rho)
-            for (int dh0 = 0; dh0 < D; dh0 += L::DH) {
-                for (int e = tid; e < L::DH * kbn; e += NT) {
-                    const int dd = e / kbn, s2 = e % kbn, d = dh0 + dd;
-                    float x = 0.f;
-                    if (s2 < rho) x = to_f32(kL[s2 * LT + d]) * fast_exp2(Gs[rho * LF + d] - Gs[s2 * LF + d]);
-                    kbT[dd * lkb + s2] = from_f32<T>(x);
+        // 2f: intra-chunk gradient on MFMA, one column half at a time: all
+        // threads scale the operands of the half, the waves owning it multiply
+        T* kET = reinterpret_cast<T*>(U + L::P2_X);   // [DH2][LC] k_s Eout_s
+        T* kIT = kET + DH2 * LC;                        // [DH2][LC] k_s / Ein_s (exponent clamped)
+        T* qET = kIT + DH2 * LC;                        // [DH2][LC] q_r Ein_r
+        T* bkET = qET + DH2 * LC;                       // [DH2][LC] beta_r k_r Ein_r
+        for (int hf = 0; hf < 2; ++hf) {
+            const int dh0 = hf * DH2;
+            __syncthreads();  // dA written (hf = 0) / previous half's operands read (hf = 1)
+            for (int e = tid; e < DH2 * (C / 4); e += NT) {
+                const int dd = e % DH2, s0 = (e / DH2) * 4, d = dh0 + dd;
+                const int b0 = s0 & ~15;
+                const bool has_next = b0 + 16 < C;
+                const float Gb = Gs[b0 * LF + d];
+                const float Gn = has_next ? Gs[(b0 + 16) * LF + d] : 0.f;
+                float ke[4], ki[4], qe[4], bke[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int s = s0 + jj;
+                    const float G = Gs[s * LF + d];
+                    const float kv = to_f32(kL[s * LT + d]);
+                    const float ein = fast_exp2(G - Gb);
+                    ke[jj] = has_next ? kv * fast_exp2(Gn - G) : 0.f;
+                    ki[jj] = kv * fast_exp2(fminf(Gb - G, kDiagGuard));
+                    qe[jj] = to_f32(qL[s * LT + d]) * ein;
+                    bke[jj] = bs[s] * kv * ein;
                 }
-                for (int e = tid; e < L::DH * kcn; e += NT) {
-                    const int dd = e / kcn, rr = e % kcn, r = kcb + rr, d = dh0 + dd;
-                    float xq = 0.f, xk = 0.f;
-                    if (r >= rho) {
-                        const float f = fast_exp2(Gs[r * LF + d] - Gs[rho * LF + d]);
-                        xq = to_f32(qL[r * LT + d]) * f;
-                        xk = bs[r] * to_f32(kL[r * LT + d]) * f;
+                store4<T>(kET + dd * LC + s0, ke[0], ke[1], ke[2], ke[3]);
+                store4<T>(kIT + dd * LC + s0, ki[0], ki[1], ki[2], ki[3]);
+                store4<T>(qET + dd * LC + s0, qe[0], qe[1], qe[2], qe[3]);
+                store4<T>(bkET + dd * LC + s0, bke[0], bke[1], bke[2], bke[3]);
+            }
+            __syncthreads();
+            if (ch != hf) continue;
+            const int l = opaque_lane_id();  // see the head body
+            // G of this wave's rows and of its block's first row; the guard
+            float gr[NTD][4], grho[NTD];
+            float rmax = 0.f;
+#pragma unroll
+            for (int t = 0; t < NTD; ++t) {
+                const int c = cd0 + 16 * t + acc_col(l);
+                grho[t] = Gs[r0 * LF + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    gr[t][i] = Gs[(r0 + acc_row(i, l)) * LF + c];
+                    rmax = fmaxf(rmax, fabsf(gr[t][i] - grho[t]));
+                }
+            }
+            const bool diag_mfma = wave_max(rmax) <= kDiagGuard;
+
+            // row side: accq, acck of rows r in block rb
+            {
+                const int l = opaque_lane_id();
+                f32x4 aq[NTD], ak[NTD];
+#pragma unroll
+                for (int t = 0; t < NTD; ++t) { aq[t] = zero4(); ak[t] = zero4(); }
+                for (int b1 = 0; b1 < rb; ++b1) {
+                    if (b1 > 0) {
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
+                            const float ph = fast_exp2(Gs[16 * (b1 + 1) * LF + c] - Gs[16 * b1 * LF + c]);
+                            aq[t] *= ph;
+                            ak[t] *= ph;
+                        }
                     }
-                    qbT[dd * lkc + rr] = from_f32<T>(xq);
-                    kbbT[dd * lkc + rr] = from_f32<T>(xk);
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) {
+                        aq[t] = mma16<T, false>(aq[t], dAqL, LC, r0, 16 * b1, kET, LC, 16 * t, 16 * b1, l);
+                        ak[t] = mma16<T, false>(ak[t], dAkL, LC, r0, 16 * b1, kET, LC, 16 * t, 16 * b1, l);
+                    }
                 }
-                __syncthreads();
-                // a wave's column half lies entirely inside or outside the D chunk
-                static_assert(L::DH % DH2 == 0, "column halves must tile the D chunks");
-                if (cd0 >= dh0 && cd0 < dh0 + L::DH) {
-                    const int bt0 = cd0 - dh0;   // operand row of this wave's first tile
-                    if (rb == ib) {  // row side of target block ib
-                        f32x4 aq[NTD], ak[NTD];
+                if (diag_mfma) {
 #pragma unroll
-                        for (int t = 0; t < NTD; ++t) { aq[t] = zero4(); ak[t] = zero4(); }
-                        for (int k0 = 0; k0 < kbn; k0 += kstep<T>()) {
-                            const auto fq = frag_kc(dAqL, LC, r0, k0, l);
-                            const auto fk = frag_kc(dAkL, LC, r0, k0, l);
+                    for (int t = 0; t < NTD; ++t) {
+                        aq[t] = mma16<T, false>(aq[t], dAqL, LC, r0, r0, kIT, LC, 16 * t, r0, l);
+                        ak[t] = mma16<T, false>(ak[t], dAkL, LC, r0, r0, kIT, LC, 16 * t, r0, l);
+                    }
+                }
 #pragma unroll
-                            for (int t = 0; t < NTD; ++t) {
-                                const auto b = frag_kc(kbT, lkb, bt0 + 16 * t, k0, l);
-                                aq[t] = Mfma<T>::mma(fq, b, aq[t]);
-                                ak[t] = Mfma<T>::mma(fk, b, ak[t]);
-                            }
+                for (int t = 0; t < NTD; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float ein = fast_exp2(gr[t][i] - grho[t]);
+                        aq[t][i] *= ein;
+                        ak[t][i] *= ein;
+                    }
+                }
+                if (!diag_mfma) {  // exact diagonal block, one exp2 per (r, s, d)
+                    for (int j2 = 0; j2 < 16; ++j2) {
+                        const int s = r0 + j2;
+                        float aqs[4], aks[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = r0 + acc_row(i, l);
+                            aqs[i] = to_f32(dAqL[r * LC + s]);
+                            aks[i] = to_f32(dAkL[r * LC + s]);
                         }
 #pragma unroll
                         for (int t = 0; t < NTD; ++t) {
                             const int c = cd0 + 16 * t + acc_col(l);
+                            const float ks = to_f32(kL[s * LT + c]), gsv = Gs[s * LF + c];
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const int r = r0 + acc_row(i, l);
-                                const float f = fast_exp2(Gs[r * LF + c] - Gs[rho * LF + c]);
-                                const float xq = f * aq[t][i], xk = f * ak[t][i];
-                                const float qv = to_f32(qL[r * LT + c]), kv = to_f32(kL[r * LT + c]);
-                                Pq[t][i] += xq;
-                                Pk[t][i] += bs[r] * xk;
-                                PG[t][i] += kLn2 * (qv * xq + bs[r] * kv * xk);
-                                dbp[i] += kv * xk;
-                            }
-                        }
-                    }
-                    if (rb == ib - 1) {  // column side of source block ib-1
-                        f32x4 dk[NTD];
-#pragma unroll
-                        for (int t = 0; t < NTD; ++t) dk[t] = zero4();
-                        for (int k0 = 0; k0 < kcn; k0 += kstep<T>()) {
-                            const auto fq = frag_kc(dAqT, LC, r0, kcb + k0, l);
-                            const auto fk = frag_kc(dAkT, LC, r0, kcb + k0, l);
-#pragma unroll
-                            for (int t = 0; t < NTD; ++t) {
-                                dk[t] = Mfma<T>::mma(fq, frag_kc(qbT, lkc, bt0 + 16 * t, k0, l), dk[t]);
-                                dk[t] = Mfma<T>::mma(fk, frag_kc(kbbT, lkc, bt0 + 16 * t, k0, l), dk[t]);
-                            }
-                        }
-#pragma unroll
-                        for (int t = 0; t < NTD; ++t) {
-                            const int c = cd0 + 16 * t + acc_col(l);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int s2 = r0 + acc_row(i, l);
-                                const float x = fast_exp2(Gs[rho * LF + c] - Gs[s2 * LF + c]) * dk[t][i];
-                                Pk[t][i] += x;
-                                PG[t][i] -= kLn2 * to_f32(kL[s2 * LT + c]) * x;
+                                if (j2 <= acc_row(i, l)) {
+                                    const float e = ks * fast_exp2(gr[t][i] - gsv);
+                                    aq[t][i] += aqs[i] * e;
+                                    ak[t][i] += aks[i] * e;
+                                }
                             }
                         }
                     }
                 }
-                __syncthreads();
+#pragma unroll
+                for (int t = 0; t < NTD; ++t) {
+                    const int c = cd0 + 16 * t + acc_col(l);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = r0 + acc_row(i, l);
+                        const float qv = to_f32(qL[r * LT + c]), kv = to_f32(kL[r * LT + c]), br = bs[r];
+                        Pq[t][i] += aq[t][i];
+                        Pk[t][i] += br * ak[t][i];
+                        PG[t][i] += kLn2 * (qv * aq[t][i] + br * kv * ak[t][i]);
+                        dbp[i] += kv * ak[t][i];
+                    }
+                }
+            }
+            // column side: dkt of sources s in block rb, later blocks first (Horner)
+            {
+                const int l = opaque_lane_id();
+                f32x4 dk[NTD];
+#pragma unroll
+                for (int t = 0; t < NTD; ++t) dk[t] = zero4();
+                for (int b2 = NB - 1; b2 > rb; --b2) {
+                    if (b2 < NB - 1) {
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
+                            dk[t] *= fast_exp2(Gs[16 * (b2 + 1) * LF + c] - Gs[16 * b2 * LF + c]);
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) {
+                        dk[t] = mma16<T, true>(dk[t], dAqL, LC, r0, 16 * b2, qET, LC, 16 * t, 16 * b2, l);
+                        dk[t] = mma16<T, true>(dk[t], dAkL, LC, r0, 16 * b2, bkET, LC, 16 * t, 16 * b2, l);
+                    }
+                }
+                if (diag_mfma) {
+                    if (rb < NB - 1) {
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
+                            dk[t] *= fast_exp2(Gs[(r0 + 16) * LF + c] - grho[t]);
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) {
+                        dk[t] = mma16<T, true>(dk[t], dAqL, LC, r0, r0, qET, LC, 16 * t, r0, l);
+                        dk[t] = mma16<T, true>(dk[t], dAkL, LC, r0, r0, bkET, LC, 16 * t, r0, l);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dk[t][i] *= fast_exp2(grho[t] - gr[t][i]);
+                    }
+                } else {
+                    if (rb < NB - 1) {
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
+                            const float gn = Gs[(r0 + 16) * LF + c];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) dk[t][i] *= fast_exp2(gn - gr[t][i]);
+                        }
+                    }
+                    for (int j2 = 0; j2 < 16; ++j2) {  // exact diagonal block
+                        const int r = r0 + j2;
+                        float aqs[4], aks[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int s = r0 + acc_row(i, l);
+                            aqs[i] = to_f32(dAqL[r * LC + s]);
+                            aks[i] = to_f32(dAkL[r * LC + s]);
+                        }
+                        const float br = bs[r];
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            const int c = cd0 + 16 * t + acc_col(l);
+                            const float qv = to_f32(qL[r * LT + c]), bkv = br * to_f32(kL[r * LT + c]);
+                            const float gv = Gs[r * LF + c];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                if (j2 >= acc_row(i, l)) {
+                                    const float e = fast_exp2(gv - gr[t][i]);
+                                    dk[t][i] += (aqs[i] * qv + aks[i] * bkv) * e;
+                                }
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NTD; ++t) {
+                    const int c = cd0 + 16 * t + acc_col(l);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s = r0 + acc_row(i, l);
+                        Pk[t][i] += dk[t][i];
+                        PG[t][i] -= kLn2 * to_f32(kL[s * LT + c]) * dk[t][i];
+                    }
+                }
             }
         }
-        // row sums of db over the 16 lanes of each row group (this column half)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x = dbp[i];
-            x += __shfl_xor(x, 1); x += __shfl_xor(x, 2);
-            x += __shfl_xor(x, 4); x += __shfl_xor(x, 8);
-            if ((l & 15) == 0) dbS[ch * C + r0 + acc_row(i, l)] = x;
-        }
-        __syncthreads();  // Gs and the cross operands are dead from here
 
-        // ================= phase 3: diagonal blocks (VALU) and epilogue =================
-        float* exq = reinterpret_cast<float*>(U + L::P3_EX);
-        float* exk = exq + C * LF;
-        float* exg = exk + C * LF;
-#pragma unroll
-        for (int t = 0; t < NTD; ++t) {
-            const int c = cd0 + 16 * t + acc_col(l);
+        // ================= epilogue (accumulator layout) =================
+        {
+            const int l = opaque_lane_id();
+            // db: row sums of the partials over this wave's column half
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = r0 + acc_row(i, l);
-                exq[r * LF + c] = Pq[t][i];
-                exk[r * LF + c] = Pk[t][i];
-                exg[r * LF + c] = PG[t][i];
+                float x = dbp[i];
+                x += __shfl_xor(x, 1); x += __shfl_xor(x, 2);
+                x += __shfl_xor(x, 4); x += __shfl_xor(x, 8);
+                if ((l & 15) == 0) dbS[ch * C + r0 + acc_row(i, l)] = x;
+            }
+            // dG_last joins the last row of the chunk
+            const int lg = l >> 4;
+            if (rb == NB - 1 && lg == 3) {
+#pragma unroll
+                for (int t = 0; t < NTD; ++t) {
+                    const int c = cd0 + 16 * t + acc_col(l);
+                    float sl = dGl[c];
+                    for (int b2 = 0; b2 < NB; ++b2) sl += dGlw[b2 * D + c];
+                    PG[t][3] += sl;
+                }
+            }
+            // reverse cumsum of dG over the chunk, per column: the lane's 4 rows,
+            // then the later lane groups, then the later row blocks
+#pragma unroll
+            for (int t = 0; t < NTD; ++t) {
+                const int c = cd0 + 16 * t + acc_col(l);
+                PG[t][2] += PG[t][3];
+                PG[t][1] += PG[t][2];
+                PG[t][0] += PG[t][1];
+                const float tot = PG[t][0];
+                const float u1 = __shfl_down(tot, 16), u2 = __shfl_down(tot, 32), u3 = __shfl_down(tot, 48);
+                const float ex = (lg < 3 ? u1 : 0.f) + (lg < 2 ? u2 : 0.f) + (lg < 1 ? u3 : 0.f);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) PG[t][i] += ex;
+                if (lg == 0) btot[rb * D + c] = PG[t][0];
+            }
+            __syncthreads();  // block totals, db partials; 2f LDS is dead
+#pragma unroll
+            for (int t = 0; t < NTD; ++t) {
+                const int c = cd0 + 16 * t + acc_col(l);
+                float suf = 0.f;
+                for (int b2 = rb + 1; b2 < NB; ++b2) suf += btot[b2 * D + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) PG[t][i] += suf;
+            }
+            // stage dq, dk, dg for row-contiguous stores
+            T* dqS = reinterpret_cast<T*>(U + L::E_DQ);
+            T* dkS = reinterpret_cast<T*>(U + L::E_DK);
+            float* dgS = reinterpret_cast<float*>(U + L::E_DG);
+#pragma unroll
+            for (int t = 0; t < NTD; ++t) {
+                const int c = cd0 + 16 * t + acc_col(l);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = r0 + acc_row(i, l);
+                    if constexpr (!SCALAR) dgS[r * LF + c] = PG[t][i];
+                    if constexpr (GROUPED) {
+                        dq_tot[t][i] += Pq[t][i];
+                        dk_tot[t][i] += Pk[t][i];
+                    } else {
+                        dqS[r * LT + c] = from_f32<T>(Pq[t][i]);
+                        dkS[r * LT + c] = from_f32<T>(Pk[t][i]);
+                    }
+                }
+            }
+            if constexpr (SCALAR) {  // dg_r = sum over channels of the suffix sums
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) x += PG[t][i];
+                    x += __shfl_xor(x, 1); x += __shfl_xor(x, 2);
+                    x += __shfl_xor(x, 4); x += __shfl_xor(x, 8);
+                    if ((l & 15) == 0) dgR[ch * C + r0 + acc_row(i, l)] = x;
+                }
+            }
+            __syncthreads();
+            if constexpr (!GROUPED) store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
+            if constexpr (!SCALAR) {
+                for (int e = tid; e < C * (D / 4); e += NT) {
+                    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+                    if (r < len)
+                        *reinterpret_cast<f32x4*>(p.dg + ((size_t)(tok0 + r) * p.H + h) * D + c) =
+                            *reinterpret_cast<const f32x4*>(dgS + r * LF + c);
+                }
             }
         }
-        __syncthreads();
-        {
-            const int d = dcol;
-            float qr[16], kr[16], ar[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = r0 + r;
-                qr[r] = to_f32(qL[rr * LT + d]);
-                kr[r] = to_f32(kL[rr * LT + d]);
-                float gv = 0.f;
-                if (rr < len) {
-                    if constexpr (SCALAR) gv = p.g[(size_t)(tok0 + rr) * p.H + h];
-                    else gv = p.g[((size_t)(tok0 + rr) * p.H + h) * D + d];
-                }
-                ar[r] = fast_exp2(gv);
-            }
-            float accq[16], acck[16], dkt[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { accq[r] = 0.f; acck[r] = 0.f; }
-            // the fp32 16x16 blocks of dAqk / dAkk, spread over the wave: lane L
-            // holds entries 4L..4L+3 of [s][r]; each (r, s) value is fetched with
-            // v_readlane into a scalar register (wave-uniform operand)
-            const f32x4 aqv = *reinterpret_cast<const f32x4*>(dqD + rb * 256 + 4 * l);
-            const f32x4 akv = *reinterpret_cast<const f32x4*>(dkD + rb * 256 + 4 * l);
-#pragma unroll
-            for (int s2 = 0; s2 < 16; ++s2) {
-                // keep each source row's loads and math together (no hoisting of
-                // the whole 16x16 block's loads into registers)
-                float E = 1.f, acc = 0.f;
-                const float ks = kr[s2];
-#pragma unroll
-                for (int r = s2; r < 16; ++r) {
-                    if (r > s2) E *= ar[r];          // E = 2^(G_r - G_s)
-                    const float aq = lane_value(aqv, s2 * 16 + r), ak = lane_value(akv, s2 * 16 + r);
-                    const float tq = ks * E;
-                    accq[r] += aq * tq;
-                    acck[r] += ak * tq;
-                    acc += (aq * qr[r] + ak * bs[r0 + r] * kr[r]) * E;
-                }
-                dkt[s2] = acc;
-            }
-            // combine with the MFMA partials; dG in place in exg; the diagonal
-            // db terms k_r . acck_r in place in exq (summed per row below)
-            float gsum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = r0 + r;
-                const float br = bs[rr];
-                const float dqv = exq[rr * LF + d] + accq[r];
-                const float dkv = exk[rr * LF + d] + br * acck[r] + dkt[r];
-                float dG = exg[rr * LF + d] + kLn2 * (qr[r] * accq[r] + kr[r] * (br * acck[r] - dkt[r]));
-                if (rb == NB - 1 && r == 15) {  // dG_last joins the last row of the chunk
-                    float sl = dGl[d];
-                    for (int b2 = 0; b2 < NB; ++b2) sl += dGlw[b2 * D + d];
-                    dG += sl;
-                }
-                if constexpr (GROUPED) {
-                    dq_tot[r] += dqv;
-                    dk_tot[r] += dkv;
-                } else if (colact && rr < len) {
-                    const size_t o = ((size_t)(tok0 + rr) * p.Hg + hk) * D + d;
-                    static_cast<T*>(p.dq)[o] = from_f32<T>(dqv);
-                    static_cast<T*>(p.dk)[o] = from_f32<T>(dkv);
-                }
-                gsum += dG;
-                if (colact) {
-                    exg[rr * LF + d] = dG;
-                    exq[rr * LF + d] = kr[r] * acck[r];
-                }
-            }
-            if (colact) btot[rb * D + d] = gsum;
-        }
-        __syncthreads();
-        // reverse cumsum of dG over the chunk, per column: in place in exg
-        if (colact) {
-            const int d = dcol;
-            float suf = 0.f;
-            for (int b2 = rb + 1; b2 < NB; ++b2) suf += btot[b2 * D + d];
-            for (int r = 15; r >= 0; --r) {
-                const int rr = r0 + r;
-                suf += exg[rr * LF + d];
-                if constexpr (SCALAR) exg[rr * LF + d] = suf;
-                else if (rr < len) p.dg[((size_t)(tok0 + rr) * p.H + h) * D + d] = suf;
-            }
-        }
-        if constexpr (SCALAR) __syncthreads();
-        // per-row sums: db = MFMA partials + sum_d k . acck (diagonal);
-        // scalar gate: dg = sum over channels of the per-channel suffix sums
         if (tid < C && tid < len) {
-            float x = dbS[tid] + dbS[C + tid];
-            for (int d = 0; d < D; ++d) x += exq[tid * LF + d];
-            static_cast<T*>(p.db)[(size_t)(tok0 + tid) * p.H + h] = from_f32<T>(x);
-            if constexpr (SCALAR) {
-                float gsum2 = 0.f;
-                for (int d = 0; d < D; ++d) gsum2 += exg[tid * LF + d];
-                p.dg[(size_t)(tok0 + tid) * p.H + h] = gsum2;
-            }
+            static_cast<T*>(p.db)[(size_t)(tok0 + tid) * p.H + h] = from_f32<T>(dbS[tid] + dbS[C + tid]);
+            if constexpr (SCALAR) p.dg[(size_t)(tok0 + tid) * p.H + h] = dgR[tid] + dgR[C + tid];
         }
     };
     if constexpr (GROUPED) {
@@ -654,17 +758,22 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         head(0);
     }
     if constexpr (GROUPED) {
-        if (colact) {
+        // dq, dk group sums: staged in LDS, stored row-contiguous
+        __syncthreads();
+        T* dqS = reinterpret_cast<T*>(U0 + L::E_DQ);
+        T* dkS = reinterpret_cast<T*>(U0 + L::E_DK);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = r0 + r;
-                if (rr < len) {
-                    const size_t o = ((size_t)(tok0 + rr) * p.Hg + hk) * D + dcol;
-                    static_cast<T*>(p.dq)[o] = from_f32<T>(dq_tot[r]);
-                    static_cast<T*>(p.dk)[o] = from_f32<T>(dk_tot[r]);
-                }
+        for (int t = 0; t < NTD; ++t) {
+            const int c = cd0 + 16 * t + acc_col(l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + acc_row(i, l);
+                dqS[r * LT + c] = from_f32<T>(dq_tot[t][i]);
+                dkS[r * LT + c] = from_f32<T>(dk_tot[t][i]);
             }
         }
+        __syncthreads();
+        store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
     }
 }
 

@@ -141,6 +141,75 @@ __device__ __forceinline__ float lane_value(f32x4 v, int idx) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---------------------------------------------------------------------------
+// 16x16 products with a reduction of exactly 16 (one 16-row block):
+// v_mfma_f32_16x16x16_{bf16,f16} (lane l holds A[l%16][4*(l/16) + 0..3],
+// B[4*(l/16) + 0..3][l%16]), or four 16x16x4 fp32 steps for fp32 operands.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma16;
+template <> struct Mfma16<__bf16> {
+    static constexpr int KL = 4, STEPS = 1;
+    using frag = bf16x4;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma16<_Float16> {
+    static constexpr int KL = 4, STEPS = 1;
+    using frag = f16x4;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma16<float> {
+    static constexpr int KL = 1, STEPS = 4;
+    using frag = float;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Step `st` fragment of a 16-long reduction, operand stored reduction-contiguous
+// (element (i, kk) at p[i*ld + kk]).
+template <typename T>
+__device__ __forceinline__ typename Mfma16<T>::frag frag16_kc(const T* p, int ld, int i0, int k0, int st, int l) {
+    using M = Mfma16<T>;
+    const T* q = p + (i0 + (l & 15)) * ld + k0 + 4 * st + (l >> 4) * M::KL;
+    return *reinterpret_cast<const typename M::frag*>(q);
+}
+// Same, operand stored with the reduction index as the row (element (i, kk) at p[kk*ld + i]).
+template <typename T>
+__device__ __forceinline__ typename Mfma16<T>::frag frag16_ks(const T* p, int ld, int i0, int k0, int st, int l) {
+    using M = Mfma16<T>;
+    typename M::frag f;
+    if constexpr (M::KL == 1) {
+        f = p[(k0 + 4 * st + (l >> 4)) * ld + i0 + (l & 15)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < M::KL; ++j) f[j] = p[(k0 + (l >> 4) * M::KL + j) * ld + i0 + (l & 15)];
+    }
+    return f;
+}
+// acc += A[i0.., k0..k0+16) * B[k0..k0+16, j0..), A reduction-contiguous (AT = false)
+// or stored transposed (AT = true: A(i, kk) at A[kk*lda + i]); B given as Bt[j][kk].
+template <typename T, bool AT>
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const T* A, int lda, int i0, int ak0,
+                                       const T* Bt, int ldb, int j0, int bk0, int l) {
+#pragma unroll
+    for (int st = 0; st < Mfma16<T>::STEPS; ++st) {
+        const auto a = AT ? frag16_ks(A, lda, i0, ak0, st, l) : frag16_kc(A, lda, i0, ak0, st, l);
+        acc = Mfma16<T>::mma(a, frag16_kc(Bt, ldb, j0, bk0, st, l), acc);
+    }
+    return acc;
+}
+
+// Maximum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // Row / column of element i (0..3) of an f32x4 accumulator tile held by this lane.
 __device__ __forceinline__ int acc_row(int i, int l = lane_id()) { return 4 * (l >> 4) + i; }
 __device__ __forceinline__ int acc_col(int l = lane_id()) { return l & 15; }

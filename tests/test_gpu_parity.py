@@ -101,6 +101,28 @@ def test_large_gates_x16():
     _check(errs, tu.tolerance(w))
 
 
+@pytest.mark.parametrize("gate_mult", [3.7, 32.0])
+def test_diagonal_guard_paths(gate_mult):
+    """In-block gate ranges around and far beyond the diagonal-block MFMA
+    guard (2^64): at x7.4 the default gates, 19 of 52 (block, column half)
+    pairs take the exact per-element path and the rest the MFMA path within
+    the same chunks; at x64 every block takes the exact path. (x16 above is
+    also all exact.)"""
+    w = scaled(KDA16, B=1, T=200, H=2, Hg=2, gate_mult=gate_mult, dht_std=0.1, seed=37)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
+def test_gdn_gqa_huge_gates():
+    """Scalar gate, GQA, C = 32, gates large enough for the exact diagonal path."""
+    w = scaled(GDN, B=1, T=150, H=4, Hg=2, gate_mult=8.0, seed=43)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
+def test_fp32_diagonal_guard_mixed():
+    w = scaled(TINY, T=130, gate_mult=3.7, h0_std=0.1, dht_std=0.1, seed=41)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
 def test_fp32_large_gates_x16():
     w = scaled(TINY, T=130, gate_mult=8.0, h0_std=0.1, dht_std=0.1, seed=23)
     _check(tu.parity(w), tu.tolerance(w))
