@@ -28,8 +28,8 @@
 // phi are applied to the accumulators between blocks (Horner); every exponent
 // is <= 0. Inside a diagonal block the source side needs 2^(G_16b - G_s) >= 1;
 // the MFMA form is used there when the block's gate range |G_r - G_16b| stays
-// within 2^64 for every column of the wave, else an exact VALU pass with one
-// exp2 per (r, s, d) (never reached at ordinary gate magnitudes). Finally
+// within 2^64 (2^8 for fp16 operands) for every column of the wave, else an
+// exact VALU pass with one exp2 per (r, s, d). Finally
 // dg = reverse cumsum of dG in the chunk (the page's fold_dg), dG_last collecting
 //   ln2 [2^G_last rowsum_v(h dh') + sum_r k_r dk~_r 2^(G_last - G_r)].
 #pragma once
@@ -135,8 +135,11 @@ __device__ __forceinline__ void store_rows(const Params& p, const T* dqS, const 
     }
 }
 
-// Diagonal blocks use the MFMA form while |G_r - G_16b| <= this bound (log2).
-constexpr float kDiagGuard = 64.f;
+// Diagonal blocks use the MFMA form while |G_r - G_16b| <= this bound (log2):
+// the operand k 2^range must stay finite and q 2^-range normal in T, so
+// 2^8 for fp16 (5 exponent bits), 2^64 for bf16 and fp32 (8 exponent bits).
+template <typename T>
+constexpr float diag_guard() { return __is_same(T, _Float16) ? 8.f : 64.f; }
 
 template <typename T, int C, int D, bool SCALAR, bool GROUPED>
 __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     const float kv = to_f32(kL[s * LT + d]);
                     const float ein = fast_exp2(G - Gb);
                     ke[jj] = has_next ? kv * fast_exp2(Gn - G) : 0.f;
-                    ki[jj] = kv * fast_exp2(fminf(Gb - G, kDiagGuard));
+                    ki[jj] = kv * fast_exp2(fminf(Gb - G, diag_guard<T>()));
                     qe[jj] = to_f32(qL[s * LT + d]) * ein;
                     bke[jj] = bs[s] * kv * ein;
                 }
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     rmax = fmaxf(rmax, fabsf(gr[t][i] - grho[t]));
                 }
             }
-            const bool diag_mfma = wave_max(rmax) <= kDiagGuard;
+            const bool diag_mfma = wave_max(rmax) <= diag_guard<T>();
 
             // row side: accq, acck of rows r in block rb
             {

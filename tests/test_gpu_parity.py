@@ -112,6 +112,13 @@ def test_diagonal_guard_paths(gate_mult):
     _check(tu.parity(w), tu.tolerance(w))
 
 
+def test_f16_diagonal_guard_mixed():
+    """fp16 operands keep the MFMA diagonal only within 2^8: at the default KDA
+    gates 44 of 52 (block, column half) pairs take the exact path, 8 the MFMA."""
+    w = scaled(KDA16, B=1, T=200, H=2, Hg=2, io_dtype=torch.float16, dht_std=0.1, seed=47)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
 def test_gdn_gqa_huge_gates():
     """Scalar gate, GQA, C = 32, gates large enough for the exact diagonal path."""
     w = scaled(GDN, B=1, T=150, H=4, Hg=2, gate_mult=8.0, seed=43)
