@@ -15,10 +15,12 @@
 // fp32. The two directions are independent and share one grid.
 //
 // The per-chunk operands (w, k~, u, q~, 2^G_last) are read straight from
-// global memory as MFMA fragments of the rows each wave owns, one chunk ahead
-// (software pipelining: the loads for chunk c+1 are in flight while chunk c
-// computes). Only the state and X / T (and do for the reverse direction)
-// pass through LDS, double-buffered, two barriers per chunk.
+// global memory as MFMA fragments of the rows each wave owns, NPF chunks
+// ahead into NPF fixed register sets (the chunk loop is unrolled NPF times so
+// that no register copy forces an early wait on a load in flight). Only the
+// state and X / T (and do for the reverse direction) pass through LDS,
+// double-buffered, two barriers per chunk; the stores of h_c and X_c (T_c) to
+// the workspace read those LDS tiles back as 16-byte row pieces.
 #pragma once
 #include "gdr_common.hpp"
 
@@ -39,27 +41,31 @@ struct SweepTiles {
     static __device__ __forceinline__ int xcol(int w, int j) { return XR >= 4 ? j : (w % (4 / XR)) * XCT + j; }
 };
 
-// Operands of one chunk, as the MFMA fragments / values this lane needs.
-template <typename T, int C, int D, int BV>
+// Operands of one chunk, as the MFMA fragments / raw values this lane needs
+// (kept in the operand type: a conversion at load time would wait for the load).
+template <typename T, int C, int D, int BV, int DIR>
 struct SweepOps {
     using S = SweepTiles<T, C, D, BV>;
     using F = typename Mfma<T>::frag;
-    F a1[S::XRT][D / S::KS];      // chunk-row product A operand: w (fwd) or k~ (rev)
-    F a2[S::SRW][C / S::KS];      // state update A operand: k~^T (fwd) or w^T (rev)
-    F a3[S::SRW][C / S::KS];      // reverse only: (scale q~)^T
-    float u[S::XRT][S::XCT][4];   // forward only: u at this lane's X elements
-    float gl[S::SRW][4];          // 2^G_last at this lane's state rows
+    using Q = typename Mfma<T>::quad;
     static constexpr int NDO = (C * (BV / (16 / sizeof(T))) + 255) / 256;
-    Vec16 dov[NDO];               // reverse only: this thread's 16-byte pieces of do
+    F a1[S::XRT][D / S::KS];                  // chunk-row product A operand: w (fwd) or k~ (rev)
+    F a2[S::SRW][C / S::KS];                  // state update A operand: k~^T (fwd) or w^T (rev)
+    F a3[DIR == 1 ? S::SRW : 1][C / S::KS];   // reverse: (scale q~)^T
+    Q u[DIR == 0 ? S::XRT : 1][S::XCT];       // forward: u at this lane's X elements
+    f32x4 gl[S::SRW];                         // 2^G_last at this lane's state rows
+    Vec16 dov[DIR == 1 ? NDO : 1];            // reverse: this thread's 16-byte pieces of do
 };
 
-template <typename T, int C, int D, int BV>
-__device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV>& o, const Params& p, int dir, int j,
-                                           int h, int v0, int w) {
+// Loads the operands of global chunk j (first token tok0, len real rows).
+template <typename T, int C, int D, int BV, int DIR>
+__device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const Params& p, int j, int tok0,
+                                           int len, int h, int v0, int w) {
     using S = SweepTiles<T, C, D, BV>;
+    using Q = typename Mfma<T>::quad;
     const size_t jh = (size_t)j * p.H + h;
-    const T* A1 = static_cast<const T*>(dir == 0 ? p.w : p.kt) + jh * C * D;
-    const T* A2 = static_cast<const T*>(dir == 0 ? p.ktT : p.wT) + jh * D * C;
+    const T* A1 = static_cast<const T*>(DIR == 0 ? p.w : p.kt) + jh * C * D;
+    const T* A2 = static_cast<const T*>(DIR == 0 ? p.ktT : p.wT) + jh * D * C;
 #pragma unroll
     for (int i = 0; i < S::XRT; ++i)
 #pragma unroll
@@ -70,10 +76,8 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV>& o, const Param
         for (int k = 0; k < C / S::KS; ++k) o.a2[i][k] = frag_kc(A2, C, 16 * (w * S::SRW + i), k * S::KS);
     const float* gl = p.glast + jh * D;
 #pragma unroll
-    for (int i = 0; i < S::SRW; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o.gl[i][e] = gl[16 * (w * S::SRW + i) + acc_row(e)];
-    if (dir == 0) {
+    for (int i = 0; i < S::SRW; ++i) o.gl[i] = *reinterpret_cast<const f32x4*>(gl + 16 * (w * S::SRW + i) + acc_row(0));
+    if constexpr (DIR == 0) {
         const T* uT = static_cast<const T*>(p.uT) + jh * D * C;
 #pragma unroll
         for (int i = 0; i < S::XRT; ++i)
@@ -81,8 +85,7 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV>& o, const Param
             for (int jj = 0; jj < S::XCT; ++jj) {
                 const int r = 16 * S::xrow(w, i) + acc_row(0);
                 const int c = v0 + 16 * S::xcol(w, jj) + acc_col();
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o.u[i][jj][e] = to_f32(uT[(size_t)c * C + r + e]);
+                o.u[i][jj] = *reinterpret_cast<const Q*>(uT + (size_t)c * C + r);
             }
     } else {
         const T* qsT = static_cast<const T*>(p.qsT) + jh * D * C;
@@ -90,52 +93,41 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV>& o, const Param
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
             for (int k = 0; k < C / S::KS; ++k) o.a3[i][k] = frag_kc(qsT, C, 16 * (w * S::SRW + i), k * S::KS);
-        // do rows of the chunk, this thread's 16-byte piece (zero past the sequence end)
+        // do rows of the chunk, this thread's 16-byte piece; rows past the
+        // sequence end read its last row (always valid) and are zeroed at use
         constexpr int V8 = 16 / sizeof(T);
-        const ChunkEntry ce = p.ctab[j];
 #pragma unroll
         for (int pi = 0; pi < o.NDO; ++pi) {
-            const int e = threadIdx.x + 256 * pi;
-            o.dov[pi] = Vec16{};
-            if (e < C * (BV / V8)) {
-                const int r = e / (BV / V8), cc = (e % (BV / V8)) * V8;
-                if (r < ce.len)
-                    o.dov[pi] = ld16(static_cast<const T*>(p.dout) + ((size_t)(ce.tok0 + r) * p.H + h) * D + v0 + cc);
-            }
+            const int e = min((int)threadIdx.x + 256 * pi, C * (BV / V8) - 1);  // spare threads: a valid duplicate
+            const int r = e / (BV / V8), cc = (e % (BV / V8)) * V8;
+            const int rr = min(r, len - 1);
+            o.dov[pi] = ld16(static_cast<const T*>(p.dout) + ((size_t)(tok0 + rr) * p.H + h) * D + v0 + cc);
         }
     }
 }
 
-template <typename T, int C, int D, int BV>
-__global__ __launch_bounds__(256) void gdr_sweep(Params p) {
+// One direction of the sweep for (sequence n, value head h, V tile at v0).
+template <typename T, int C, int D, int BV, int DIR, int NPF>
+__device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS, T* sX0, T* sX1, T* sDo0,
+                                          T* sDo1) {
     using S = SweepTiles<T, C, D, BV>;
-    constexpr int NVT = D / BV, SCT = S::SCT, KS = S::KS;
+    using Ops = SweepOps<T, C, D, BV, DIR>;
+    constexpr int SCT = S::SCT, KS = S::KS;
     constexpr int LS = D + pad<T>();                 // state^T rows [BV][LS]
     constexpr int LX = C + pad<T>();                 // X^T / -T^T / do^T rows [BV][LX]
     constexpr int V8 = 16 / sizeof(T);
-    __shared__ __attribute__((aligned(16))) T sS[BV * LS];
-    __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
-    __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
-
-    // Block order: the V tile varies slowest. Workgroups are dispatched to the
-    // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the NVT
-    // tiles of one (direction, sequence, head) land on the same XCD and share
-    // the chunk operands (w, k~, q~, do) through its L2.
-    const int ngroups = 2 * p.N * p.H;
-    const int vt = blockIdx.x / ngroups;
-    int bid = blockIdx.x % ngroups;
-    const int h = bid % p.H; bid /= p.H;
-    const int n = bid % p.N;
-    const int dir = bid / p.N;
-    const int v0 = vt * BV;
     const int w = wave_id();
     const int c0 = p.seq_off[n], c1 = p.seq_off[n + 1];
     const int nch = c1 - c0;
+    // chunk geometry of the sequence (the chunk table's, computed here so that
+    // no load of it sits between a prefetch and its use)
+    const int stok0 = p.varlen ? p.cu[n] : (int)(n * p.T);
+    const int slen = p.varlen ? p.cu[n + 1] - p.cu[n] : (int)p.T;
     const size_t sh = ((size_t)n * p.H + h) * D * D;
 
     f32x4 st[S::SRW][SCT];
     {   // initial state: h0 (forward) or dht (reverse), zero when absent
-        const float* init = dir == 0 ? p.h0 : p.dht;
+        const float* init = DIR == 0 ? p.h0 : p.dht;
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
@@ -146,45 +138,48 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
                     st[i][ct][e] = init ? init[sh + (size_t)d * D + c] : 0.f;
                 }
     }
+    // step k of this direction works on chunk `it` of the sequence
+    auto chunk_it = [&](int k) { return DIR == 0 ? k : nch - 1 - k; };
+    auto load = [&](Ops& o, int k) __attribute__((always_inline)) {
+        const int it = chunk_it(k < nch ? k : nch - 1);   // past the end: a redundant valid load
+        sweep_load<T, C, D, BV, DIR>(o, p, c0 + it, stok0 + it * C, min(C, slen - it * C), h, v0, w);
+    };
+    auto step = [&](const Ops& cur, const int k) __attribute__((always_inline)) {
+        const int it = chunk_it(k);
+        const size_t jh = (size_t)(c0 + it) * p.H + h;
+        T* sX = (k & 1) ? sX1 : sX0;
+        T* sDo = (k & 1) ? sDo1 : sDo0;
 
-    SweepOps<T, C, D, BV> cur, nxt;
-    auto chunk_of = [&](int it) { return dir == 0 ? c0 + it : c1 - 1 - it; };
-    if (nch > 0) sweep_load(cur, p, dir, chunk_of(0), h, v0, w);
-
-    for (int it = 0; it < nch; ++it) {
-        const int j = chunk_of(it);
-        const int buf = it & 1;
-        const size_t jh = (size_t)j * p.H + h;
-        if (it + 1 < nch) sweep_load(nxt, p, dir, chunk_of(it + 1), h, v0, w);
-
-        // 1. publish the incoming state: workspace (row-major, for the gradient
-        //    kernel) and LDS (transposed: B operand with K contiguous)
-        T* gS = static_cast<T*>(dir == 0 ? p.hbuf : p.dhbuf) + jh * D * D;
+        // 1. publish the incoming state to LDS (transposed: B operand with K
+        //    contiguous); do^T of this chunk's V tile for the reverse direction
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
             for (int ct = 0; ct < SCT; ++ct) {
                 const int d = 16 * (w * S::SRW + i) + acc_row(0), c = 16 * ct + acc_col();
-#pragma unroll
-                for (int e = 0; e < 4; ++e) gS[(size_t)(d + e) * D + v0 + c] = from_f32<T>(st[i][ct][e]);
                 store4<T>(sS + c * LS + d, st[i][ct][0], st[i][ct][1], st[i][ct][2], st[i][ct][3]);
             }
-        if (dir == 1) {  // do^T of this chunk's V tile
+        if constexpr (DIR == 1) {
+            const int len = min(C, slen - it * C);
 #pragma unroll
-            for (int pi = 0; pi < cur.NDO; ++pi) {
+            for (int pi = 0; pi < Ops::NDO; ++pi) {
                 const int e = threadIdx.x + 256 * pi;
                 if (e < C * (BV / V8)) {
                     const int r = e / (BV / V8), cc = (e % (BV / V8)) * V8;
-                    const T* xp = reinterpret_cast<const T*>(&cur.dov[pi]);
+                    // opaque here: keeps the element extraction (and the wait
+                    // for the load) from being hoisted to the previous chunk
+                    Vec16 dv = cur.dov[pi];
+                    asm volatile("" : "+v"(dv.w[0]), "+v"(dv.w[1]), "+v"(dv.w[2]), "+v"(dv.w[3]));
+                    const T* xp = reinterpret_cast<const T*>(&dv);
 #pragma unroll
-                    for (int q = 0; q < V8; ++q) sDo[buf][(cc + q) * LX + r] = xp[q];
+                    for (int q = 0; q < V8; ++q) sDo[(cc + q) * LX + r] = r < len ? xp[q] : T(0.f);
                 }
             }
         }
         __syncthreads();
 
-        // 2. chunk-row product: X = u - w h (fwd) or T = k~ dh (rev)
-        T* gX = static_cast<T*>(dir == 0 ? p.xbuf : p.tbuf) + jh * C * D;
+        // 2. chunk-row product: X = u - w h (fwd) or T = k~ dh (rev); forward
+        //    keeps +X, reverse keeps -T so the state update is a pure sum
 #pragma unroll
         for (int i = 0; i < S::XRT; ++i)
 #pragma unroll
@@ -192,18 +187,29 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
                 const int ct = S::xcol(w, jj);
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int k = 0; k < D / KS; ++k)
-                    acc = Mfma<T>::mma(cur.a1[i][k], frag_kc(sS, LS, 16 * ct, k * KS), acc);
+                for (int k2 = 0; k2 < D / KS; ++k2)
+                    acc = Mfma<T>::mma(cur.a1[i][k2], frag_kc(sS, LS, 16 * ct, k2 * KS), acc);
                 const int r = 16 * S::xrow(w, i) + acc_row(0), c = 16 * ct + acc_col();
                 float o[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = dir == 0 ? cur.u[i][jj][e] - acc[e] : acc[e];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) gX[(size_t)(r + e) * D + v0 + c] = from_f32<T>(o[e]);
-                // forward keeps +X; reverse keeps -T so the state update is a pure sum
-                const float sg = dir == 0 ? 1.f : -1.f;
-                store4<T>(sX[buf] + c * LX + r, sg * o[0], sg * o[1], sg * o[2], sg * o[3]);
+                for (int e = 0; e < 4; ++e) o[e] = DIR == 0 ? to_f32(cur.u[i][jj][e]) - acc[e] : -acc[e];
+                store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
             }
+        {   // the incoming state to the workspace, row-major: 8 columns per piece
+            T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D + v0;
+#pragma unroll
+            for (int pi = 0; pi < (D * BV / V8 + 255) / 256; ++pi) {
+                const int e = threadIdx.x + 256 * pi;
+                if (e < D * BV / V8) {
+                    const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                    Vec16 v;
+                    T* vp = reinterpret_cast<T*>(&v);
+#pragma unroll
+                    for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
+                    st16(gS + (size_t)d * D + c, v);
+                }
+            }
+        }
         __syncthreads();
 
         // 3. state update: st = Diag(2^G_last) st + A2 X (+ (scale q~)^T do for reverse).
@@ -216,17 +222,53 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) st[i][ct][e] *= cur.gl[i][e];
 #pragma unroll
-                for (int k = 0; k < C / KS; ++k)
-                    st[i][ct] = Mfma<T>::mma(cur.a2[i][k], frag_kc(sX[buf], LX, 16 * ct, k * KS), st[i][ct]);
-                if (dir == 1) {
+                for (int k2 = 0; k2 < C / KS; ++k2)
+                    st[i][ct] = Mfma<T>::mma(cur.a2[i][k2], frag_kc(sX, LX, 16 * ct, k2 * KS), st[i][ct]);
+                if constexpr (DIR == 1) {
 #pragma unroll
-                    for (int k = 0; k < C / KS; ++k)
-                        st[i][ct] = Mfma<T>::mma(cur.a3[i][k], frag_kc(sDo[buf], LX, 16 * ct, k * KS), st[i][ct]);
+                    for (int k2 = 0; k2 < C / KS; ++k2)
+                        st[i][ct] = Mfma<T>::mma(cur.a3[i][k2], frag_kc(sDo, LX, 16 * ct, k2 * KS), st[i][ct]);
                 }
             }
-        cur = nxt;
+        {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
+            T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D + v0;
+#pragma unroll
+            for (int pi = 0; pi < (C * BV / V8 + 255) / 256; ++pi) {
+                const int e = threadIdx.x + 256 * pi;
+                if (e < C * BV / V8) {
+                    const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                    Vec16 v;
+                    T* vp = reinterpret_cast<T*>(&v);
+#pragma unroll
+                    for (int q = 0; q < V8; ++q) {
+                        const T x = sX[(c + q) * LX + r];
+                        vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
+                    }
+                    st16(gX + (size_t)r * D + c, v);
+                }
+            }
+        }
+    };
+
+    if (nch > 0) {
+        // NPF register sets, each refilled right after its chunk is done; the
+        // loop is unrolled NPF times so that the sets never move
+        Ops ops[NPF];
+#pragma unroll
+        for (int s2 = 0; s2 < NPF; ++s2) load(ops[s2], s2);
+        int k0 = 0;
+        for (; k0 + NPF <= nch; k0 += NPF) {
+#pragma unroll
+            for (int s2 = 0; s2 < NPF; ++s2) {
+                step(ops[s2], k0 + s2);
+                load(ops[s2], k0 + s2 + NPF);
+            }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < NPF - 1; ++s2)
+            if (k0 + s2 < nch) step(ops[s2], k0 + s2);
     }
-    if (dir == 1) {
+    if constexpr (DIR == 1) {
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
@@ -237,6 +279,29 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
                     p.dh0[sh + (size_t)d * D + c] = st[i][ct][e];
                 }
     }
+}
+
+template <typename T, int C, int D, int BV>
+__global__ __launch_bounds__(256) void gdr_sweep(Params p) {
+    constexpr int LS = D + pad<T>();
+    constexpr int LX = C + pad<T>();
+    constexpr int NPF = 3;                           // chunks of operands in flight
+    __shared__ __attribute__((aligned(16))) T sS[BV * LS];
+    __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
+    __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
+
+    // Block order: the V tile varies slowest. Workgroups are dispatched to the
+    // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the D/BV
+    // tiles of one (direction, sequence, head) land on the same XCD and share
+    // the chunk operands (w, k~, q~, do) through its L2.
+    const int ngroups = 2 * p.N * p.H;
+    const int vt = blockIdx.x / ngroups;
+    int bid = blockIdx.x % ngroups;
+    const int h = bid % p.H; bid /= p.H;
+    const int n = bid % p.N;
+    const int dir = bid / p.N;
+    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS, sX[0], sX[1], sDo[0], sDo[1]);
+    else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS, sX[0], sX[1], sDo[0], sDo[1]);
 }
 
 }  // namespace gdr
