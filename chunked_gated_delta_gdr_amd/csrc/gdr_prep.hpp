@@ -10,13 +10,16 @@
 //           FlashQLA page's CONSUMER_A steps),
 //   w     = A (beta k 2^G),  u = A (beta v),
 //   k~    = k 2^(G_last - G),  q~ = q 2^G - Aqk w,  2^G_last.
-// Diagonal 16x16 blocks of Aqk/Akk are formed per element, one decay per
-// (r, s, d), as the bwd_intra page's module docstring requires: the decay is
-// a running product of per-token factors 2^g <= 1 along s (never a
-// factorisation inside a diagonal block). Off-diagonal blocks use bf16/fp16
-// MFMA on operands prescaled through the block boundary rho = 16 i of the
-// target row block: q 2^(G_r - G_rho) and k 2^(G_rho - G_s), both exponents
-// <= 0 (the per-block-boundary form of the same page).
+// Diagonal 16x16 blocks of Aqk/Akk use MFMA on operands scaled through the
+// block's first row b0: q_r 2^(G_r - G_b0) <= 1 against k_s 2^(G_b0 - G_s),
+// while the block's gate range |G_r - G_b0| stays within a bound that keeps
+// the second operand finite in the operand type (2^64 for bf16 / fp32, 2^8
+// for fp16); beyond it the block is formed per element, one decay per
+// (r, s, d), as a running product of per-token factors 2^g <= 1 along s.
+// Off-diagonal blocks use MFMA on operands prescaled through the block
+// boundary rho = 16 i of the target row block: q 2^(G_r - G_rho) and
+// k 2^(G_rho - G_s), both exponents <= 0 (the per-block-boundary form of the
+// bwd_intra page).
 #pragma once
 #include "gdr_common.hpp"
 
@@ -214,11 +217,52 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         __syncthreads();
     }
 
-    // ---- phase 2: diagonal 16x16 blocks of Aqk / Akk (VALU, per element) ----
-    // lane -> (block m, mirror row pair pr, d-part e8); the pair (16m+pr,
-    // 16m+15-pr) gives every lane 17 (r, s) steps. Partial dot products over
-    // the d-part are summed across the 8 parts with xor shuffles.
+    // ---- phase 2: diagonal 16x16 blocks of Aqk / Akk, wave m -> block m ----
+    bool diag_mfma;
     {
+        // MFMA form: lane l builds the fragments of its own row b0 + l%16 and
+        // d-range (the A and B operands share the lane -> (row, d) map)
+        using F = typename Mfma<T>::frag;
+        constexpr int KL = Mfma<T>::KL, KS = 4 * KL;
+        constexpr float guard = __is_same(T, _Float16) ? 8.f : 64.f;
+        const int l = lane_id(), b0 = 16 * w, r = b0 + (l & 15);
+        f32x4 aq = zero4(), ak = zero4();
+        float rmax = 0.f;
+#pragma unroll 2
+        for (int k0 = 0; k0 < D; k0 += KS) {
+            const int d0 = k0 + (l >> 4) * KL;
+            F fq, fk, fi;
+#pragma unroll
+            for (int i = 0; i < KL; ++i) {
+                const int d = d0 + i;
+                const float x = Gs[r * LF + d] - Gs[b0 * LF + d];
+                rmax = fmaxf(rmax, fabsf(x));
+                const float e = fast_exp2(x), ei = fast_exp2(fminf(-x, guard));
+                const float qv = to_f32(qL[r * LT + d]), kv = to_f32(kL[r * LT + d]);
+                if constexpr (KL == 1) {
+                    fq = qv * e; fk = kv * e; fi = kv * ei;
+                } else {
+                    fq[i] = from_f32<T>(qv * e); fk[i] = from_f32<T>(kv * e); fi[i] = from_f32<T>(kv * ei);
+                }
+            }
+            aq = Mfma<T>::mma(fq, fi, aq);
+            ak = Mfma<T>::mma(fk, fi, ak);
+        }
+        diag_mfma = wave_max(rmax) <= guard;
+        if (diag_mfma) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = b0 + acc_row(i, l), s2 = b0 + acc_col(l);
+                if (s2 <= rr) AqkF[rr * LCF + s2] = aq[i];
+                if (s2 < rr) AkkF[rr * LCF + s2] = bs[rr] * ak[i];
+            }
+        }
+    }
+    // per-element form (gate range beyond the bound): lane -> (mirror row
+    // pair pr, d-part e8) of the wave's block; the pair (16m+pr, 16m+15-pr)
+    // gives every lane 17 (r, s) steps. Partial dot products over the d-part
+    // are summed across the 8 parts with xor shuffles.
+    if (!diag_mfma) {
         constexpr int PW = D / 8;
         static_assert(PW % 8 == 0, "d-part of whole 8-element vectors");
         const int m = tid >> 6, pr = (tid & 63) >> 3, e8 = tid & 7, d0 = e8 * PW;
