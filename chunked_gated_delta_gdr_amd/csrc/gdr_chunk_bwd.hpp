@@ -67,7 +67,9 @@ struct BwdLds {
     static constexpr size_t P1_DXL = P1_DHL + sz(D, LB, sizeof(T));          // T [C][LB]
     static constexpr size_t P1_DXT = P1_DXL + sz(C, LB, sizeof(T));          // T [BVS][LC]
     static constexpr size_t P1_VL = P1_DXT + sz(BVS, LC, sizeof(T));         // T [C][LB]
-    static constexpr size_t P1_END = P1_VL + sz(C, LB, sizeof(T));
+    static constexpr size_t P1_DOL = P1_VL + sz(C, LB, sizeof(T));          // T [C][LB] do rows
+    static constexpr size_t P1_TL = P1_DOL + sz(C, LB, sizeof(T));           // T [C][LB] T = k~ dh'
+    static constexpr size_t P1_END = P1_TL + sz(C, LB, sizeof(T));
     // phase 2: Gs lives from 2a to the end of 2f
     static constexpr size_t P2_GS = 0;                                       // f32 [C][LF]
     static constexpr size_t P2_A = P2_GS + sz(C, LF, 4);
@@ -93,7 +95,11 @@ struct BwdLds {
     static constexpr size_t E_DK = E_DQ + sz(C, LT, sizeof(T));
     static constexpr size_t E_DG = E_DK + sz(C, LT, sizeof(T));
     static constexpr size_t E_END = E_DG + sz(C, LF, 4);
-    static constexpr size_t U_BYTES = cmax(cmax(P1_END, P2_B_END), cmax(P2_X_END, E_END));
+    // dv [C][LT], staged in phase 1 and stored in 2a: clear of the phase-1
+    // buffers and of what 2a writes (Gs, segment totals, k 2^G)
+    static constexpr size_t DVS = cmax(P1_END, P2_KG + sz(C, LT, sizeof(T)));
+    static constexpr size_t DVS_END = DVS + sz(C, LT, sizeof(T));
+    static constexpr size_t U_BYTES = cmax(cmax(cmax(P1_END, P2_B_END), cmax(P2_X_END, E_END)), DVS_END);
     static constexpr size_t TOTAL = U_OFF + U_BYTES;
     static_assert(P2_DA_END <= P2_T1T, "dAqk/dAkk operands must not overlap T1T");
     static_assert(size_t(4) * C * 16 <= sz(D, LC, sizeof(T)), "cumsum segment totals fit the dw region");
@@ -219,13 +225,15 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         for (int r = tid; r < C; r += NT) bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
 
         // ================= phase 1: state products over V slices =================
+        // The slice pieces (rows of do, v, X, T and of h, dh') are loaded one
+        // slice ahead into registers; every MFMA operand then comes from LDS or
+        // from the row fragments of scale Aqk^T and A^T held in registers.
         f32x4 dqh[NTD], dkt_[NTD], dwP[NTD], dAq[NTC], dAp[NTC];
 #pragma unroll
         for (int t = 0; t < NTD; ++t) { dqh[t] = zero4(); dkt_[t] = zero4(); dwP[t] = zero4(); }
 #pragma unroll
         for (int t = 0; t < NTC; ++t) { dAq[t] = zero4(); dAp[t] = zero4(); }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};   // partial db of rows r0 + acc_row(i, l)
-        float hdh = 0.f;                        // partial rowsum(h dh') of column tid
 
         T* doT = reinterpret_cast<T*>(U + L::P1_DOT);
         T* XL = reinterpret_cast<T*>(U + L::P1_XL);
@@ -234,38 +242,91 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         T* dXL = reinterpret_cast<T*>(U + L::P1_DXL);
         T* dXT = reinterpret_cast<T*>(U + L::P1_DXT);
         T* vL = reinterpret_cast<T*>(U + L::P1_VL);
-        T* dvout = static_cast<T*>(p.dv) + ((size_t)tok0 * p.H + h) * D;
+        T* doL = reinterpret_cast<T*>(U + L::P1_DOL);
+        T* TL = reinterpret_cast<T*>(U + L::P1_TL);
+        T* dvS = reinterpret_cast<T*>(U + L::DVS);
+
+        using Frag = typename Mfma<T>::frag;
+        constexpr int KS = kstep<T>(), NKC = C / KS;
+        Frag fAq[NKC], fAT[NKC];   // rows r0.. of scale Aqk^T and A^T (A^T again in 2c, 2e)
+#pragma unroll
+        for (int k2 = 0; k2 < NKC; ++k2) {
+            fAq[k2] = frag_kc(sAqkT, C, r0, k2 * KS, l);
+            fAT[k2] = frag_kc(AT, C, r0, k2 * KS, l);
+        }
+
+        constexpr int PR = BVS / V8;                              // 16-byte pieces per slice row
+        constexpr int NPC = (C * PR + NT - 1) / NT, NPD = (D * PR + NT - 1) / NT;
+        Vec16 pdo[NPC], pv[NPC], px[NPC], pt[NPC], ph[NPD], pdh[NPD];
+        float hdh[NPD];                                           // partial rowsum(h dh') per piece row
+#pragma unroll
+        for (int i = 0; i < NPD; ++i) hdh[i] = 0.f;
+        // unconditional loads (spare threads and rows past the sequence end read
+        // valid duplicates, zeroed at use), so no load waits on a branch
+        auto load_slice = [&](const int v0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NPC; ++i) {
+                const int e = min(tid + NT * i, C * PR - 1);
+                const int r = e / PR, c = (e % PR) * V8, rt = min(r, len - 1);
+                pdo[i] = ld16(dorow + (long)rt * ldo + v0 + c);
+                pv[i] = ld16(v + ((size_t)(tok0 + rt) * p.H + h) * D + v0 + c);
+                px[i] = ld16(xb + (size_t)r * D + v0 + c);
+                pt[i] = ld16(tb + (size_t)r * D + v0 + c);
+            }
+#pragma unroll
+            for (int i = 0; i < NPD; ++i) {
+                const int e = min(tid + NT * i, D * PR - 1);
+                const int d = e / PR, c = (e % PR) * V8;
+                ph[i] = ld16(hb + (size_t)d * D + v0 + c);
+                pdh[i] = ld16(dhb + (size_t)d * D + v0 + c);
+            }
+        };
+        load_slice(0);
 
         for (int v0 = 0; v0 < D; v0 += BVS) {
-            __syncthreads();
-            for (int e = tid; e < C * (BVS / V8); e += NT) {
-                const int r = e / (BVS / V8), c = (e % (BVS / V8)) * V8;
-                Vec16 dv{}, vv{};
-                if (r < len) {
-                    dv = ld16(dorow + (long)r * ldo + v0 + c);
-                    vv = ld16(v + ((size_t)(tok0 + r) * p.H + h) * D + v0 + c);
-                }
-                const T* dp = reinterpret_cast<const T*>(&dv);
+            __syncthreads();  // the previous slice's LDS reads are over
 #pragma unroll
-                for (int i = 0; i < V8; ++i) doT[(c + i) * LC + r] = dp[i];
-                st16(vL + r * LB + c, vv);
-                st16(XL + r * LB + c, ld16(xb + (size_t)r * D + v0 + c));
+            for (int i = 0; i < NPC; ++i) {
+                const int e = tid + NT * i;
+                if (e < C * PR) {
+                    const int r = e / PR, c = (e % PR) * V8;
+                    const bool real = r < len;
+                    const Vec16 dv = real ? pdo[i] : Vec16{}, vv = real ? pv[i] : Vec16{};
+                    const T* dp = reinterpret_cast<const T*>(&dv);
+#pragma unroll
+                    for (int q2 = 0; q2 < V8; ++q2) doT[(c + q2) * LC + r] = dp[q2];
+                    st16(doL + r * LB + c, dv);
+                    st16(vL + r * LB + c, vv);
+                    st16(XL + r * LB + c, px[i]);
+                    st16(TL + r * LB + c, pt[i]);
+                }
             }
-            for (int e = tid; e < D * (BVS / V8); e += NT) {
-                const int d = e / (BVS / V8), c = (e % (BVS / V8)) * V8;
-                st16(hL + d * LB + c, ld16(hb + (size_t)d * D + v0 + c));
-                st16(dhL + d * LB + c, ld16(dhb + (size_t)d * D + v0 + c));
+#pragma unroll
+            for (int i = 0; i < NPD; ++i) {
+                const int e = tid + NT * i;
+                if (e < D * PR) {
+                    const int d = e / PR, c = (e % PR) * V8;
+                    st16(hL + d * LB + c, ph[i]);
+                    st16(dhL + d * LB + c, pdh[i]);
+                    const T* ha = reinterpret_cast<const T*>(&ph[i]);
+                    const T* hb2 = reinterpret_cast<const T*>(&pdh[i]);
+                    float s2 = 0.f;
+#pragma unroll
+                    for (int q2 = 0; q2 < V8; ++q2) s2 += to_f32(ha[q2]) * to_f32(hb2[q2]);
+                    hdh[i] += s2;
+                }
             }
+            load_slice(min(v0 + BVS, D - BVS));  // next slice (the last one again at the end)
             __syncthreads();
-            // dX = T + sAqkT do  (own rows, own half of the slice)
+            // dX = T + scale Aqk^T do  (own rows, own half of the slice)
             f32x4 dX[NTV];
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dX[t][i] = to_f32(tb[(size_t)(r0 + acc_row(i, l)) * D + v0 + cv0 + 16 * t + acc_col(l)]);
+                    dX[t][i] = to_f32(TL[(r0 + acc_row(i, l)) * LB + cv0 + 16 * t + acc_col(l)]);
             }
-            panel_mma<T, NTV, C>(dX, sAqkT, C, r0, doT, LC, cv0, l);
+            panel_mma_ra<T, NTV, NKC>(dX, fAq, doT, LC, cv0, l);
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
                 const int c = cv0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
@@ -273,18 +334,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 for (int i = 0; i < 4; ++i) dXL[(rr + i) * LB + c] = from_f32<T>(dX[t][i]);
                 store4<T>(dXT + c * LC + rr, dX[t][0], dX[t][1], dX[t][2], dX[t][3]);
             }
-            // rowsum(h dh') over this slice, column d = tid
-            if (tid < D) {
-                float s2 = 0.f;
-#pragma unroll 8
-                for (int c = 0; c < BVS; ++c) s2 += to_f32(hL[tid * LB + c]) * to_f32(dhL[tid * LB + c]);
-                hdh += s2;
-            }
             __syncthreads();
 #pragma unroll
-            for (int k0 = 0; k0 < BVS; k0 += kstep<T>()) {
-                const auto a_do = frag_rows(dorow, ldo, r0, v0 + k0, len, l);
-                const auto a_x = frag_kc(xb + v0, D, r0, k0, l);
+            for (int k0 = 0; k0 < BVS; k0 += KS) {
+                const auto a_do = frag_kc(doL, LB, r0, k0, l);
+                const auto a_x = frag_kc(XL, LB, r0, k0, l);
                 const auto a_dx = frag_kc(dXL, LB, r0, k0, l);
 #pragma unroll
                 for (int t = 0; t < NTC; ++t) {
@@ -299,11 +353,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     dkt_[t] = Mfma<T>::mma(a_x, frag_kc(dhL, LB, cd0 + 16 * t, k0, l), dkt_[t]);
                 }
             }
-            // dv^ = A^T dX; dv = beta dv^; db += rowsum(dv^ v)
+            // dv^ = A^T dX; dv = beta dv^ (staged for row stores); db += rowsum(dv^ v)
             f32x4 dvh[NTV];
 #pragma unroll
             for (int t = 0; t < NTV; ++t) dvh[t] = zero4();
-            panel_mma<T, NTV, C>(dvh, AT, C, r0, dXT, LC, cv0, l);
+            panel_mma_ra<T, NTV, NKC>(dvh, fAT, dXT, LC, cv0, l);
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
                 const int c = cv0 + 16 * t + acc_col(l);
@@ -311,15 +365,31 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 for (int i = 0; i < 4; ++i) {
                     const int r = r0 + acc_row(i, l);
                     dbp[i] += dvh[t][i] * to_f32(vL[r * LB + c]);
-                    if (r < len) dvout[(size_t)r * ldo + v0 + c] = from_f32<T>(bs[r] * dvh[t][i]);
+                    dvS[r * LT + v0 + c] = from_f32<T>(bs[r] * dvh[t][i]);
                 }
             }
         }
-        // dG_last, part 1: ln2 2^G_last rowsum_v(h dh')  (glast of this chunk)
-        if (tid < D) dGl[tid] = kLn2 * p.glast[jh * D + tid] * hdh;
-        __syncthreads();  // phase-1 LDS is dead from here
+        // dG_last, part 1: ln2 2^G_last rowsum_v(h dh') (the PR pieces of a row
+        // sit in PR consecutive lanes)
+#pragma unroll
+        for (int i = 0; i < NPD; ++i) {
+            float x = hdh[i];
+#pragma unroll
+            for (int m = 1; m < PR; m <<= 1) x += __shfl_xor(x, m);
+            const int e = tid + NT * i;
+            if (e < D * PR && e % PR == 0) dGl[e / PR] = kLn2 * p.glast[jh * D + e / PR] * x;
+        }
+        __syncthreads();  // phase-1 LDS is dead from here; dv is staged
 
         // ================= phase 2 =================
+        // dv rows to the output, 16 bytes per access
+        {
+            T* dvout = static_cast<T*>(p.dv) + ((size_t)tok0 * p.H + h) * D;
+            for (int e = tid; e < C * (D / V8); e += NT) {
+                const int r = e / (D / V8), c = (e % (D / V8)) * V8;
+                if (r < len) st16(dvout + (size_t)r * ldo + c, ld16(dvS + r * LT + c));
+            }
+        }
         // 2a: G = chunk-local inclusive cumsum of g, one column and NT/D row
         // segments per thread, and k 2^G
         float* Gs = reinterpret_cast<float*>(U + L::P2_GS);
@@ -392,7 +462,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             f32x4 dkh[NTD];
 #pragma unroll
             for (int t = 0; t < NTD; ++t) dkh[t] = zero4();
-            panel_mma<T, NTD, C>(dkh, AT, C, r0, dwT, LC, cd0, l);
+            panel_mma_ra<T, NTD, NKC>(dkh, fAT, dwT, LC, cd0, l);
 #pragma unroll
             for (int t = 0; t < NTD; ++t) {
                 const int c = cd0 + 16 * t + acc_col(l);
@@ -438,7 +508,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             f32x4 dAk[NTC];
 #pragma unroll
             for (int t = 0; t < NTC; ++t) dAk[t] = zero4();
-            panel_mma<T, NTC, C>(dAk, AT, C, r0, T1T, LC, cc0, l);
+            panel_mma_ra<T, NTC, NKC>(dAk, fAT, T1T, LC, cc0, l);
             __syncthreads();  // T1T reads done before the dA operands overwrite dead buffers
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {

@@ -104,6 +104,28 @@ __device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda,
     }
 }
 
+// Row-panel products with one operand already in registers (fragments of a
+// C-long reduction): A rows (a[k] for reduction step k) against Bt in memory,
+// or A in memory against Bt fragments b[t][k] of the NT column tiles.
+template <typename T, int NT, int NK>
+__device__ __forceinline__ void panel_mma_ra(f32x4 (&acc)[NT], const typename Mfma<T>::frag (&a)[NK],
+                                             const T* Bt, int ldb, int j0, int l) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a[k], frag_kc(Bt, ldb, j0 + 16 * t, k * kstep<T>(), l), acc[t]);
+}
+template <typename T, int NT, int NK>
+__device__ __forceinline__ void panel_mma_rb(f32x4 (&acc)[NT], const T* A, int lda, int i0,
+                                             const typename Mfma<T>::frag (&b)[NT][NK], int l) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        const auto a = frag_kc(A, lda, i0, k * kstep<T>(), l);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, b[t][k], acc[t]);
+    }
+}
+
 // Same with a run-time reduction length kd (a multiple of kstep<T>()).
 template <typename T, int NT>
 __device__ __forceinline__ void panel_mma_n(f32x4 (&acc)[NT], const T* A, int lda, int i0,
