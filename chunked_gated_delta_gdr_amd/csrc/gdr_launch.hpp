@@ -20,7 +20,7 @@ hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
     gdr_chunk_table<C><<<dim3(1), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(1);
     if (p.nc_max > 0)
-        gdr_prep<T, C, D, SCALAR><<<dim3(p.nc_max, p.H), dim3(64 * (C / 16)), 0, stream>>>(p);
+        gdr_prep<T, C, D, SCALAR><<<dim3(p.nc_max, p.H), dim3(128 * (C / 16)), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(2);
     gdr_sweep<T, C, D, kSweepBV><<<dim3(2 * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(3);

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
 template <typename T, int C, int D>
 struct PrepLds {
     static constexpr int NB = C / 16;
-    static constexpr int NT = 64 * NB;
+    static constexpr int NW = 2 * NB;         // waves: two per 16-row block
+    static constexpr int NT = 64 * NW;
     static constexpr int LT = D + pad<T>();   // T  [*][D]
     static constexpr int LC = C + pad<T>();   // T  [*][C]
     static constexpr int LF = D + 4;          // f32 [*][D]
@@ -140,10 +141,11 @@ __device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
 }
 
 template <typename T, int C, int D, bool SCALAR>
-__global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
+__global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     using L = PrepLds<T, C, D>;
     constexpr int NB = L::NB, NT = L::NT, LT = L::LT, LC = L::LC, LF = L::LF, LCF = L::LCF;
     constexpr int NTD = D / 16;  // column tiles of a [C][D] product
+    constexpr int NTH = NTD / 2; // per wave: one column half
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
     float* Gs = reinterpret_cast<float*>(smem + L::G_OFF);
     float* At = reinterpret_cast<float*>(smem + L::X_OFF);    // phase 1-2: 2^g per token
@@ -217,7 +219,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         __syncthreads();
     }
 
-    // ---- phase 2: diagonal 16x16 blocks of Aqk / Akk, wave m -> block m ----
+    // ---- phase 2: diagonal 16x16 blocks; wave w -> block w % NB, Aqk (w < NB) or Akk ----
+    const bool is_kk = w >= NB;
     bool diag_mfma;
     {
         // MFMA form: lane l builds the fragments of its own row b0 + l%16 and
@@ -225,47 +228,48 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         using F = typename Mfma<T>::frag;
         constexpr int KL = Mfma<T>::KL, KS = 4 * KL;
         constexpr float guard = __is_same(T, _Float16) ? 8.f : 64.f;
-        const int l = lane_id(), b0 = 16 * w, r = b0 + (l & 15);
-        f32x4 aq = zero4(), ak = zero4();
+        const int l = lane_id(), b0 = 16 * (w % NB), r = b0 + (l & 15);
+        f32x4 acc = zero4();
         float rmax = 0.f;
 #pragma unroll 2
         for (int k0 = 0; k0 < D; k0 += KS) {
             const int d0 = k0 + (l >> 4) * KL;
-            F fq, fk, fi;
+            F fa, fi;
+            const T* arow = (is_kk ? kL : qL) + r * LT;
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
                 const int d = d0 + i;
                 const float x = Gs[r * LF + d] - Gs[b0 * LF + d];
                 rmax = fmaxf(rmax, fabsf(x));
                 const float e = fast_exp2(x), ei = fast_exp2(fminf(-x, guard));
-                const float qv = to_f32(qL[r * LT + d]), kv = to_f32(kL[r * LT + d]);
+                const float av = to_f32(arow[d]), kv = to_f32(kL[r * LT + d]);
                 if constexpr (KL == 1) {
-                    fq = qv * e; fk = kv * e; fi = kv * ei;
+                    fa = av * e; fi = kv * ei;
                 } else {
-                    fq[i] = from_f32<T>(qv * e); fk[i] = from_f32<T>(kv * e); fi[i] = from_f32<T>(kv * ei);
+                    fa[i] = from_f32<T>(av * e); fi[i] = from_f32<T>(kv * ei);
                 }
             }
-            aq = Mfma<T>::mma(fq, fi, aq);
-            ak = Mfma<T>::mma(fk, fi, ak);
+            acc = Mfma<T>::mma(fa, fi, acc);
         }
         diag_mfma = wave_max(rmax) <= guard;
         if (diag_mfma) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = b0 + acc_row(i, l), s2 = b0 + acc_col(l);
-                if (s2 <= rr) AqkF[rr * LCF + s2] = aq[i];
-                if (s2 < rr) AkkF[rr * LCF + s2] = bs[rr] * ak[i];
+                if (!is_kk && s2 <= rr) AqkF[rr * LCF + s2] = acc[i];
+                if (is_kk && s2 < rr) AkkF[rr * LCF + s2] = bs[rr] * acc[i];
             }
         }
     }
-    // per-element form (gate range beyond the bound): lane -> (mirror row
-    // pair pr, d-part e8) of the wave's block; the pair (16m+pr, 16m+15-pr)
+    // per-element form (gate range beyond the bound; both waves of the block
+    // compute, each keeps its matrix): lane -> (mirror row pair pr, d-part
+    // e8) of the wave's block; the pair (16m+pr, 16m+15-pr)
     // gives every lane 17 (r, s) steps. Partial dot products over the d-part
     // are summed across the 8 parts with xor shuffles.
     if (!diag_mfma) {
         constexpr int PW = D / 8;
         static_assert(PW % 8 == 0, "d-part of whole 8-element vectors");
-        const int m = tid >> 6, pr = (tid & 63) >> 3, e8 = tid & 7, d0 = e8 * PW;
+        const int m = w % NB, pr = (tid & 63) >> 3, e8 = tid & 7, d0 = e8 * PW;
         float qr[PW], kr[PW], E[PW];
         int r = 16 * m + pr, s = r;
         auto load_row = [&](int rr) {
@@ -303,8 +307,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
             pq += __shfl_xor(pq, 2); pk += __shfl_xor(pk, 2);
             pq += __shfl_xor(pq, 4); pk += __shfl_xor(pk, 4);
             if (e8 == 0) {
-                AqkF[r * LCF + s] = pq;
-                if (s < r) AkkF[r * LCF + s] = bs[r] * pk;
+                if (!is_kk) AqkF[r * LCF + s] = pq;
+                else if (s < r) AkkF[r * LCF + s] = bs[r] * pk;
             }
             --s;
         }
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
         __syncthreads();
         // tiles: (which in {Aqk, Akk}) x (rho/16 column tiles)
         const int ntile = 2 * ib;
-        for (int t = w; t < ntile; t += NB) {
+        for (int t = w; t < ntile; t += L::NW) {
             const int which = t / ib, ct = t % ib;
             f32x4 acc[1] = {zero4()};
             panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct);
@@ -428,17 +432,18 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     }
     __syncthreads();
 
-    // ---- phase 6: w = A k^ (wave w owns rows 16w..16w+15 of every [C][D] product) ----
-    const int r0 = 16 * w;
-    f32x4 acc[NTD];
+    // ---- phase 6: w = A k^ (wave w owns rows 16 (w % NB) .. +16 and the
+    //      column half w / NB of every [C][D] product) ----
+    const int r0 = 16 * (w % NB), ch0 = (w / NB) * (D / 2);
+    f32x4 acc[NTH];
 #pragma unroll
-    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
-    panel_mma<T, NTD, C>(acc, AtL, LC, r0, khT, LC, 0);
+    for (int t = 0; t < NTH; ++t) acc[t] = zero4();
+    panel_mma<T, NTH, C>(acc, AtL, LC, r0, khT, LC, ch0);
     __syncthreads();  // khT is about to be overwritten by w^T
     T* wTL = Xb;  // [D][LC]
 #pragma unroll
-    for (int t = 0; t < NTD; ++t) {
-        const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+    for (int t = 0; t < NTH; ++t) {
+        const int c = ch0 + 16 * t + acc_col(), rb = r0 + acc_row(0);
         store4<T>(wTL + c * LC + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     }
     __syncthreads();
@@ -462,13 +467,13 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
 
     // ---- phase 7: q~ = q 2^G - Aqk w, stored as scale * q~^T ----
 #pragma unroll
-    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
-    panel_mma<T, NTD, C>(acc, AqkL, LC, r0, wTL, LC, 0);
+    for (int t = 0; t < NTH; ++t) acc[t] = zero4();
+    panel_mma<T, NTH, C>(acc, AqkL, LC, r0, wTL, LC, ch0);
     {
         T* gq = static_cast<T*>(p.qsT) + jh * D * C;
 #pragma unroll
-        for (int t = 0; t < NTD; ++t) {
-            const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+        for (int t = 0; t < NTH; ++t) {
+            const int c = ch0 + 16 * t + acc_col(), rb = r0 + acc_row(0);
             float o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -492,13 +497,13 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_prep(Params p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
-    panel_mma<T, NTD, C>(acc, AtL, LC, r0, vhT, LC, 0);
+    for (int t = 0; t < NTH; ++t) acc[t] = zero4();
+    panel_mma<T, NTH, C>(acc, AtL, LC, r0, vhT, LC, ch0);
     {
         T* gu = static_cast<T*>(p.uT) + jh * D * C;
 #pragma unroll
-        for (int t = 0; t < NTD; ++t) {
-            const int c = 16 * t + acc_col(), rb = r0 + acc_row(0);
+        for (int t = 0; t < NTH; ++t) {
+            const int c = ch0 + 16 * t + acc_col(), rb = r0 + acc_row(0);
             store4<T>(gu + c * C + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
         }
     }
