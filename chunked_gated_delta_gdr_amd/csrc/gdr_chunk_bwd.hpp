@@ -181,16 +181,23 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     const T* dout = static_cast<const T*>(p.dout);
     const T* beta = static_cast<const T*>(p.beta);
 
-    // q, k rows of this chunk (zero past the sequence end)
-    for (int e = tid; e < C * (D / V8); e += NT) {
-        const int r = e / (D / V8), d0 = (e % (D / V8)) * V8;
-        Vec16 qv{}, kv{};
-        if (r < len) {
-            qv = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-            kv = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
+    // q, k rows of this chunk (all requested first; zero past the sequence end)
+    {
+        constexpr int NQP = C * (D / V8) / NT;
+        static_assert(NQP * NT == C * (D / V8), "piece split");
+        Vec16 qv[NQP], kv[NQP];
+#pragma unroll
+        for (int i = 0; i < NQP; ++i) {
+            const int e = tid + i * NT, r = min(e / (D / V8), len - 1), d0 = (e % (D / V8)) * V8;
+            qv[i] = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
+            kv[i] = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
         }
-        st16(qL0 + r * LT + d0, qv);
-        st16(kL0 + r * LT + d0, kv);
+#pragma unroll
+        for (int i = 0; i < NQP; ++i) {
+            const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8;
+            st16(qL0 + r * LT + d0, r < len ? qv[i] : Vec16{});
+            st16(kL0 + r * LT + d0, r < len ? kv[i] : Vec16{});
+        }
     }
 
     // GROUPED: fp32 group sums of dq, dk in this wave's accumulator tiles

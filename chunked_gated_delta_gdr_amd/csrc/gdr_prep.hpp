@@ -171,34 +171,52 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     const size_t jh = size_t(j) * p.H + h;
     constexpr int V8 = 16 / sizeof(T);  // elements per 16-byte vector
 
-    // ---- phase 1: raw gate -> 2^g table and G; q, k, beta ----
-    for (int e = tid; e < C * (D / 4); e += NT) {
-        const int r = e / (D / 4), d0 = (e % (D / 4)) * 4;
-        f32x4 gv = zero4();
-        if (r < len) {
-            if constexpr (SCALAR) {
-                const float s = p.g[(size_t)(tok0 + r) * p.H + h];
-                gv = f32x4{s, s, s, s};
-            } else {
-                gv = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + r) * p.H + h) * D + d0);
-            }
+    // ---- phase 1: every global input of the chunk is requested up front
+    //      (fixed trip counts; rows past the sequence end read the last row and
+    //      are zeroed at use); v stays in registers until phase 8 ----
+    constexpr int NGP = C * (D / 4) / NT;    // 4-float gate pieces per thread
+    constexpr int NQP = C * (D / V8) / NT;   // 16-byte q / k / v pieces per thread
+    static_assert(NGP * NT == C * (D / 4) && NQP * NT == C * (D / V8), "piece split");
+    f32x4 gpre[NGP];
+    Vec16 qpre[NQP], kpre[NQP], vpre[NQP];
+#pragma unroll
+    for (int i = 0; i < NGP; ++i) {
+        const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4, rt = min(r, len - 1);
+        if constexpr (SCALAR) {
+            const float sg = p.g[(size_t)(tok0 + rt) * p.H + h];
+            gpre[i] = f32x4{sg, sg, sg, sg};
+        } else {
+            gpre[i] = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + rt) * p.H + h) * D + d0);
         }
+    }
+#pragma unroll
+    for (int i = 0; i < NQP; ++i) {
+        const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8, rt = min(r, len - 1);
+        qpre[i] = ld16(q + ((size_t)(tok0 + rt) * p.Hg + hk) * D + d0);
+        kpre[i] = ld16(k + ((size_t)(tok0 + rt) * p.Hg + hk) * D + d0);
+        vpre[i] = ld16(v + ((size_t)(tok0 + rt) * p.H + h) * D + d0);
+    }
+    const float bpre = to_f32(beta[(size_t)(tok0 + min(tid, len - 1)) * p.H + h]);
+    for (int e = tid; e < C * LCF / 4; e += NT) {
+        reinterpret_cast<f32x4*>(AqkF)[e] = zero4();
+        reinterpret_cast<f32x4*>(AkkF)[e] = zero4();
+        reinterpret_cast<f32x4*>(AF)[e] = zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < NGP; ++i) {
+        const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4;
+        const f32x4 gv = r < len ? gpre[i] : zero4();
         *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = gv;
         *reinterpret_cast<f32x4*>(At + r * LF + d0) =
             f32x4{fast_exp2(gv[0]), fast_exp2(gv[1]), fast_exp2(gv[2]), fast_exp2(gv[3])};
     }
-    for (int e = tid; e < C * (D / V8); e += NT) {
-        const int r = e / (D / V8), d0 = (e % (D / V8)) * V8;
-        Vec16 qv{}, kv{};
-        if (r < len) {
-            qv = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-            kv = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-        }
-        st16(qL + r * LT + d0, qv);
-        st16(kL + r * LT + d0, kv);
+#pragma unroll
+    for (int i = 0; i < NQP; ++i) {
+        const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        st16(qL + r * LT + d0, r < len ? qpre[i] : Vec16{});
+        st16(kL + r * LT + d0, r < len ? kpre[i] : Vec16{});
     }
-    for (int r = tid; r < C; r += NT) bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
-    for (int e = tid; e < C * LCF; e += NT) { AqkF[e] = 0.f; AkkF[e] = 0.f; AF[e] = 0.f; }
+    if (tid < C) bs[tid] = tid < len ? bpre : 0.f;
     __syncthreads();
     {   // column cumsum in NSEG segments of SR rows: local scans, then segment offsets
         constexpr int NSEG = NT / D > 0 ? NT / D : 1, SR = C / NSEG;
@@ -394,31 +412,34 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         __syncthreads();
     }
 
-    // ---- phase 5: A, Aqk to the workspace; in place as MFMA operands in LDS ----
-    constexpr int PER = C * C / NT;   // elements of a C x C matrix per thread
-    float av[PER], qv[PER];
-    {
+    // ---- phase 5: A, A^T and scale Aqk^T to the workspace in 8-element row
+    //      pieces; A and Aqk in place as MFMA operands in LDS ----
+    float av[8], qv[8];   // this thread's piece of A and Aqk (at most one: C <= 64)
+    static_assert(C * (C / 8) <= NT, "one piece of a C x C matrix per thread");
+    const bool has_piece = tid < C * (C / 8);
+    const int pr5 = tid / (C / 8), ps5 = (tid % (C / 8)) * 8;
+    if (has_piece) {
         T* gA = static_cast<T*>(p.Am) + jh * C * C;
         T* gAT = static_cast<T*>(p.AT) + jh * C * C;
         T* gSq = static_cast<T*>(p.sAqkT) + jh * C * C;
+        float at[8], sq[8];
+        load8f(AF + pr5 * LCF + ps5, av);
+        load8f(AqkF + pr5 * LCF + ps5, qv);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = tid + i * NT, r = e / C, s2 = e % C;
-            av[i] = AF[r * LCF + s2];
-            qv[i] = AqkF[r * LCF + s2];
-            gA[e] = from_f32<T>(av[i]);
-            gAT[e] = from_f32<T>(AF[s2 * LCF + r]);         // AT[r][s] = A[s][r]
-            gSq[e] = from_f32<T>(p.scale * AqkF[s2 * LCF + r]);
+        for (int i = 0; i < 8; ++i) {
+            at[i] = AF[(ps5 + i) * LCF + pr5];                // A^T[r][s] = A[s][r]
+            sq[i] = p.scale * AqkF[(ps5 + i) * LCF + pr5];
         }
+        store8<T>(gA + pr5 * C + ps5, av);
+        store8<T>(gAT + pr5 * C + ps5, at);
+        store8<T>(gSq + pr5 * C + ps5, sq);
     }
     __syncthreads();
     T* AtL = reinterpret_cast<T*>(smem + L::AF_OFF);    // A   [C][LC], over the dead fp32 A
     T* AqkL = reinterpret_cast<T*>(smem + L::AQK_OFF);  // Aqk [C][LC], over the dead fp32 Aqk
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * NT, r = e / C, s2 = e % C;
-        AtL[r * LC + s2] = from_f32<T>(av[i]);
-        AqkL[r * LC + s2] = from_f32<T>(qv[i]);
+    if (has_piece) {
+        store8<T>(AtL + pr5 * LC + ps5, av);
+        store8<T>(AqkL + pr5 * LC + ps5, qv);
     }
     // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^): 8 consecutive s per item
     T* khT = Xb;  // [D][LC]
@@ -487,10 +508,10 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 
     // ---- phase 8: u = A (beta v) ----
     T* vhT = Xb;  // [D][LC]
-    for (int e = tid; e < C * (D / V8); e += NT) {
-        const int s2 = e / (D / V8), d0 = (e % (D / V8)) * V8;
-        Vec16 vv{};
-        if (s2 < len) vv = ld16(v + ((size_t)(tok0 + s2) * p.H + h) * D + d0);
+#pragma unroll
+    for (int i5 = 0; i5 < NQP; ++i5) {
+        const int e = tid + i5 * NT, s2 = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        const Vec16 vv = s2 < len ? vpre[i5] : Vec16{};
         const T* vp = reinterpret_cast<const T*>(&vv);
 #pragma unroll
         for (int i = 0; i < V8; ++i) vhT[(d0 + i) * LC + s2] = from_f32<T>(bs[s2] * to_f32(vp[i]));
