@@ -26,8 +26,10 @@
 //   2^(G_r - G_s) = Ein_r * phi_{b'+1} ... phi_{b-1} * Eout_s,
 // so the operands k Eout, q Ein, beta k Ein are scaled once per chunk and the
 // phi are applied to the accumulators between blocks (Horner); every exponent
-// is <= 0. Inside a diagonal block the source side needs 2^(G_16b - G_s) >= 1;
-// the MFMA form is used there when the block's gate range |G_r - G_16b| stays
+// is <= 0. Inside a diagonal block the source side needs 2^(G_16b - G_s) >= 1,
+// taken as the k Eout operand times 2^(G_16b - G_16(b+1)) on the accumulator
+// (the last block references its own last row); the MFMA form is used there
+// when the block's gate range, its next block's first row included, stays
 // within 2^64 (2^8 for fp16 operands) for every column of the wave, else an
 // exact VALU pass with one exp2 per (r, s, d). Finally
 // dg = reverse cumsum of dG in the chunk (the page's fold_dg), dG_last collecting
@@ -86,10 +88,10 @@ struct BwdLds {
     //   they must stay clear of T1T, still read in 2e
     static constexpr size_t P2_DAQ = P2_A;
     static constexpr size_t P2_DA_END = P2_DAQ + 2 * sz(C, LC, sizeof(T));
-    //   2f: scaled operands of one column half, transposed: k Eout, k / Ein,
-    //   q Ein, beta k Ein, each [D/2][LC]
+    //   2f: scaled operands of both column halves, transposed: k Eout, q Ein,
+    //   beta k Ein, each [2][D/2][LC]
     static constexpr size_t P2_X = P2_DA_END;
-    static constexpr size_t P2_X_END = P2_X + 4 * sz(D / 2, LC, sizeof(T));
+    static constexpr size_t P2_X_END = P2_X + 6 * sz(D / 2, LC, sizeof(T));
     // epilogue: dq, dk [C][LT] and dg f32 [C][LF] staged for row-contiguous stores
     static constexpr size_t E_DQ = 0;
     static constexpr size_t E_DK = E_DQ + sz(C, LT, sizeof(T));
@@ -529,42 +531,45 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             }
         }
 
-        // 2f: intra-chunk gradient on MFMA, one column half at a time: all
-        // threads scale the operands of the half, the waves owning it multiply
-        T* kET = reinterpret_cast<T*>(U + L::P2_X);   // [DH2][LC] k_s Eout_s
-        T* kIT = kET + DH2 * LC;                        // [DH2][LC] k_s / Ein_s (exponent clamped)
-        T* qET = kIT + DH2 * LC;                        // [DH2][LC] q_r Ein_r
-        T* bkET = qET + DH2 * LC;                       // [DH2][LC] beta_r k_r Ein_r
-        for (int hf = 0; hf < 2; ++hf) {
-            const int dh0 = hf * DH2;
-            __syncthreads();  // dA written (hf = 0) / previous half's operands read (hf = 1)
-            for (int e = tid; e < DH2 * (C / 4); e += NT) {
-                const int dd = e % DH2, s0 = (e / DH2) * 4, d = dh0 + dd;
-                const int b0 = s0 & ~15;
-                const bool has_next = b0 + 16 < C;
-                const float Gb = Gs[b0 * LF + d];
-                const float Gn = has_next ? Gs[(b0 + 16) * LF + d] : 0.f;
-                float ke[4], ki[4], qe[4], bke[4];
+        // 2f: intra-chunk gradient on MFMA: all threads scale the operands of
+        // both column halves, then every wave multiplies in its own half
+        T* const kE0 = reinterpret_cast<T*>(U + L::P2_X);   // [2][DH2][LC] k_s Eout_s
+        T* const qE0 = kE0 + 2 * DH2 * LC;                    // [2][DH2][LC] q_r Ein_r
+        T* const bkE0 = qE0 + 2 * DH2 * LC;                   // [2][DH2][LC] beta_r k_r Ein_r
+        __syncthreads();  // dA written
+        for (int e = tid; e < D * (C / 4); e += NT) {
+            const int d = e % D, s0 = (e / D) * 4;
+            const int b0 = s0 & ~15;
+            const int nb = b0 + 16 < C ? b0 + 16 : C - 1;  // Eout reference (last block: its last row)
+            const float Gb = Gs[b0 * LF + d], Gn = Gs[nb * LF + d];
+            float ke[4], qe[4], bke[4];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int s = s0 + jj;
-                    const float G = Gs[s * LF + d];
-                    const float kv = to_f32(kL[s * LT + d]);
-                    const float ein = fast_exp2(G - Gb);
-                    ke[jj] = has_next ? kv * fast_exp2(Gn - G) : 0.f;
-                    ki[jj] = kv * fast_exp2(fminf(Gb - G, diag_guard<T>()));
-                    qe[jj] = to_f32(qL[s * LT + d]) * ein;
-                    bke[jj] = bs[s] * kv * ein;
-                }
-                store4<T>(kET + dd * LC + s0, ke[0], ke[1], ke[2], ke[3]);
-                store4<T>(kIT + dd * LC + s0, ki[0], ki[1], ki[2], ki[3]);
-                store4<T>(qET + dd * LC + s0, qe[0], qe[1], qe[2], qe[3]);
-                store4<T>(bkET + dd * LC + s0, bke[0], bke[1], bke[2], bke[3]);
+            for (int jj = 0; jj < 4; ++jj) {
+                const int s = s0 + jj;
+                const float G = Gs[s * LF + d];
+                const float kv = to_f32(kL[s * LT + d]);
+                const float ein = fast_exp2(G - Gb);
+                ke[jj] = kv * fast_exp2(Gn - G);
+                qe[jj] = to_f32(qL[s * LT + d]) * ein;
+                bke[jj] = bs[s] * kv * ein;
             }
-            __syncthreads();
+            const int o = ((d / DH2) * DH2 + d % DH2) * LC + s0;
+            store4<T>(kE0 + o, ke[0], ke[1], ke[2], ke[3]);
+            store4<T>(qE0 + o, qe[0], qe[1], qe[2], qe[3]);
+            store4<T>(bkE0 + o, bke[0], bke[1], bke[2], bke[3]);
+        }
+        __syncthreads();
+        // each wave runs its half once, at hf == ch (the loop keeps the compiler
+        // from moving the half's address arithmetic ahead of the fill)
+#pragma unroll 1
+        for (int hf = 0; hf < 2; ++hf) {
             if (ch != hf) continue;
+            T* const kET = kE0 + ch * DH2 * LC;
+            T* const qET = qE0 + ch * DH2 * LC;
+            T* const bkET = bkE0 + ch * DH2 * LC;
             const int l = opaque_lane_id();  // see the head body
             // G of this wave's rows and of its block's first row; the guard
+            // also covers the next block's first row (the diagonal's Eout reference)
             float gr[NTD][4], grho[NTD];
             float rmax = 0.f;
 #pragma unroll
@@ -576,6 +581,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     gr[t][i] = Gs[(r0 + acc_row(i, l)) * LF + c];
                     rmax = fmaxf(rmax, fabsf(gr[t][i] - grho[t]));
                 }
+                if (rb < NB - 1) rmax = fmaxf(rmax, fabsf(Gs[(r0 + 16) * LF + c] - grho[t]));
             }
             const bool diag_mfma = wave_max(rmax) <= diag_guard<T>();
 
@@ -601,20 +607,30 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                         ak[t] = mma16<T, false>(ak[t], dAkL, LC, r0, 16 * b1, kET, LC, 16 * t, 16 * b1, l);
                     }
                 }
+                // reference of the sum: G_16rb for the cross part alone; with the
+                // diagonal on MFMA (sources k Eout, reference G_nb) the cross part
+                // is moved to G_nb first (a factor <= 1, >= 2^-guard)
+                const int nbr = rb < NB - 1 ? r0 + 16 : C - 1;
+                float gref[NTD];
+#pragma unroll
+                for (int t = 0; t < NTD; ++t) gref[t] = diag_mfma ? Gs[nbr * LF + cd0 + 16 * t + acc_col(l)] : grho[t];
                 if (diag_mfma) {
 #pragma unroll
                     for (int t = 0; t < NTD; ++t) {
-                        aq[t] = mma16<T, false>(aq[t], dAqL, LC, r0, r0, kIT, LC, 16 * t, r0, l);
-                        ak[t] = mma16<T, false>(ak[t], dAkL, LC, r0, r0, kIT, LC, 16 * t, r0, l);
+                        const float ph = fast_exp2(gref[t] - grho[t]);
+                        aq[t] *= ph;
+                        ak[t] *= ph;
+                        aq[t] = mma16<T, false>(aq[t], dAqL, LC, r0, r0, kET, LC, 16 * t, r0, l);
+                        ak[t] = mma16<T, false>(ak[t], dAkL, LC, r0, r0, kET, LC, 16 * t, r0, l);
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < NTD; ++t) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float ein = fast_exp2(gr[t][i] - grho[t]);
-                        aq[t][i] *= ein;
-                        ak[t][i] *= ein;
+                        const float f = fast_exp2(gr[t][i] - gref[t]);   // Ein, or 2^(G_r - G_nb) <= 2^guard
+                        aq[t][i] *= f;
+                        ak[t][i] *= f;
                     }
                 }
                 if (!diag_mfma) {  // exact diagonal block, one exp2 per (r, s, d)
