@@ -140,8 +140,8 @@ __device__ __forceinline__ void panel_mma_n(f32x4 (&acc)[NT], const T* A, int ld
 // fp32 16x16 tile product on fp32 arrays, reduction length kd (multiple of 4):
 // acc += A[(ai0+i)*lda + ak0 + kk] * B[(bk0+kk)*ldb + bj0 + j].
 __device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* A, int lda, int ai0, int ak0,
-                                          const float* B, int ldb, int bk0, int bj0, int kd) {
-    const int l = lane_id();
+                                          const float* B, int ldb, int bk0, int bj0, int kd,
+                                          int l = lane_id()) {
     for (int k = 0; k < kd; k += 4) {
         float a = A[(ai0 + (l & 15)) * lda + ak0 + k + (l >> 4)];
         float b = B[(bk0 + k + (l >> 4)) * ldb + bj0 + (l & 15)];

@@ -12,6 +12,19 @@ using LaunchFn = hipError_t (*)(const Params&, hipStream_t, hipEvent_t const* ev
 
 constexpr int kSweepBV = 32;  // V columns of the state per sweep workgroup
 
+// Compute units of the current device (queried once per device).
+inline int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <typename T, int C, int D, bool SCALAR>
 hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
@@ -19,8 +32,12 @@ hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
     // chunk table (device-side, so varlen needs no host sync)
     gdr_chunk_table<C><<<dim3(1), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(1);
-    if (p.nc_max > 0)
-        gdr_prep<T, C, D, SCALAR><<<dim3(p.nc_max, p.H), dim3(128 * (C / 16)), 0, stream>>>(p);
+    if (p.nc_max > 0) {
+        // persistent: at most one workgroup per compute unit (its LDS allows no more)
+        const int items = p.nc_max * p.H;
+        gdr_prep<T, C, D, SCALAR><<<dim3(items < compute_units() ? items : compute_units()),
+                                    dim3(128 * (C / 16)), 0, stream>>>(p);
+    }
     if (e == hipSuccess) e = mark(2);
     gdr_sweep<T, C, D, kSweepBV><<<dim3(2 * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(3);

@@ -158,45 +158,71 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     float* scr = reinterpret_cast<float*>(smem + L::SCR_OFF);
     float* bs = reinterpret_cast<float*>(smem + L::BETA_OFF);
 
-    const int j = blockIdx.x, h = blockIdx.y;
-    if (j >= p.seq_off[p.N]) return;
-    const ChunkEntry ce = p.ctab[j];
-    const int tok0 = ce.tok0, len = ce.len;
-    const int hk = h / p.G;
+    // Persistent: at most one workgroup per CU walks the (chunk, value head)
+    // items blockIdx.x, + gridDim.x, ...; the next item's g, q, k, beta are
+    // requested right after the current ones reach LDS, its v after the
+    // current v is used (v stays in registers until its product).
+    const int nit = p.seq_off[p.N] * p.H;
+    int item = blockIdx.x;
+    if (item >= nit) return;
     const int tid = threadIdx.x, w = wave_id();
     const T* q = static_cast<const T*>(p.q);
     const T* k = static_cast<const T*>(p.k);
     const T* v = static_cast<const T*>(p.v);
     const T* beta = static_cast<const T*>(p.beta);
-    const size_t jh = size_t(j) * p.H + h;
     constexpr int V8 = 16 / sizeof(T);  // elements per 16-byte vector
-
-    // ---- phase 1: every global input of the chunk is requested up front
-    //      (fixed trip counts; rows past the sequence end read the last row and
-    //      are zeroed at use); v stays in registers until phase 8 ----
     constexpr int NGP = C * (D / 4) / NT;    // 4-float gate pieces per thread
     constexpr int NQP = C * (D / V8) / NT;   // 16-byte q / k / v pieces per thread
     static_assert(NGP * NT == C * (D / 4) && NQP * NT == C * (D / V8), "piece split");
     f32x4 gpre[NGP];
     Vec16 qpre[NQP], kpre[NQP], vpre[NQP];
+    float bpre;
+    // rows past the sequence end read the last row (zeroed at use)
+    auto load_in = [&](const int it, const ChunkEntry& e2) __attribute__((always_inline)) {
+        const int hh = it % p.H, hkk = hh / p.G;
 #pragma unroll
-    for (int i = 0; i < NGP; ++i) {
-        const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4, rt = min(r, len - 1);
-        if constexpr (SCALAR) {
-            const float sg = p.g[(size_t)(tok0 + rt) * p.H + h];
-            gpre[i] = f32x4{sg, sg, sg, sg};
-        } else {
-            gpre[i] = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(tok0 + rt) * p.H + h) * D + d0);
+        for (int i = 0; i < NGP; ++i) {
+            const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4, rt = min(r, e2.len - 1);
+            if constexpr (SCALAR) {
+                const float sg = p.g[(size_t)(e2.tok0 + rt) * p.H + hh];
+                gpre[i] = f32x4{sg, sg, sg, sg};
+            } else {
+                gpre[i] = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(e2.tok0 + rt) * p.H + hh) * D + d0);
+            }
         }
-    }
 #pragma unroll
-    for (int i = 0; i < NQP; ++i) {
-        const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8, rt = min(r, len - 1);
-        qpre[i] = ld16(q + ((size_t)(tok0 + rt) * p.Hg + hk) * D + d0);
-        kpre[i] = ld16(k + ((size_t)(tok0 + rt) * p.Hg + hk) * D + d0);
-        vpre[i] = ld16(v + ((size_t)(tok0 + rt) * p.H + h) * D + d0);
-    }
-    const float bpre = to_f32(beta[(size_t)(tok0 + min(tid, len - 1)) * p.H + h]);
+        for (int i = 0; i < NQP; ++i) {
+            const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8, rt = min(r, e2.len - 1);
+            qpre[i] = ld16(q + ((size_t)(e2.tok0 + rt) * p.Hg + hkk) * D + d0);
+            kpre[i] = ld16(k + ((size_t)(e2.tok0 + rt) * p.Hg + hkk) * D + d0);
+        }
+        bpre = to_f32(beta[(size_t)(e2.tok0 + min(tid, e2.len - 1)) * p.H + hh]);
+    };
+    auto load_v = [&](const int it, const ChunkEntry& e2) __attribute__((always_inline)) {
+        const int hh = it % p.H;
+#pragma unroll
+        for (int i = 0; i < NQP; ++i) {
+            const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8, rt = min(r, e2.len - 1);
+            vpre[i] = ld16(v + ((size_t)(e2.tok0 + rt) * p.H + hh) * D + d0);
+        }
+    };
+    ChunkEntry ce = p.ctab[item / p.H];
+    load_in(item, ce);
+    load_v(item, ce);
+
+    for (; item < nit; item += gridDim.x) {
+    const int j = item / p.H, h = item % p.H;
+    const int tok0 = ce.tok0, len = ce.len;
+    const size_t jh = size_t(j) * p.H + h;
+    const int nxt = min(item + (int)gridDim.x, nit - 1);   // past the end: a redundant valid load
+    const ChunkEntry ce_n = p.ctab[nxt / p.H];
+    // a fresh opaque thread index per item: thread-dependent address arithmetic
+    // is recomputed in every item instead of being kept live across items
+    const int tid = [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }();
+    const int l = tid & 63;
+    __syncthreads();  // the previous item's LDS use is over
+
+    // ---- phase 1: this item's inputs (already in registers) to LDS ----
     for (int e = tid; e < C * LCF / 4; e += NT) {
         reinterpret_cast<f32x4*>(AqkF)[e] = zero4();
         reinterpret_cast<f32x4*>(AkkF)[e] = zero4();
@@ -217,6 +243,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         st16(kL + r * LT + d0, r < len ? kpre[i] : Vec16{});
     }
     if (tid < C) bs[tid] = tid < len ? bpre : 0.f;
+    load_in(nxt, ce_n);  // the next item's g, q, k, beta
     __syncthreads();
     {   // column cumsum in NSEG segments of SR rows: local scans, then segment offsets
         constexpr int NSEG = NT / D > 0 ? NT / D : 1, SR = C / NSEG;
@@ -246,7 +273,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         using F = typename Mfma<T>::frag;
         constexpr int KL = Mfma<T>::KL, KS = 4 * KL;
         constexpr float guard = __is_same(T, _Float16) ? 8.f : 64.f;
-        const int l = lane_id(), b0 = 16 * (w % NB), r = b0 + (l & 15);
+        const int b0 = 16 * (w % NB), r = b0 + (l & 15);
         f32x4 acc = zero4();
         float rmax = 0.f;
 #pragma unroll 2
@@ -364,10 +391,10 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         for (int t = w; t < ntile; t += L::NW) {
             const int which = t / ib, ct = t % ib;
             f32x4 acc[1] = {zero4()};
-            panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct);
+            panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct, l);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = rho + acc_row(i), s2 = 16 * ct + acc_col();
+                const int r = rho + acc_row(i, l), s2 = 16 * ct + acc_col(l);
                 if (which) AkkF[r * LCF + s2] = bs[r] * acc[0][i];
                 else AqkF[r * LCF + s2] = acc[0][i];
             }
@@ -397,17 +424,17 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         if (w < bi) {
             const int bj = w;
             f32x4 acc = zero4();
-            acc = tile_f32(acc, AkkF, LCF, 16 * bi, 16 * bj, AF, LCF, 16 * bj, 16 * bj, 16 * (bi - bj));
+            acc = tile_f32(acc, AkkF, LCF, 16 * bi, 16 * bj, AF, LCF, 16 * bj, 16 * bj, 16 * (bi - bj), l);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[acc_row(i) * 20 + acc_col()] = acc[i];
+            for (int i = 0; i < 4; ++i) sc[acc_row(i, l) * 20 + acc_col(l)] = acc[i];
         }
         __syncthreads();
         if (w < bi) {
             const int bj = w;
             f32x4 acc = zero4();
-            acc = tile_f32(acc, AF, LCF, 16 * bi, 16 * bi, sc, 20, 0, 0, 16);
+            acc = tile_f32(acc, AF, LCF, 16 * bi, 16 * bi, sc, 20, 0, 0, 16, l);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) AF[(16 * bi + acc_row(i)) * LCF + 16 * bj + acc_col()] = -acc[i];
+            for (int i = 0; i < 4; ++i) AF[(16 * bi + acc_row(i, l)) * LCF + 16 * bj + acc_col(l)] = -acc[i];
         }
         __syncthreads();
     }
@@ -459,12 +486,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     f32x4 acc[NTH];
 #pragma unroll
     for (int t = 0; t < NTH; ++t) acc[t] = zero4();
-    panel_mma<T, NTH, C>(acc, AtL, LC, r0, khT, LC, ch0);
+    panel_mma<T, NTH, C>(acc, AtL, LC, r0, khT, LC, ch0, l);
     __syncthreads();  // khT is about to be overwritten by w^T
     T* wTL = Xb;  // [D][LC]
 #pragma unroll
     for (int t = 0; t < NTH; ++t) {
-        const int c = ch0 + 16 * t + acc_col(), rb = r0 + acc_row(0);
+        const int c = ch0 + 16 * t + acc_col(l), rb = r0 + acc_row(0, l);
         store4<T>(wTL + c * LC + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     }
     __syncthreads();
@@ -489,12 +516,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     // ---- phase 7: q~ = q 2^G - Aqk w, stored as scale * q~^T ----
 #pragma unroll
     for (int t = 0; t < NTH; ++t) acc[t] = zero4();
-    panel_mma<T, NTH, C>(acc, AqkL, LC, r0, wTL, LC, ch0);
+    panel_mma<T, NTH, C>(acc, AqkL, LC, r0, wTL, LC, ch0, l);
     {
         T* gq = static_cast<T*>(p.qsT) + jh * D * C;
 #pragma unroll
         for (int t = 0; t < NTH; ++t) {
-            const int c = ch0 + 16 * t + acc_col(), rb = r0 + acc_row(0);
+            const int c = ch0 + 16 * t + acc_col(l), rb = r0 + acc_row(0, l);
             float o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -516,15 +543,16 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
         for (int i = 0; i < V8; ++i) vhT[(d0 + i) * LC + s2] = from_f32<T>(bs[s2] * to_f32(vp[i]));
     }
+    load_v(nxt, ce_n);  // the next item's v
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NTH; ++t) acc[t] = zero4();
-    panel_mma<T, NTH, C>(acc, AtL, LC, r0, vhT, LC, ch0);
+    panel_mma<T, NTH, C>(acc, AtL, LC, r0, vhT, LC, ch0, l);
     {
         T* gu = static_cast<T*>(p.uT) + jh * D * C;
 #pragma unroll
         for (int t = 0; t < NTH; ++t) {
-            const int c = ch0 + 16 * t + acc_col(), rb = r0 + acc_row(0);
+            const int c = ch0 + 16 * t + acc_col(l), rb = r0 + acc_row(0, l);
             store4<T>(gu + c * C + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
         }
     }
@@ -553,6 +581,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             store8<T>(gktT + d * C + r0b, x);
         }
         for (int d = tid; d < D; d += NT) p.glast[jh * D + d] = fast_exp2(Gs[(C - 1) * LF + d]);
+    }
+    ce = ce_n;
     }
 }
 
