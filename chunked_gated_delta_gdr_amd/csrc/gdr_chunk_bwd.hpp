@@ -42,7 +42,7 @@ namespace gdr {
 template <typename T, int C, int D>
 struct BwdLds {
     static constexpr int NB = C / 16;
-    static constexpr int BVS = 32;  // V slice of the state products
+    static constexpr int BVS = kTileV;  // V slice of the state products (the stored tile)
     static constexpr int LT = D + pad<T>();
     static constexpr int LC = C + pad<T>();
     static constexpr int LB = BVS + pad<T>();
@@ -279,15 +279,15 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 const int r = e / PR, c = (e % PR) * V8, rt = min(r, len - 1);
                 pdo[i] = ld16(dorow + (long)rt * ldo + v0 + c);
                 pv[i] = ld16(v + ((size_t)(tok0 + rt) * p.H + h) * D + v0 + c);
-                px[i] = ld16(xb + (size_t)r * D + v0 + c);
-                pt[i] = ld16(tb + (size_t)r * D + v0 + c);
+                px[i] = ld16(xb + (size_t)v0 * C + r * BVS + c);   // V-tiled
+                pt[i] = ld16(tb + (size_t)v0 * C + r * BVS + c);
             }
 #pragma unroll
             for (int i = 0; i < NPD; ++i) {
                 const int e = min(tid + NT * i, D * PR - 1);
                 const int d = e / PR, c = (e % PR) * V8;
-                ph[i] = ld16(hb + (size_t)d * D + v0 + c);
-                pdh[i] = ld16(dhb + (size_t)d * D + v0 + c);
+                ph[i] = ld16(hb + (size_t)v0 * D + d * BVS + c);   // V-tiled
+                pdh[i] = ld16(dhb + (size_t)v0 * D + d * BVS + c);
             }
         };
         load_slice(0);

@@ -266,6 +266,10 @@ __device__ __forceinline__ void st16(void* p, Vec16 v) { *reinterpret_cast<Vec16
 // ---------------------------------------------------------------------------
 // Kernel parameters (one struct passed by value to every kernel).
 // ---------------------------------------------------------------------------
+// Column tile of the stored per-chunk states and X / T (the state sweep's
+// V tile and the gradient kernel's V slice).
+constexpr int kTileV = 32;
+
 struct ChunkEntry {
     int tok0;   // flattened token index (b*T + t) of the chunk's first token
     int len;    // real tokens in the chunk (1..C)
@@ -299,10 +303,12 @@ struct Params {
     void* uT;            // [nc][H][D][C]  u = A (beta v), transposed
     void* qsT;           // [nc][H][D][C]  scale * (q 2^G - Aqk w), transposed
     float* glast;        // [nc][H][D]     2^G_last
-    void* hbuf;          // [nc][H][D][D]  state before the chunk
-    void* xbuf;          // [nc][H][C][D]  X = u - w h
-    void* dhbuf;         // [nc][H][D][D]  dL/dS at the chunk end
-    void* tbuf;          // [nc][H][C][D]  k~ dh
+    // V-tiled ([..][D / kTileV][rows][kTileV]): one contiguous block per
+    // (chunk, head, tile of kTileV state columns)
+    void* hbuf;          // [nc][H][D/kTileV][D][kTileV]  state before the chunk
+    void* xbuf;          // [nc][H][D/kTileV][C][kTileV]  X = u - w h
+    void* dhbuf;         // [nc][H][D/kTileV][D][kTileV]  dL/dS at the chunk end
+    void* tbuf;          // [nc][H][D/kTileV][C][kTileV]  k~ dh
 };
 
 }  // namespace gdr

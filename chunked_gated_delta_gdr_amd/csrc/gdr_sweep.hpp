@@ -196,7 +196,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
             }
         {   // the incoming state to the workspace, row-major: 8 columns per piece
-            T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D + v0;
+            T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D + (size_t)v0 * D;  // this V tile
 #pragma unroll
             for (int pi = 0; pi < (D * BV / V8 + 255) / 256; ++pi) {
                 const int e = threadIdx.x + 256 * pi;
@@ -206,7 +206,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                     T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
                     for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
-                    st16(gS + (size_t)d * D + c, v);
+                    st16(gS + (size_t)d * BV + c, v);
                 }
             }
         }
@@ -231,7 +231,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 }
             }
         {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
-            T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D + v0;
+            T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D + (size_t)v0 * C;  // this V tile
 #pragma unroll
             for (int pi = 0; pi < (C * BV / V8 + 255) / 256; ++pi) {
                 const int e = threadIdx.x + 256 * pi;
@@ -244,7 +244,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                         const T x = sX[(c + q) * LX + r];
                         vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
                     }
-                    st16(gX + (size_t)r * D + c, v);
+                    st16(gX + (size_t)r * BV + c, v);
                 }
             }
         }
@@ -286,6 +286,7 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     constexpr int LS = D + pad<T>();
     constexpr int LX = C + pad<T>();
     constexpr int NPF = 3;                           // chunks of operands in flight
+    static_assert(BV == kTileV, "the stored states are tiled by the sweep's V tile");
     __shared__ __attribute__((aligned(16))) T sS[BV * LS];
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
     __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];

@@ -146,7 +146,8 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d,
  *   5 w, 6 w^T, 7 k~, 8 k~^T, 9 u^T, 10 scale*q~^T, 11 2^G_last,
  *   12 h (state before each chunk), 13 X, 14 dh (state gradient at each
  *   chunk end), 15 T = k~ dh, 16 = total bytes.
- * Per-chunk regions are [chunks][H][..] in io_dtype (2^G_last in fp32).
+ * Per-chunk regions are [chunks][H][..] in io_dtype (2^G_last in fp32);
+ * h, X, dh and T are stored in tiles of 32 state columns, [D/32][rows][32].
  * For inspecting intermediates in tests; n must be >= 17.
  * Returns GDR_OK, GDR_EINVAL or GDR_EUNSUPPORTED. Touches no GPU state.
  */

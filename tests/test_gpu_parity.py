@@ -150,7 +150,9 @@ def test_stage_states_match_oracle():
     nch, D = ref["h_chunks"].shape[0], w.K
     for name, key in (("h", "h_chunks"), ("dh", "dh_chunks")):
         raw = ws[offs[name]: offs[name] + nch * w.H * D * D * 2].cpu()
-        got = raw.view(torch.bfloat16).double().numpy().reshape(nch, w.H, D, D)
+        # stored in tiles of 32 state columns: [nch][H][D/32][D][32]
+        got = (raw.view(torch.bfloat16).double().numpy().reshape(nch, w.H, D // 32, D, 32)
+               .transpose(0, 1, 3, 2, 4).reshape(nch, w.H, D, D))
         err = np.abs(got - ref[key]).max() / np.abs(ref[key]).max()
         assert err < 2e-2, f"{name}: {err}"
 
