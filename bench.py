@@ -214,6 +214,55 @@ def summarize_kernel_stats(stats_csv: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def bench_fwd(args, w, inp, t, tokens, n_chunks, n_seqs, ws) -> int:
+    """The forward pass (o and the final states) on the same workload: total
+    time per call with HIP events on the launch stream."""
+    import torch
+    import chunked_gated_delta_gdr_amd as gdr
+    dev = t["q"].device
+    o = torch.empty_like(t["v"])
+    ht = torch.empty((n_seqs, w.H, w.K, w.V), dtype=torch.float32, device=dev)
+
+    def step():
+        gdr.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], h0=t["h0"], cu_seqlens=t["cu_seqlens"],
+                scale=inp["scale"], chunk_size=w.chunk, workspace=ws, out=(o, ht))
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    es = 4 if w.io_dtype == torch.float32 else 2
+    th = tokens * w.H
+    # bytes: q, k, v, g, beta read once, o written once, the per-chunk state
+    # written once and read once, h0 read and ht written per (sequence, head)
+    qk = 2 * w.K * es * w.Hg / w.H
+    gb = w.K * 4 if w.gate == "kda" else 4
+    per_th = qk + w.V * es + gb + es + w.V * es + 2 * w.K * w.V * es * n_chunks * w.H / th \
+        + 2 * w.K * w.V * 4 * n_seqs * w.H / th
+    res = {
+        "metric": "gated-delta-rule fwd tokens/s (B*T) at H=16,K=V=128",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[w.io_dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "fwd", "tokens": tokens, "H": w.H, "Hg": w.Hg, "K": w.K,
+                   "V": w.V, "chunk": w.chunk, "gate": w.gate, "n_seqs": n_seqs,
+                   "parallelism": "single-gpu"},
+        "step_roofline": {"method_bytes": per_th * th,
+                          "hbm_frac": per_th * th / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +270,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="kda_fixed_h16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("bwd", "fwd"), default="bwd",
+                    help="bwd (the headline) or fwd (the forward pass: o and final states)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after the timed steps, run a plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -262,6 +313,9 @@ def main() -> int:
     out = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"]),
            torch.empty_like(t["g"]), torch.empty_like(t["beta"]),
            torch.empty_like(t["h0"]))
+
+    if args.which == "fwd":
+        return bench_fwd(args, w, inp, t, tokens, n_chunks, n_seqs, ws)
 
     def step(events=None):
         gdr.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], h0=t["h0"], dht=t["dht"],

@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["bwd", "workspace_bytes", "workspace_offsets", "library_path", "Desc",
+__all__ = ["bwd", "fwd", "workspace_bytes", "workspace_offsets", "library_path", "Desc",
            "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +63,8 @@ def _load():
         lib.gdr_bwd_with_events.restype = ctypes.c_int
         lib.gdr_bwd_with_events.argtypes = [D] + [P] * 15 + [P, ctypes.c_size_t, P,
                                                               ctypes.POINTER(ctypes.c_void_p)]
+        lib.gdr_fwd.restype = ctypes.c_int
+        lib.gdr_fwd.argtypes = [D] + [P] * 9 + [P, ctypes.c_size_t, P]
         lib.gdr_strerror.restype = ctypes.c_char_p
         lib.gdr_strerror.argtypes = [ctypes.c_int]
         lib.gdr_version.restype = ctypes.c_char_p
@@ -194,3 +196,53 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
     if rc != 0:
         raise _err(rc)
     return dq, dk, dv, dg, db, dh0
+
+
+def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk_size: int = 64,
+        workspace: Optional[torch.Tensor] = None, out=None, final_state: bool = True):
+    """Forward of the gated delta rule: returns (o, ht).
+
+    Same inputs as :func:`bwd` (without do, dht). o [B,T,H,V] in the io dtype;
+    ht fp32 [N,H,K,V] (None when ``final_state`` is False). ``workspace`` and
+    ``out`` (o, ht) may be preallocated.
+    """
+    lib = _load()
+    io = q.dtype
+    if io not in _DTYPES:
+        raise TypeError(f"unsupported io dtype {io}")
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    gate = GATE_PER_CHANNEL if g.dim() == 4 else GATE_SCALAR
+    n_seqs, N = 0, B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.shape[0],))
+        n_seqs = N = cu_seqlens.shape[0] - 1
+    _need(q, "q", io, (B, T, Hg, K))
+    _need(k, "k", io, (B, T, Hg, K))
+    _need(v, "v", io, (B, T, H, V))
+    _need(beta, "beta", io, (B, T, H))
+    _need(g, "g", torch.float32, (B, T, H, K) if gate == GATE_PER_CHANNEL else (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, H, K, V))
+    desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
+                     io_dtype=io, scale=float(scale) if scale is not None else 0.0)
+    rc = check(desc)
+    if rc != 0:
+        raise _err(rc)
+    nbytes = workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() < nbytes or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be uint8 with >= {nbytes} bytes")
+    if out is None:
+        o = torch.empty_like(v)
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device) if final_state else None
+    else:
+        o, ht = out
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.gdr_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                     _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),
+                     ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise _err(rc)
+    return o, ht

@@ -92,27 +92,20 @@ int gdr_bwd_workspace_offsets(const gdr_bwd_desc_t* d, size_t* offsets, int n) {
     return GDR_OK;
 }
 
-int gdr_bwd_with_events(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v,
-                        const float* g, const void* beta, const float* h0, const void* do_,
-                        const float* dht, const int32_t* cu_seqlens, void* dq, void* dk, void* dv,
-                        float* dg, void* db, float* dh0, void* workspace, size_t workspace_bytes,
-                        void* stream, void* const* stage_events) {
+}  // extern "C"
+
+// Checks shared by both passes and the parameter block (problem, workspace).
+static int fill_params(const gdr_bwd_desc_t* d, const int32_t* cu_seqlens, void* workspace,
+                       size_t workspace_bytes, gdr::Params& p) {
     int rc = gdr_bwd_check(d);
     if (rc != GDR_OK) return rc;
-    const void* req[] = {q, k, v, g, beta, do_, dq, dk, dv, dg, db, dh0};
-    for (const void* p : req)
-        if (!p || !aligned16(p)) return GDR_EINVAL;
-    if ((h0 && !aligned16(h0)) || (dht && !aligned16(dht))) return GDR_EINVAL;
     if ((d->n_seqs > 0) != (cu_seqlens != nullptr)) return GDR_EINVAL;
     size_t off[WS_COUNT + 1];
     layout(d, off);
     if (!workspace || workspace_bytes < off[WS_COUNT]) return GDR_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GDR_EINVAL;
-    gdr::LaunchFn fn = gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR);
-    if (!fn) return GDR_EUNSUPPORTED;
-
     char* ws = static_cast<char*>(workspace);
-    gdr::Params p{};
+    p = gdr::Params{};
     p.B = d->B;
     p.T = d->T;
     p.H = d->H;
@@ -122,9 +115,7 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d, const void* q, const void* k, c
     p.nc_max = (int)max_chunks(d);
     p.varlen = d->n_seqs > 0;
     p.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->K);
-    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = do_; p.dht = dht;
     p.cu = cu_seqlens;
-    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
     p.ctab = reinterpret_cast<gdr::ChunkEntry*>(ws + off[WS_CTAB]);
     p.seq_off = reinterpret_cast<int*>(ws + off[WS_SEQOFF]);
     p.sAqkT = ws + off[WS_SAQKT];
@@ -141,14 +132,59 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d, const void* q, const void* k, c
     p.xbuf = ws + off[WS_X];
     p.dhbuf = ws + off[WS_DH];
     p.tbuf = ws + off[WS_T];
+    return GDR_OK;
+}
 
-    hipError_t e = fn(p, static_cast<hipStream_t>(stream),
-                      reinterpret_cast<hipEvent_t const*>(stage_events));
+static int launch(gdr::LaunchFn fn, const gdr::Params& p, void* stream, void* const* events) {
+    if (!fn) return GDR_EUNSUPPORTED;
+    hipError_t e = fn(p, static_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t const*>(events));
     if (e != hipSuccess) {
         g_hip_msg = std::string("HIP error: ") + hipGetErrorString(e);
         return GDR_EHIP;
     }
     return GDR_OK;
+}
+
+extern "C" {
+
+int gdr_bwd_with_events(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v,
+                        const float* g, const void* beta, const float* h0, const void* do_,
+                        const float* dht, const int32_t* cu_seqlens, void* dq, void* dk, void* dv,
+                        float* dg, void* db, float* dh0, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* stage_events) {
+    int rc = gdr_bwd_check(d);
+    if (rc != GDR_OK) return rc;
+    const void* req[] = {q, k, v, g, beta, do_, dq, dk, dv, dg, db, dh0};
+    for (const void* ptr : req)
+        if (!ptr || !aligned16(ptr)) return GDR_EINVAL;
+    if ((h0 && !aligned16(h0)) || (dht && !aligned16(dht))) return GDR_EINVAL;
+    gdr::Params p;
+    rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
+    if (rc != GDR_OK) return rc;
+    p.dirs = 2;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = do_; p.dht = dht;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
+    return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 0), p,
+                  stream, stage_events);
+}
+
+int gdr_fwd(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v, const float* g,
+            const void* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
+            void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = gdr_bwd_check(d);
+    if (rc != GDR_OK) return rc;
+    const void* req[] = {q, k, v, g, beta, o};
+    for (const void* ptr : req)
+        if (!ptr || !aligned16(ptr)) return GDR_EINVAL;
+    if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return GDR_EINVAL;
+    gdr::Params p;
+    rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
+    if (rc != GDR_OK) return rc;
+    p.dirs = 1;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
+    p.o = o; p.ht = ht;
+    return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 1), p,
+                  stream, nullptr);
 }
 
 int gdr_bwd(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v, const float* g,

@@ -284,12 +284,14 @@ struct Params {
     int N;               // sequences
     int nc_max;          // chunk-table capacity (grid size of chunk-parallel kernels)
     int varlen;
+    int dirs;            // state sweeps run: 1 = forward only (the forward pass), 2 = both
     float scale;
     // inputs
     const void* q; const void* k; const void* v; const float* g; const void* beta;
     const float* h0; const void* dout; const float* dht; const int* cu;
     // outputs
     void* dq; void* dk; void* dv; float* dg; void* db; float* dh0;
+    void* o; float* ht;  // forward pass: outputs and final states (ht may be NULL)
     // workspace
     ChunkEntry* ctab;    // [nc_max]
     int* seq_off;        // [N+1] first chunk of each sequence; seq_off[N] = chunk count

@@ -6,19 +6,22 @@ namespace gdr {
 
 #define GDR_DECL(T, C, D)                                                         \
     extern template hipError_t launch_bwd<T, C, D, false>(const Params&, hipStream_t, hipEvent_t const*); \
-    extern template hipError_t launch_bwd<T, C, D, true>(const Params&, hipStream_t, hipEvent_t const*);
+    extern template hipError_t launch_bwd<T, C, D, true>(const Params&, hipStream_t, hipEvent_t const*);  \
+    extern template hipError_t launch_fwd<T, C, D, false>(const Params&, hipStream_t, hipEvent_t const*); \
+    extern template hipError_t launch_fwd<T, C, D, true>(const Params&, hipStream_t, hipEvent_t const*);
 #define GDR_DECL_T(T) GDR_DECL(T, 32, 64) GDR_DECL(T, 32, 128) GDR_DECL(T, 64, 64) GDR_DECL(T, 64, 128)
 GDR_DECL(float, 32, 64)
 GDR_DECL(float, 64, 64)
 GDR_DECL_T(__bf16)
 GDR_DECL_T(_Float16)
 
-#define GDR_CASE(T, C, D)                                                \
-    if (chunk == C && dim == D)                                          \
-        return scalar ? &launch_bwd<T, C, D, true> : &launch_bwd<T, C, D, false>;
+#define GDR_CASE(T, C, D)                                                                         \
+    if (chunk == C && dim == D)                                                                   \
+        return pass ? (scalar ? &launch_fwd<T, C, D, true> : &launch_fwd<T, C, D, false>)         \
+                    : (scalar ? &launch_bwd<T, C, D, true> : &launch_bwd<T, C, D, false>);
 
 template <typename T>
-static LaunchFn pick(int chunk, int dim, int scalar) {
+static LaunchFn pick(int chunk, int dim, int scalar, int pass) {
     GDR_CASE(T, 32, 64) GDR_CASE(T, 32, 128) GDR_CASE(T, 64, 64) GDR_CASE(T, 64, 128)
     return nullptr;
 }
@@ -26,17 +29,17 @@ static LaunchFn pick(int chunk, int dim, int scalar) {
 // fp32 io (full-precision operands) is built for K = V = 64 only: its LDS
 // tiles are twice as large and K = 128 does not fit the 160 KB of a CU.
 template <>
-LaunchFn pick<float>(int chunk, int dim, int scalar) {
+LaunchFn pick<float>(int chunk, int dim, int scalar, int pass) {
     GDR_CASE(float, 32, 64) GDR_CASE(float, 64, 64)
     return nullptr;
 }
 #undef GDR_CASE
 
-LaunchFn find_launcher(int io_dtype, int chunk, int dim, int scalar) {
+LaunchFn find_launcher(int io_dtype, int chunk, int dim, int scalar, int pass) {
     switch (io_dtype) {
-        case 0: return pick<float>(chunk, dim, scalar);
-        case 1: return pick<__bf16>(chunk, dim, scalar);
-        case 2: return pick<_Float16>(chunk, dim, scalar);
+        case 0: return pick<float>(chunk, dim, scalar, pass);
+        case 1: return pick<__bf16>(chunk, dim, scalar, pass);
+        case 2: return pick<_Float16>(chunk, dim, scalar, pass);
         default: return nullptr;
     }
 }

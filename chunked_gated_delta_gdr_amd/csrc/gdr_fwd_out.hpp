@@ -1,0 +1,98 @@
+// gdr_fwd_out.hpp -- chunk-parallel output kernel of the forward pass.
+//
+// With h_c the state before chunk c (from the forward state sweep) and the
+// chunk factors of the preparation kernel, the chunk form of the output
+//     o_c = scale [(q 2^G) h_c + Aqk X_c],   X_c = u - w h_c
+// (the WY recompute of the FlashQLA page's fused_bwd.py) is, with
+// q~ = q 2^G - Aqk w,
+//     o_c = (scale q~) h_c + (scale Aqk) u,
+// two products on the stored scale q~^T, scale Aqk^T, u^T and h_c. One
+// workgroup per (chunk, value head); wave w owns rows 16 w .. +16 and every
+// column. Operands are staged in LDS as stored; the ones kept with the
+// reduction index as the row are read as strided fragments.
+#pragma once
+#include "gdr_common.hpp"
+
+namespace gdr {
+
+template <typename T, int C, int D>
+struct FwdOutLds {
+    static constexpr int LC = C + pad<T>(), LH = D + pad<T>();
+    static constexpr size_t QS = 0;                                  // T [D][LC] scale q~^T
+    static constexpr size_t SA = QS + size_t(D) * LC * sizeof(T);    // T [C][LC] scale Aqk^T
+    static constexpr size_t UT = SA + size_t(C) * LC * sizeof(T);    // T [D][LC] u^T
+    static constexpr size_t HL = UT + size_t(D) * LC * sizeof(T);    // T [D][LH] h_c, row-major
+    static constexpr size_t TOTAL = HL + size_t(D) * LH * sizeof(T);
+    static constexpr size_t OS = 0;                                  // T [C][LH] o, over the dead operands
+    static_assert(size_t(C) * LH * sizeof(T) <= HL, "o staging clear of h");
+    static_assert(TOTAL <= 163840, "LDS budget of gdr_fwd_out");
+};
+
+template <typename T, int C, int D>
+__global__ __launch_bounds__(64 * (C / 16)) void gdr_fwd_out(Params p) {
+    using L = FwdOutLds<T, C, D>;
+    constexpr int NB = C / 16, NT = 64 * NB, LC = L::LC, LH = L::LH, NTD = D / 16;
+    constexpr int V8 = 16 / sizeof(T), KS = kstep<T>(), PT = kTileV / V8;
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    T* qsL = reinterpret_cast<T*>(smem + L::QS);
+    T* saL = reinterpret_cast<T*>(smem + L::SA);
+    T* uL = reinterpret_cast<T*>(smem + L::UT);
+    T* hL = reinterpret_cast<T*>(smem + L::HL);
+    T* oS = reinterpret_cast<T*>(smem + L::OS);
+
+    const int j = blockIdx.x, h = blockIdx.y;
+    if (j >= p.seq_off[p.N]) return;
+    const ChunkEntry ce = p.ctab[j];
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const size_t jh = (size_t)j * p.H + h;
+    const T* gq = static_cast<const T*>(p.qsT) + jh * D * C;
+    const T* ga = static_cast<const T*>(p.sAqkT) + jh * C * C;
+    const T* gu = static_cast<const T*>(p.uT) + jh * D * C;
+    const T* gh = static_cast<const T*>(p.hbuf) + jh * D * D;   // [D/kTileV][D][kTileV]
+
+    for (int e = tid; e < D * (C / V8); e += NT) {
+        const int d = e / (C / V8), c = (e % (C / V8)) * V8;
+        st16(qsL + d * LC + c, ld16(gq + (size_t)d * C + c));
+        st16(uL + d * LC + c, ld16(gu + (size_t)d * C + c));
+    }
+    for (int e = tid; e < C * (C / V8); e += NT) {
+        const int r = e / (C / V8), c = (e % (C / V8)) * V8;
+        st16(saL + r * LC + c, ld16(ga + (size_t)r * C + c));
+    }
+    for (int e = tid; e < D * (D / V8); e += NT) {   // contiguous in the tiled layout
+        const int vt = e / (D * PT), rem = e % (D * PT), d = rem / PT, c = (rem % PT) * V8;
+        st16(hL + d * LH + vt * kTileV + c, ld16(gh + (size_t)vt * D * kTileV + d * kTileV + c));
+    }
+    __syncthreads();
+
+    const int r0 = 16 * w;
+    f32x4 acc[NTD];
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) acc[t] = zero4();
+    // (scale q~) h: A(r, d) = qsT[d][r], B(d, v) = h[d][v]
+    for (int k0 = 0; k0 < D; k0 += KS) {
+        const auto a = frag_ks(qsL, LC, r0, k0, l);
+#pragma unroll
+        for (int t = 0; t < NTD; ++t) acc[t] = Mfma<T>::mma(a, frag_ks(hL, LH, 16 * t, k0, l), acc[t]);
+    }
+    // (scale Aqk) u: A(r, s) = sAqkT[s][r], B(s, v) = u[s][v] = uT[v][s]
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += KS) {
+        const auto a = frag_ks(saL, LC, r0, k0, l);
+#pragma unroll
+        for (int t = 0; t < NTD; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(uL, LC, 16 * t, k0, l), acc[t]);
+    }
+    __syncthreads();  // operands read: the staging of o overwrites them
+#pragma unroll
+    for (int t = 0; t < NTD; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oS[(r0 + acc_row(i, l)) * LH + 16 * t + acc_col(l)] = from_f32<T>(acc[t][i]);
+    __syncthreads();
+    T* go = static_cast<T*>(p.o) + ((size_t)ce.tok0 * p.H + h) * D;
+    for (int e = tid; e < C * (D / V8); e += NT) {
+        const int r = e / (D / V8), c = (e % (D / V8)) * V8;
+        if (r < ce.len) st16(go + (size_t)r * p.H * D + c, ld16(oS + r * LH + c));
+    }
+}
+
+}  // namespace gdr

@@ -1,6 +1,8 @@
-// Explicit instantiation: io dtype _Float16, chunk 64, K = V = 128, both gate forms.
+// Explicit instantiation: io dtype _Float16, chunk 64, K = V = 128, both gate forms, both passes.
 #include "gdr_launch.hpp"
 namespace gdr {
 template hipError_t launch_bwd<_Float16, 64, 128, false>(const Params&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_fwd<_Float16, 64, 128, false>(const Params&, hipStream_t, hipEvent_t const*);
 template hipError_t launch_bwd<_Float16, 64, 128, true>(const Params&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_fwd<_Float16, 64, 128, true>(const Params&, hipStream_t, hipEvent_t const*);
 }  // namespace gdr

@@ -1,6 +1,7 @@
 // gdr_launch.hpp -- enqueues the four kernels of one backward pass on a stream.
 #pragma once
 #include "gdr_chunk_bwd.hpp"
+#include "gdr_fwd_out.hpp"
 #include "gdr_prep.hpp"
 #include "gdr_sweep.hpp"
 
@@ -25,8 +26,10 @@ inline int compute_units() {
     return cached[dev];
 }
 
+// Chunk table, per-chunk preparation and the state sweep(s) (p.dirs of them):
+// the start of both passes. ev as above (entries 0..3).
 template <typename T, int C, int D, bool SCALAR>
-hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
+hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
     hipError_t e = mark(0);
     // chunk table (device-side, so varlen needs no host sync)
@@ -39,19 +42,37 @@ hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
                                     dim3(128 * (C / 16)), 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(2);
-    gdr_sweep<T, C, D, kSweepBV><<<dim3(2 * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
+    gdr_sweep<T, C, D, kSweepBV><<<dim3(p.dirs * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(3);
+    return e;
+}
+
+// The backward pass (p.dirs == 2): four kernels.
+template <typename T, int C, int D, bool SCALAR>
+hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
+    hipError_t e = launch_front<T, C, D, SCALAR>(p, stream, ev);
     if (p.nc_max > 0) {
         const dim3 grid(p.nc_max, p.Hg), block(128 * (C / 16));
         if (p.G > 1) gdr_chunk_bwd<T, C, D, SCALAR, true><<<grid, block, 0, stream>>>(p);
         else gdr_chunk_bwd<T, C, D, SCALAR, false><<<grid, block, 0, stream>>>(p);
     }
-    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[4], stream);
+    const hipError_t le = hipGetLastError();
+    return le != hipSuccess ? le : e;
+}
+
+// The forward pass (p.dirs == 1): the same front, then the output kernel.
+template <typename T, int C, int D, bool SCALAR>
+hipError_t launch_fwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
+    hipError_t e = launch_front<T, C, D, SCALAR>(p, stream, ev);
+    if (p.nc_max > 0) gdr_fwd_out<T, C, D><<<dim3(p.nc_max, p.H), dim3(64 * (C / 16)), 0, stream>>>(p);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[4], stream);
     const hipError_t le = hipGetLastError();
     return le != hipSuccess ? le : e;
 }
 
 // Instantiated in gdr_inst_*.hip; looked up by the C ABI.
-LaunchFn find_launcher(int io_dtype, int chunk, int dim, int scalar);
+// pass: 0 = backward, 1 = forward.
+LaunchFn find_launcher(int io_dtype, int chunk, int dim, int scalar, int pass);
 
 }  // namespace gdr

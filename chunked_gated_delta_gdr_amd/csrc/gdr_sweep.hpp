@@ -268,7 +268,9 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
         for (int s2 = 0; s2 < NPF - 1; ++s2)
             if (k0 + s2 < nch) step(ops[s2], k0 + s2);
     }
-    if constexpr (DIR == 1) {
+    // the final state: dh0 (reverse), or ht for the forward pass when asked
+    float* fin = DIR == 1 ? p.dh0 : p.ht;
+    if (fin) {
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
@@ -276,7 +278,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int d = 16 * (w * S::SRW + i) + acc_row(e), c = v0 + 16 * ct + acc_col();
-                    p.dh0[sh + (size_t)d * D + c] = st[i][ct][e];
+                    fin[sh + (size_t)d * D + c] = st[i][ct][e];
                 }
     }
 }
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the D/BV
     // tiles of one (direction, sequence, head) land on the same XCD and share
     // the chunk operands (w, k~, q~, do) through its L2.
-    const int ngroups = 2 * p.N * p.H;
+    const int ngroups = p.dirs * p.N * p.H;   // dirs = 1: forward only
     const int vt = blockIdx.x / ngroups;
     int bid = blockIdx.x % ngroups;
     const int h = bid % p.H; bid /= p.H;

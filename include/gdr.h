@@ -141,6 +141,26 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d,
                         void* const* stage_events);
 
 /*
+ * The forward pass of the same recurrence: o_t = scale S_t^T q_t for every
+ * token and the final state S_T of every sequence, in the chunk form
+ *   o_c = scale [(q 2^G) h_c + Aqk X_c],   X_c = u_c - w_c h_c,
+ * h_{c+1} = Diag(2^G_last) h_c + (k 2^(G_last - G))^T X_c
+ * (the WY recompute on the FlashQLA page's fused_bwd.py; the kda chain of the
+ * kernel-fun page opens with its forward stage). Inputs q, k, v, g, beta, h0,
+ * cu_seqlens: as for gdr_bwd. Outputs (device, fully overwritten):
+ *   o           [B,T,H,V]  io_dtype
+ *   ht          [N,H,K,V]  fp32 final states; NULL = not written
+ * workspace:    as for gdr_bwd (gdr_bwd_workspace_bytes(d) bytes); the pass
+ *               leaves the per-chunk states h_c in it (region 12).
+ * Same descriptor, alignment, ownership and error codes as gdr_bwd.
+ */
+int gdr_fwd(const gdr_bwd_desc_t* d,
+            const void* q, const void* k, const void* v, const float* g,
+            const void* beta, const float* h0, const int32_t* cu_seqlens,
+            void* o, float* ht,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Byte offsets of the workspace regions for descriptor d, in this order:
  *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A, 4 A^T,
  *   5 w, 6 w^T, 7 k~, 8 k~^T, 9 u^T, 10 scale*q~^T, 11 2^G_last,

@@ -107,3 +107,22 @@ def test_bwd_argument_errors_before_any_launch(lib):
     dvl = desc(B=1, T=1000, n_seqs=4)
     assert _call(lib, dvl, None, big, gdr.workspace_bytes(dvl)) == -1  # varlen without cu_seqlens
     assert _call(lib, d, {"cu": ctypes.c_void_p(0x200000)}, big, need) == -1  # cu without varlen
+
+
+def test_fwd_argument_errors(lib):
+    """gdr_fwd rejects bad arguments before touching the GPU."""
+    d = desc()
+    P = ctypes.c_void_p
+    ptrs = [P(0x100000 * (i + 1)) for i in range(6)]   # q, k, v, g, beta, o
+    ws = P(0x1000000)
+    n = lib.gdr_bwd_workspace_bytes(ctypes.byref(d))
+    def call(q=ptrs[0], o=ptrs[5], wsp=ws, wsb=n, cu=None, dd=d):
+        return lib.gdr_fwd(ctypes.byref(dd), q, ptrs[1], ptrs[2], ptrs[3], ptrs[4], None, cu, o, None,
+                           wsp, ctypes.c_size_t(wsb), None)
+    assert call(q=None) == -1                      # required input missing
+    assert call(o=None) == -1                      # output missing
+    assert call(q=P(0x100001)) == -1               # misaligned
+    assert call(wsb=n - 1) == -3                   # workspace too small
+    assert call(wsp=None) == -3
+    assert call(cu=P(0x2000000)) == -1             # cu_seqlens without n_seqs
+    assert call(dd=desc(K=96, V=96)) == -2         # unsupported
