@@ -27,11 +27,15 @@ namespace gdr {
 
 // ---------------------------------------------------------------------------
 // Chunk table: one workgroup. seq_off[n] = first global chunk of sequence n,
-// ctab[j] = {first token, length, sequence}. Fixed length: B sequences of T.
+// ctab[j] = {first token, length, sequence, chunk index in the sequence}.
+// Fixed length: B sequences of T. Sequences are taken 256 at a time: a scan
+// of their chunk counts gives their first chunks, then every thread writes
+// entries of the block's chunks, finding each chunk's sequence by binary
+// search over the scan (so a long sequence is not written by one thread).
 // ---------------------------------------------------------------------------
 template <int C>
 __global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
-    __shared__ int s_scan[256];
+    __shared__ int s_scan[256], s_tok[256], s_len[256];
     __shared__ int s_base;
     const int tid = threadIdx.x;
     if (tid == 0) s_base = 0;
@@ -50,6 +54,8 @@ __global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
         }
         const int nch = (len + C - 1) / C;
         s_scan[tid] = nch;
+        s_tok[tid] = tok0;
+        s_len[tid] = len;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
             int v = tid >= off ? s_scan[tid - off] : 0;
@@ -57,20 +63,25 @@ __global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
             s_scan[tid] += v;
             __syncthreads();
         }
-        const int first = s_base + s_scan[tid] - nch;
-        if (n < p.N) {
-            p.seq_off[n] = first;
-            for (int c = 0; c < nch && first + c < p.nc_max; ++c) {
-                ChunkEntry e;
-                e.tok0 = tok0 + c * C;
-                e.len = min(C, len - c * C);
-                e.seq = n;
-                e.pad_ = c;
-                p.ctab[first + c] = e;
+        const int base = s_base, tot = s_scan[255];
+        if (n < p.N) p.seq_off[n] = min(base + s_scan[tid] - nch, p.nc_max);
+        for (int c = tid; c < tot && base + c < p.nc_max; c += 256) {
+            int lo = 0, hi = 255;   // first i with s_scan[i] > c
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_scan[mid] > c) hi = mid;
+                else lo = mid + 1;
             }
+            const int cc = c - (lo ? s_scan[lo - 1] : 0);   // chunk index within sequence n0 + lo
+            ChunkEntry e;
+            e.tok0 = s_tok[lo] + cc * C;
+            e.len = min(C, s_len[lo] - cc * C);
+            e.seq = n0 + lo;
+            e.pad_ = cc;
+            p.ctab[base + c] = e;
         }
         __syncthreads();
-        if (tid == 255) s_base += s_scan[255];
+        if (tid == 0) s_base = base + tot;
         __syncthreads();
     }
     if (tid == 0) p.seq_off[p.N] = min(s_base, p.nc_max);
@@ -198,11 +209,13 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         }
         bpre = to_f32(beta[(size_t)(e2.tok0 + min(tid, e2.len - 1)) * p.H + hh]);
     };
+    // v pieces go token-fastest (one 16-byte piece per token row and lane), so
+    // that their transposed LDS writes in the u product hit distinct banks
     auto load_v = [&](const int it, const ChunkEntry& e2) __attribute__((always_inline)) {
         const int hh = it % p.H;
 #pragma unroll
         for (int i = 0; i < NQP; ++i) {
-            const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8, rt = min(r, e2.len - 1);
+            const int e = tid + i * NT, r = e % C, d0 = (e / C) * V8, rt = min(r, e2.len - 1);
             vpre[i] = ld16(v + ((size_t)(e2.tok0 + rt) * p.H + hh) * D + d0);
         }
     };
@@ -444,7 +457,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     float av[8], qv[8];   // this thread's piece of A and Aqk (at most one: C <= 64)
     static_assert(C * (C / 8) <= NT, "one piece of a C x C matrix per thread");
     const bool has_piece = tid < C * (C / 8);
-    const int pr5 = tid / (C / 8), ps5 = (tid % (C / 8)) * 8;
+    const int pr5 = tid % C, ps5 = (tid / C) * 8;   // row fastest: transposed reads conflict-free
     if (has_piece) {
         T* gA = static_cast<T*>(p.Am) + jh * C * C;
         T* gAT = static_cast<T*>(p.AT) + jh * C * C;
@@ -471,7 +484,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^): 8 consecutive s per item
     T* khT = Xb;  // [D][LC]
     for (int e = tid; e < D * (C / 8); e += NT) {
-        const int d = e / (C / 8), s0 = (e % (C / 8)) * 8;
+        const int d = e % D, s0 = (e / D) * 8;   // d fastest: row reads and 16-byte column writes without bank conflicts
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             store8<T>(gwT + d * C + s0, x);
         }
         for (int e = tid; e < C * (D / 8); e += NT) {
-            const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            const int r = e % C, d0 = (e / C) * 8;   // r fastest: the transposed reads conflict-free
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = to_f32(wTL[(d0 + i) * LC + r]);
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     T* vhT = Xb;  // [D][LC]
 #pragma unroll
     for (int i5 = 0; i5 < NQP; ++i5) {
-        const int e = tid + i5 * NT, s2 = e / (D / V8), d0 = (e % (D / V8)) * V8;
+        const int e = tid + i5 * NT, s2 = e % C, d0 = (e / C) * V8;   // as loaded: token fastest
         const Vec16 vv = s2 < len ? vpre[i5] : Vec16{};
         const T* vp = reinterpret_cast<const T*>(&vv);
 #pragma unroll
@@ -572,7 +585,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             store8<T>(gkt + r * D + d0, x);
         }
         for (int e = tid; e < D * (C / 8); e += NT) {
-            const int d = e / (C / 8), r0b = (e % (C / 8)) * 8;
+            const int d = e % D, r0b = (e / D) * 8;   // d fastest (bank-conflict free)
             const float gl = Gs[(C - 1) * LF + d];
             float x[8];
 #pragma unroll
