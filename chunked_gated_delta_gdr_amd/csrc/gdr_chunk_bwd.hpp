@@ -60,7 +60,8 @@ struct BwdLds {
     static constexpr size_t GL_OFF = DGR_OFF + 2 * C * 4;                    // f32 [D] dG_last
     static constexpr size_t GLW_OFF = GL_OFF + D * 4;                        // f32 [NB][D] per-wave dG_last
     static constexpr size_t BT_OFF = GLW_OFF + size_t(NB) * D * 4;           // f32 [NB][D] block totals
-    static constexpr size_t U_OFF = BT_OFF + size_t(NB) * D * 4;             // union region
+    static constexpr size_t AM_OFF = BT_OFF + size_t(NB) * D * 4;            // T [C][LC] A of the head
+    static constexpr size_t U_OFF = AM_OFF + sz(C, LC, sizeof(T));           // union region
     // phase 1 (state products, one V slice)
     static constexpr size_t P1_DOT = 0;                                      // T [BVS][LC]
     static constexpr size_t P1_XL = P1_DOT + sz(BVS, LC, sizeof(T));         // T [C][LB]
@@ -183,23 +184,16 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     const T* dout = static_cast<const T*>(p.dout);
     const T* beta = static_cast<const T*>(p.beta);
 
-    // q, k rows of this chunk (all requested first; zero past the sequence end)
-    {
-        constexpr int NQP = C * (D / V8) / NT;
-        static_assert(NQP * NT == C * (D / V8), "piece split");
-        Vec16 qv[NQP], kv[NQP];
+    // q, k rows of this chunk, requested first (zero past the sequence end);
+    // they reach LDS in the first head, after that head's own requests
+    constexpr int NQP = C * (D / V8) / NT;
+    static_assert(NQP * NT == C * (D / V8), "piece split");
+    Vec16 qv[NQP], kv[NQP];
 #pragma unroll
-        for (int i = 0; i < NQP; ++i) {
-            const int e = tid + i * NT, r = min(e / (D / V8), len - 1), d0 = (e % (D / V8)) * V8;
-            qv[i] = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-            kv[i] = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-        }
-#pragma unroll
-        for (int i = 0; i < NQP; ++i) {
-            const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8;
-            st16(qL0 + r * LT + d0, r < len ? qv[i] : Vec16{});
-            st16(kL0 + r * LT + d0, r < len ? kv[i] : Vec16{});
-        }
+    for (int i = 0; i < NQP; ++i) {
+        const int e = tid + i * NT, r = min(e / (D / V8), len - 1), d0 = (e % (D / V8)) * V8;
+        qv[i] = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
+        kv[i] = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
     }
 
     // GROUPED: fp32 group sums of dq, dk in this wave's accumulator tiles
@@ -213,7 +207,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     // a loop around this body lets the compiler hoist the (lane-dependent)
     // address arithmetic of every unrolled LDS access out of it and keep it
     // live across iterations, which costs hundreds of registers.
-    auto head = [&](const int gi) __attribute__((always_inline)) {
+    auto head = [&](const int gi, const bool first) __attribute__((always_inline)) {
         const int l = opaque_lane_id();  // fresh per head: see above
         char* U = U0;
         T* qL = qL0;
@@ -231,7 +225,17 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         const long ldo = (long)p.H * D;
 
         __syncthreads();  // previous head's LDS use is over
-        for (int r = tid; r < C; r += NT) bs[r] = r < len ? to_f32(beta[(size_t)(tok0 + r) * p.H + h]) : 0.f;
+        // The head's small inputs are requested together with its first slice
+        // (below), so that one wait covers them all: beta, 2^G_last, A (staged
+        // in LDS for dA A^T); each thread holds at most a few values.
+        constexpr int NAM = (C * (C / V8) + NT - 1) / NT;
+        const float pbeta = to_f32(beta[(size_t)(tok0 + min(tid, len - 1)) * p.H + h]);
+        Vec16 pam[NAM];
+#pragma unroll
+        for (int i = 0; i < NAM; ++i) {
+            const int e = min(tid + NT * i, C * (C / V8) - 1);
+            pam[i] = ld16(Am + (size_t)e * V8);
+        }
 
         // ================= phase 1: state products over V slices =================
         // The slice pieces (rows of do, v, X, T and of h, dh') are loaded one
@@ -291,9 +295,36 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             }
         };
         load_slice(0);
+        float pgl[NPD];   // 2^G_last of the row this thread closes in dG_last
+#pragma unroll
+        for (int i = 0; i < NPD; ++i) pgl[i] = p.glast[jh * D + min((tid + NT * i) / PR, D - 1)];
+        if (first) {
+#pragma unroll
+            for (int i = 0; i < NQP; ++i) {
+                const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8;
+                st16(qL0 + r * LT + d0, r < len ? qv[i] : Vec16{});
+                st16(kL0 + r * LT + d0, r < len ? kv[i] : Vec16{});
+            }
+        }
+        // gate rows of the cumsum in 2a (one column, SR rows per thread), requested
+        // in the last slice in place of a slice load; rows past the end zeroed at use
+        constexpr int NSEG = NT / D, SR = C / NSEG;
+        static_assert(NT % D == 0 && C % NSEG == 0, "cumsum segments");
+        const int gd = tid % D, gsg = tid / D, grs0 = gsg * SR;
+        float gpre[SR];
 
+#pragma unroll
         for (int v0 = 0; v0 < D; v0 += BVS) {
             __syncthreads();  // the previous slice's LDS reads are over
+            if (v0 == 0) {
+                if (tid < C) bs[tid] = tid < len ? pbeta : 0.f;
+                T* AmL = reinterpret_cast<T*>(smem + L::AM_OFF);
+#pragma unroll
+                for (int i = 0; i < NAM; ++i) {
+                    const int e = min(tid + NT * i, C * (C / V8) - 1);
+                    st16(AmL + (e / (C / V8)) * LC + (e % (C / V8)) * V8, pam[i]);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < NPC; ++i) {
                 const int e = tid + NT * i;
@@ -325,7 +356,16 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     hdh[i] += s2;
                 }
             }
-            load_slice(min(v0 + BVS, D - BVS));  // next slice (the last one again at the end)
+            if (v0 + BVS < D) {
+                load_slice(v0 + BVS);   // next slice
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < SR; ++jj) {
+                    const int rt = min(grs0 + jj, len - 1);
+                    if constexpr (SCALAR) gpre[jj] = p.g[(size_t)(tok0 + rt) * p.H + h];
+                    else gpre[jj] = p.g[((size_t)(tok0 + rt) * p.H + h) * D + gd];
+                }
+            }
             __syncthreads();
             // dX = T + scale Aqk^T do  (own rows, own half of the slice)
             f32x4 dX[NTV];
@@ -386,7 +426,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
 #pragma unroll
             for (int m = 1; m < PR; m <<= 1) x += __shfl_xor(x, m);
             const int e = tid + NT * i;
-            if (e < D * PR && e % PR == 0) dGl[e / PR] = kLn2 * p.glast[jh * D + e / PR] * x;
+            if (e < D * PR && e % PR == 0) dGl[e / PR] = kLn2 * pgl[i] * x;
         }
         __syncthreads();  // phase-1 LDS is dead from here; dv is staged
 
@@ -404,21 +444,13 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         float* Gs = reinterpret_cast<float*>(U + L::P2_GS);
         T* kgL = reinterpret_cast<T*>(U + L::P2_KG);
         {
-            constexpr int NSEG = NT / D, SR = C / NSEG;
-            static_assert(NT % D == 0 && C % NSEG == 0, "cumsum segments");
             float* segt = reinterpret_cast<float*>(U + L::P2_SEG);
-            const int d = tid % D, sg = tid / D, rs0 = sg * SR;
+            const int d = gd, sg = gsg, rs0 = grs0;
             float gl[SR];
             float run = 0.f;
 #pragma unroll
             for (int jj = 0; jj < SR; ++jj) {
-                const int r = rs0 + jj;
-                float gv = 0.f;
-                if (r < len) {
-                    if constexpr (SCALAR) gv = p.g[(size_t)(tok0 + r) * p.H + h];
-                    else gv = p.g[((size_t)(tok0 + r) * p.H + h) * D + d];
-                }
-                run += gv;
+                run += rs0 + jj < len ? gpre[jj] : 0.f;
                 gl[jj] = run;
             }
             segt[sg * D + d] = run;
@@ -501,7 +533,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             f32x4 t1[NTC];
 #pragma unroll
             for (int t = 0; t < NTC; ++t) t1[t] = zero4();
-            panel_mma<T, NTC, C>(t1, dAL, LC, r0, Am, C, cc0, l);
+            panel_mma<T, NTC, C>(t1, dAL, LC, r0, reinterpret_cast<const T*>(smem + L::AM_OFF), LC, cc0, l);
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
                 const int c = cc0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
@@ -848,10 +880,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             if constexpr (SCALAR) p.dg[(size_t)(tok0 + tid) * p.H + h] = dgR[tid] + dgR[C + tid];
         }
     };
+    head(0, true);
     if constexpr (GROUPED) {
-        for (int gi = 0; gi < p.G; ++gi) head(gi);
-    } else {
-        head(0);
+        for (int gi = 1; gi < p.G; ++gi) head(gi, false);
     }
     if constexpr (GROUPED) {
         // dq, dk group sums: staged in LDS, stored row-contiguous

@@ -195,19 +195,21 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 for (int e = 0; e < 4; ++e) o[e] = DIR == 0 ? to_f32(cur.u[i][jj][e]) - acc[e] : -acc[e];
                 store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
             }
-        {   // the incoming state to the workspace, row-major: 8 columns per piece
+        {   // the incoming state to the workspace, row-major: 8 columns per piece.
+            // Stores are never behind a branch (spare threads repeat a piece with
+            // the same data): a store on one path only would make the compiler's
+            // memory-counter waits for the prefetched loads also wait for it.
+            constexpr int NP = D * BV / V8;
             T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D + (size_t)v0 * D;  // this V tile
 #pragma unroll
-            for (int pi = 0; pi < (D * BV / V8 + 255) / 256; ++pi) {
-                const int e = threadIdx.x + 256 * pi;
-                if (e < D * BV / V8) {
-                    const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
-                    Vec16 v;
-                    T* vp = reinterpret_cast<T*>(&v);
+            for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
+                const int e = (int)(threadIdx.x + 256 * pi) % NP;
+                const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                Vec16 v;
+                T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
-                    for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
-                    st16(gS + (size_t)d * BV + c, v);
-                }
+                for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
+                st16(gS + (size_t)d * BV + c, v);
             }
         }
         __syncthreads();
@@ -231,21 +233,21 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 }
             }
         {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
+            // (unconditional stores, as above)
+            constexpr int NP = C * BV / V8;
             T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D + (size_t)v0 * C;  // this V tile
 #pragma unroll
-            for (int pi = 0; pi < (C * BV / V8 + 255) / 256; ++pi) {
-                const int e = threadIdx.x + 256 * pi;
-                if (e < C * BV / V8) {
-                    const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
-                    Vec16 v;
-                    T* vp = reinterpret_cast<T*>(&v);
+            for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
+                const int e = (int)(threadIdx.x + 256 * pi) % NP;
+                const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                Vec16 v;
+                T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
-                    for (int q = 0; q < V8; ++q) {
-                        const T x = sX[(c + q) * LX + r];
-                        vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
-                    }
-                    st16(gX + (size_t)r * BV + c, v);
+                for (int q = 0; q < V8; ++q) {
+                    const T x = sX[(c + q) * LX + r];
+                    vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
                 }
+                st16(gX + (size_t)r * BV + c, v);
             }
         }
     };
