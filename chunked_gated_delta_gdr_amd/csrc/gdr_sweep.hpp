@@ -108,7 +108,7 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
 
 // One direction of the sweep for (sequence n, value head h, V tile at v0).
 template <typename T, int C, int D, int BV, int DIR, int NPF>
-__device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS, T* sX0, T* sX1, T* sDo0,
+__device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS0, T* sS1, T* sX0, T* sX1, T* sDo0,
                                           T* sDo1) {
     using S = SweepTiles<T, C, D, BV>;
     using Ops = SweepOps<T, C, D, BV, DIR>;
@@ -147,6 +147,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
     auto step = [&](const Ops& cur, const int k) __attribute__((always_inline)) {
         const int it = chunk_it(k);
         const size_t jh = (size_t)(c0 + it) * p.H + h;
+        T* sS = (k & 1) ? sS1 : sS0;
         T* sX = (k & 1) ? sX1 : sX0;
         T* sDo = (k & 1) ? sDo1 : sDo0;
 
@@ -179,23 +180,78 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
         __syncthreads();
 
         // 2. chunk-row product: X = u - w h (fwd) or T = k~ dh (rev); forward
-        //    keeps +X, reverse keeps -T so the state update is a pure sum
+        //    keeps +X, reverse keeps -T so the state update is a pure sum. All
+        //    B fragments are read before the first product (the scheduling
+        //    barrier keeps the compiler from sinking each read to its use, which
+        //    would expose one LDS round trip per MFMA).
+        {
+            typename Mfma<T>::frag bx[S::XCT][D / KS];
 #pragma unroll
-        for (int i = 0; i < S::XRT; ++i)
+            for (int jj = 0; jj < S::XCT; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < S::XCT; ++jj) {
-                const int ct = S::xcol(w, jj);
-                f32x4 acc = zero4();
+                for (int k2 = 0; k2 < D / KS; ++k2) bx[jj][k2] = frag_kc(sS, LS, 16 * S::xcol(w, jj), k2 * KS);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < S::XRT; ++i) {
+                f32x4 acc[S::XCT];
+#pragma unroll
+                for (int jj = 0; jj < S::XCT; ++jj) acc[jj] = zero4();
 #pragma unroll
                 for (int k2 = 0; k2 < D / KS; ++k2)
-                    acc = Mfma<T>::mma(cur.a1[i][k2], frag_kc(sS, LS, 16 * ct, k2 * KS), acc);
-                const int r = 16 * S::xrow(w, i) + acc_row(0), c = 16 * ct + acc_col();
-                float o[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = DIR == 0 ? to_f32(cur.u[i][jj][e]) - acc[e] : -acc[e];
-                store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
+                    for (int jj = 0; jj < S::XCT; ++jj) acc[jj] = Mfma<T>::mma(cur.a1[i][k2], bx[jj][k2], acc[jj]);
+#pragma unroll
+                for (int jj = 0; jj < S::XCT; ++jj) {
+                    const int r = 16 * S::xrow(w, i) + acc_row(0), c = 16 * S::xcol(w, jj) + acc_col();
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = DIR == 0 ? to_f32(cur.u[i][jj][e]) - acc[jj][e] : -acc[jj][e];
+                    store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
+                }
             }
-        {   // the incoming state to the workspace, row-major: 8 columns per piece.
+        }
+        __syncthreads();
+
+        // 3. state update: st = Diag(2^G_last) st + A2 X (+ (scale q~)^T do for reverse).
+        //    State, X / T and do^T are double-buffered: the next chunk writes the
+        //    other buffers, and this chunk's buffers are rewritten only after
+        //    the next chunk's barriers, which every wave reaches after its
+        //    copy-outs below, so no third barrier is needed.
+        {   // B fragments first (as in 2), then the SRW x SCT chains interleaved
+            typename Mfma<T>::frag bxs[SCT][C / KS], bdo[DIR == 1 ? SCT : 1][C / KS];
+#pragma unroll
+            for (int ct = 0; ct < SCT; ++ct)
+#pragma unroll
+                for (int k2 = 0; k2 < C / KS; ++k2) {
+                    bxs[ct][k2] = frag_kc(sX, LX, 16 * ct, k2 * KS);
+                    if constexpr (DIR == 1) bdo[ct][k2] = frag_kc(sDo, LX, 16 * ct, k2 * KS);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < S::SRW; ++i)
+#pragma unroll
+                for (int ct = 0; ct < SCT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st[i][ct][e] *= cur.gl[i][e];
+#pragma unroll
+            for (int k2 = 0; k2 < C / KS; ++k2)
+#pragma unroll
+                for (int i = 0; i < S::SRW; ++i)
+#pragma unroll
+                    for (int ct = 0; ct < SCT; ++ct)
+                        st[i][ct] = Mfma<T>::mma(cur.a2[i][k2], bxs[ct][k2], st[i][ct]);
+            if constexpr (DIR == 1) {
+#pragma unroll
+                for (int k2 = 0; k2 < C / KS; ++k2)
+#pragma unroll
+                    for (int i = 0; i < S::SRW; ++i)
+#pragma unroll
+                        for (int ct = 0; ct < SCT; ++ct)
+                            st[i][ct] = Mfma<T>::mma(cur.a3[i][k2], bdo[ct][k2], st[i][ct]);
+            }
+        }
+        {   // the incoming state to the workspace, row-major: 8 columns per piece,
+            // read back from its LDS buffer while the update's MFMAs run.
             // Stores are never behind a branch (spare threads repeat a piece with
             // the same data): a store on one path only would make the compiler's
             // memory-counter waits for the prefetched loads also wait for it.
@@ -212,26 +268,6 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 st16(gS + (size_t)d * BV + c, v);
             }
         }
-        __syncthreads();
-
-        // 3. state update: st = Diag(2^G_last) st + A2 X (+ (scale q~)^T do for reverse).
-        //    The next chunk's step 1 rewrites sS (read only before the last barrier)
-        //    and the other buffer of sX / sDo, so no third barrier is needed.
-#pragma unroll
-        for (int i = 0; i < S::SRW; ++i)
-#pragma unroll
-            for (int ct = 0; ct < SCT; ++ct) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st[i][ct][e] *= cur.gl[i][e];
-#pragma unroll
-                for (int k2 = 0; k2 < C / KS; ++k2)
-                    st[i][ct] = Mfma<T>::mma(cur.a2[i][k2], frag_kc(sX, LX, 16 * ct, k2 * KS), st[i][ct]);
-                if constexpr (DIR == 1) {
-#pragma unroll
-                    for (int k2 = 0; k2 < C / KS; ++k2)
-                        st[i][ct] = Mfma<T>::mma(cur.a3[i][k2], frag_kc(sDo, LX, 16 * ct, k2 * KS), st[i][ct]);
-                }
-            }
         {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
             // (unconditional stores, as above)
             constexpr int NP = C * BV / V8;
@@ -291,7 +327,7 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     constexpr int LX = C + pad<T>();
     constexpr int NPF = 3;                           // chunks of operands in flight
     static_assert(BV == kTileV, "the stored states are tiled by the sweep's V tile");
-    __shared__ __attribute__((aligned(16))) T sS[BV * LS];
+    __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
     __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
 
@@ -305,8 +341,8 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     const int h = bid % p.H; bid /= p.H;
     const int n = bid % p.N;
     const int dir = bid / p.N;
-    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS, sX[0], sX[1], sDo[0], sDo[1]);
-    else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS, sX[0], sX[1], sDo[0], sDo[1]);
+    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1]);
+    else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1]);
 }
 
 }  // namespace gdr
