@@ -263,6 +263,53 @@ def bench_fwd(args, w, inp, t, tokens, n_chunks, n_seqs, ws) -> int:
     return 0
 
 
+def bench_train(args, w, inp, t, tokens, n_chunks, n_seqs, ws) -> int:
+    """A training step's kernels: the forward pass, then the backward after it
+    on the same workspace (gdr_bwd_after_fwd). Times each half and the pair
+    with HIP events on the launch stream."""
+    import torch
+    import chunked_gated_delta_gdr_amd as gdr
+    dev = t["q"].device
+    o = torch.empty_like(t["v"])
+    ht = torch.empty((n_seqs, w.H, w.K, w.V), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"]),
+             torch.empty_like(t["g"]), torch.empty_like(t["beta"]),
+             torch.empty((n_seqs, w.H, w.K, w.V), dtype=torch.float32, device=dev))
+    common = dict(cu_seqlens=t["cu_seqlens"], scale=inp["scale"], chunk_size=w.chunk)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        gdr.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], h0=t["h0"], workspace=ws, out=(o, ht), **common)
+        if e: e[1].record(stream)
+        gdr.bwd_after_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], ws, dht=t["dht"], out=grads,
+                          **common)
+        if e: e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for e in ev:
+        step(e)
+    torch.cuda.synchronize()
+    f = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    b = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    res = {
+        "metric": "gated-delta-rule fwd + bwd-after-fwd tokens/s (B*T) at H=16,K=V=128",
+        "value": tokens / ((f + b) * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": f + b, "fwd_ms": f, "bwd_after_fwd_ms": b,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[w.io_dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "train", "tokens": tokens, "H": w.H, "Hg": w.Hg, "K": w.K,
+                   "V": w.V, "chunk": w.chunk, "gate": w.gate, "n_seqs": n_seqs,
+                   "parallelism": "single-gpu"},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,8 +317,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="kda_fixed_h16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("bwd", "fwd"), default="bwd",
-                    help="bwd (the headline) or fwd (the forward pass: o and final states)")
+    ap.add_argument("--pass", dest="which", choices=("bwd", "fwd", "train"), default="bwd",
+                    help="bwd (the headline), fwd (the forward pass: o and final states) or "
+                         "train (the forward pass, then the backward after it on its workspace)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after the timed steps, run a plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -316,6 +364,8 @@ def main() -> int:
 
     if args.which == "fwd":
         return bench_fwd(args, w, inp, t, tokens, n_chunks, n_seqs, ws)
+    if args.which == "train":
+        return bench_train(args, w, inp, t, tokens, n_chunks, n_seqs, ws)
 
     def step(events=None):
         gdr.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], h0=t["h0"], dht=t["dht"],

@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["bwd", "fwd", "workspace_bytes", "workspace_offsets", "library_path", "Desc",
+__all__ = ["bwd", "bwd_after_fwd", "fwd", "workspace_bytes", "workspace_offsets", "library_path", "Desc",
            "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +65,8 @@ def _load():
                                                               ctypes.POINTER(ctypes.c_void_p)]
         lib.gdr_fwd.restype = ctypes.c_int
         lib.gdr_fwd.argtypes = [D] + [P] * 9 + [P, ctypes.c_size_t, P]
+        lib.gdr_bwd_after_fwd.restype = ctypes.c_int
+        lib.gdr_bwd_after_fwd.argtypes = [D] + [P] * 14 + [P, ctypes.c_size_t, P]
         lib.gdr_strerror.restype = ctypes.c_char_p
         lib.gdr_strerror.argtypes = [ctypes.c_int]
         lib.gdr_version.restype = ctypes.c_char_p
@@ -126,7 +128,7 @@ STAGES = ("chunk_table", "prep", "sweep", "chunk_bwd")
 
 def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
         chunk_size: int = 64, workspace: Optional[torch.Tensor] = None, out=None,
-        stage_events=None):
+        stage_events=None, after_fwd: bool = False):
     """Backward of the gated delta rule (see include/gdr.h for the definition).
 
     q, k [B,T,Hg,K]; v, do [B,T,H,V]; beta [B,T,H] (all in one io dtype:
@@ -137,7 +139,8 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
     workspace_bytes) may be passed to avoid an allocation per call; ``out``
     may hold preallocated outputs in the same order. ``stage_events``: five
     torch.cuda.Event(enable_timing=True), already recorded once, recorded at
-    the kernel boundaries (see gdr_bwd_with_events).
+    the kernel boundaries (see gdr_bwd_with_events). ``after_fwd``: see
+    :func:`bwd_after_fwd`.
     """
     lib = _load()
     io = q.dtype
@@ -162,6 +165,8 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
         _need(h0, "h0", torch.float32, (N, H, K, V))
     if dht is not None:
         _need(dht, "dht", torch.float32, (N, H, K, V))
+    if after_fwd and (h0 is not None or workspace is None or stage_events is not None):
+        raise ValueError("after_fwd: pass the forward's workspace, and no h0 or stage_events")
     desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
                      io_dtype=io, scale=float(scale) if scale is not None else 0.0)
     rc = check(desc)
@@ -186,7 +191,9 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
             _ptr(h0), _ptr(do), _ptr(dht), _ptr(cu_seqlens),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0),
             _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
-    if stage_events is None:
+    if after_fwd:
+        rc = lib.gdr_bwd_after_fwd(*(args[:6] + args[7:]))   # no h0
+    elif stage_events is None:
         rc = lib.gdr_bwd(*args)
     else:
         if len(stage_events) != 5 or any(e.cuda_event == 0 for e in stage_events):
@@ -196,6 +203,19 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
     if rc != 0:
         raise _err(rc)
     return dq, dk, dv, dg, db, dh0
+
+
+def bwd_after_fwd(q, k, v, g, beta, do, workspace: torch.Tensor, dht=None, cu_seqlens=None,
+                  scale=None, chunk_size: int = 64, out=None):
+    """Backward after :func:`fwd`, from the per-chunk states it saved.
+
+    ``workspace`` must be the one a :func:`fwd` call filled, with the same
+    q, k, v, g, beta, h0, cu_seqlens, scale and chunk size, unchanged since
+    (gdr_bwd_after_fwd in include/gdr.h): only the reverse sweep and the
+    gradient kernel run. Returns what :func:`bwd` returns for those inputs.
+    """
+    return bwd(q, k, v, g, beta, do, dht=dht, cu_seqlens=cu_seqlens, scale=scale,
+               chunk_size=chunk_size, workspace=workspace, out=out, after_fwd=True)
 
 
 def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk_size: int = 64,

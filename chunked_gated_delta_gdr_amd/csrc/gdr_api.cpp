@@ -162,6 +162,7 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d, const void* q, const void* k, c
     rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
     if (rc != GDR_OK) return rc;
     p.dirs = 2;
+    p.dir0 = 0;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = do_; p.dht = dht;
     p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
     return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 0), p,
@@ -181,9 +182,31 @@ int gdr_fwd(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v
     rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
     if (rc != GDR_OK) return rc;
     p.dirs = 1;
+    p.dir0 = 0;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
     p.o = o; p.ht = ht;
     return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 1), p,
+                  stream, nullptr);
+}
+
+int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v,
+                      const float* g, const void* beta, const void* do_, const float* dht,
+                      const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float* dg, void* db,
+                      float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = gdr_bwd_check(d);
+    if (rc != GDR_OK) return rc;
+    const void* req[] = {q, k, v, g, beta, do_, dq, dk, dv, dg, db, dh0};
+    for (const void* ptr : req)
+        if (!ptr || !aligned16(ptr)) return GDR_EINVAL;
+    if (dht && !aligned16(dht)) return GDR_EINVAL;
+    gdr::Params p;
+    rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
+    if (rc != GDR_OK) return rc;
+    p.dirs = 1;
+    p.dir0 = 1;   // reverse sweep only: the forward's table, factors, h and X are in the workspace
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.dout = do_; p.dht = dht;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
+    return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 0), p,
                   stream, nullptr);
 }
 

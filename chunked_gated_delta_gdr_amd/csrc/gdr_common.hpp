@@ -284,7 +284,10 @@ struct Params {
     int N;               // sequences
     int nc_max;          // chunk-table capacity (grid size of chunk-parallel kernels)
     int varlen;
-    int dirs;            // state sweeps run: 1 = forward only (the forward pass), 2 = both
+    int dirs;            // state sweeps run: 1 = one direction, 2 = both
+    int dir0;            // first direction: 0 = forward (forward pass, or both for the
+                         // backward); 1 = reverse only (a backward after the forward
+                         // pass, whose table, factors, h and X are in the workspace)
     float scale;
     // inputs
     const void* q; const void* k; const void* v; const float* g; const void* beta;

@@ -26,8 +26,12 @@ inline int compute_units() {
     return cached[dev];
 }
 
-// Chunk table, per-chunk preparation and the state sweep(s) (p.dirs of them):
-// the start of both passes. ev as above (entries 0..3).
+// Chunk table, per-chunk preparation and the state sweep(s) (p.dirs of them,
+// from direction p.dir0): the start of both passes. A backward after the
+// forward pass (p.dir0 == 1) finds the factors, h and X in the workspace and
+// runs the reverse sweep only; it rebuilds the chunk table all the same, so
+// that every index the kernels use comes from cu_seqlens and the shapes, not
+// from workspace contents. ev as above (entries 0..3).
 template <typename T, int C, int D, bool SCALAR>
 hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
@@ -35,7 +39,7 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     // chunk table (device-side, so varlen needs no host sync)
     gdr_chunk_table<C><<<dim3(1), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(1);
-    if (p.nc_max > 0) {
+    if (p.dir0 == 0 && p.nc_max > 0) {
         // persistent: at most one workgroup per compute unit (its LDS allows no more)
         const int items = p.nc_max * p.H;
         gdr_prep<T, C, D, SCALAR><<<dim3(items < compute_units() ? items : compute_units()),
@@ -47,7 +51,8 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     return e;
 }
 
-// The backward pass (p.dirs == 2): four kernels.
+// The backward pass: four kernels (p.dirs == 2), or the reverse sweep and the
+// gradient kernel after the forward pass (p.dir0 == 1, p.dirs == 1).
 template <typename T, int C, int D, bool SCALAR>
 hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
     hipError_t e = launch_front<T, C, D, SCALAR>(p, stream, ev);

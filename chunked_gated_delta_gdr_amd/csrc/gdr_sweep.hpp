@@ -335,12 +335,12 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the D/BV
     // tiles of one (direction, sequence, head) land on the same XCD and share
     // the chunk operands (w, k~, q~, do) through its L2.
-    const int ngroups = p.dirs * p.N * p.H;   // dirs = 1: forward only
+    const int ngroups = p.dirs * p.N * p.H;   // dirs = 1: the direction dir0 only
     const int vt = blockIdx.x / ngroups;
     int bid = blockIdx.x % ngroups;
     const int h = bid % p.H; bid /= p.H;
     const int n = bid % p.N;
-    const int dir = bid / p.N;
+    const int dir = p.dir0 + bid / p.N;
     if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1]);
     else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1]);
 }

@@ -161,6 +161,27 @@ int gdr_fwd(const gdr_bwd_desc_t* d,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The backward pass after gdr_fwd, from the per-chunk states the forward pass
+ * saved (the FlashQLA page's backward takes the forward's per-chunk states and
+ * its A factor as inputs instead of recomputing them). `workspace` must be the
+ * buffer of a gdr_fwd call with the same descriptor and the same q, k, v, g,
+ * beta, h0 and cu_seqlens, unchanged since: it holds that call's chunk table,
+ * WY factors and per-chunk h and X, so this call runs only the chunk table,
+ * the reverse state sweep and the gradient kernel (no preparation or forward
+ * sweep; h0 is not needed again). The results equal gdr_bwd's on the same
+ * inputs. Arguments, outputs, alignment and error codes: as for gdr_bwd
+ * (without h0). A workspace that does not hold such a forward state is not
+ * detected: the outputs are then meaningless, but every access stays within
+ * the given buffers (the chunk table is rebuilt from cu_seqlens and the shapes).
+ */
+int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d,
+                      const void* q, const void* k, const void* v, const float* g,
+                      const void* beta, const void* do_, const float* dht,
+                      const int32_t* cu_seqlens,
+                      void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Byte offsets of the workspace regions for descriptor d, in this order:
  *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A, 4 A^T,
  *   5 w, 6 w^T, 7 k~, 8 k~^T, 9 u^T, 10 scale*q~^T, 11 2^G_last,

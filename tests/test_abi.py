@@ -126,3 +126,26 @@ def test_fwd_argument_errors(lib):
     assert call(wsp=None) == -3
     assert call(cu=P(0x2000000)) == -1             # cu_seqlens without n_seqs
     assert call(dd=desc(K=96, V=96)) == -2         # unsupported
+
+
+def test_bwd_after_fwd_argument_errors(lib):
+    """gdr_bwd_after_fwd rejects bad arguments before touching the GPU."""
+    d = desc()
+    P = ctypes.c_void_p
+    ptrs = [P(0x100000 * (i + 1)) for i in range(12)]   # q k v g beta do dq dk dv dg db dh0
+    ws = P(0x1000000)
+    n = lib.gdr_bwd_workspace_bytes(ctypes.byref(d))
+    def call(over=None, wsp=ws, wsb=n, cu=None, dd=d):
+        a = list(ptrs)
+        for i, v in (over or {}).items():
+            a[i] = v
+        return lib.gdr_bwd_after_fwd(ctypes.byref(dd), *a[:6], None, cu, *a[6:],
+                                     wsp, ctypes.c_size_t(wsb), None)
+    assert call({0: None}) == -1                   # q missing
+    assert call({11: None}) == -1                  # dh0 missing (always written)
+    assert call({9: P(0x100004)}) == -1            # misaligned dg
+    assert call(wsb=n - 1) == -3                   # workspace too small
+    assert call(wsp=None) == -3
+    assert call(wsp=P(0x1000010)) == -1            # workspace not 256-aligned
+    assert call(cu=P(0x2000000)) == -1             # cu_seqlens without n_seqs
+    assert call(dd=desc(K=96, V=96)) == -2         # unsupported
