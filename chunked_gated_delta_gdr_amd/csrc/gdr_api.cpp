@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "gdr.h"
@@ -52,6 +53,14 @@ void layout(const gdr_bwd_desc_t* d, size_t off[WS_COUNT + 1]) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Required token buffers: non-null and 16-byte aligned, except that with no
+// tokens at all (T == 0) they may be null (no kernel touches them then).
+bool token_buffers_ok(const gdr_bwd_desc_t* d, std::initializer_list<const void*> ptrs) {
+    for (const void* ptr : ptrs)
+        if ((!ptr && d->T > 0) || !aligned16(ptr)) return false;
+    return true;
+}
 
 }  // namespace
 
@@ -154,9 +163,8 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d, const void* q, const void* k, c
                         void* stream, void* const* stage_events) {
     int rc = gdr_bwd_check(d);
     if (rc != GDR_OK) return rc;
-    const void* req[] = {q, k, v, g, beta, do_, dq, dk, dv, dg, db, dh0};
-    for (const void* ptr : req)
-        if (!ptr || !aligned16(ptr)) return GDR_EINVAL;
+    if (!token_buffers_ok(d, {q, k, v, g, beta, do_, dq, dk, dv, dg, db})) return GDR_EINVAL;
+    if (!dh0 || !aligned16(dh0)) return GDR_EINVAL;
     if ((h0 && !aligned16(h0)) || (dht && !aligned16(dht))) return GDR_EINVAL;
     gdr::Params p;
     rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
@@ -174,9 +182,7 @@ int gdr_fwd(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v
             void* workspace, size_t workspace_bytes, void* stream) {
     int rc = gdr_bwd_check(d);
     if (rc != GDR_OK) return rc;
-    const void* req[] = {q, k, v, g, beta, o};
-    for (const void* ptr : req)
-        if (!ptr || !aligned16(ptr)) return GDR_EINVAL;
+    if (!token_buffers_ok(d, {q, k, v, g, beta, o})) return GDR_EINVAL;
     if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return GDR_EINVAL;
     gdr::Params p;
     rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
@@ -195,9 +201,8 @@ int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d, const void* q, const void* k, con
                       float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = gdr_bwd_check(d);
     if (rc != GDR_OK) return rc;
-    const void* req[] = {q, k, v, g, beta, do_, dq, dk, dv, dg, db, dh0};
-    for (const void* ptr : req)
-        if (!ptr || !aligned16(ptr)) return GDR_EINVAL;
+    if (!token_buffers_ok(d, {q, k, v, g, beta, do_, dq, dk, dv, dg, db})) return GDR_EINVAL;
+    if (!dh0 || !aligned16(dh0)) return GDR_EINVAL;
     if (dht && !aligned16(dht)) return GDR_EINVAL;
     gdr::Params p;
     rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);

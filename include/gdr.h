@@ -114,7 +114,9 @@ size_t gdr_bwd_workspace_bytes(const gdr_bwd_desc_t* d);
  * workspace:    device buffer of at least gdr_bwd_workspace_bytes(d) bytes,
  *               256-byte aligned; contents on entry are ignored.
  * Every buffer must be 16-byte aligned. Varlen tokens outside
- * [cu_seqlens[0], cu_seqlens[n_seqs]) are not written.
+ * [cu_seqlens[0], cu_seqlens[n_seqs]) are not written. With T == 0 (no tokens;
+ * varlen: every sequence empty) the token buffers may be NULL; dh0 is still
+ * written (= dht, or zero).
  */
 int gdr_bwd(const gdr_bwd_desc_t* d,
             const void* q, const void* k, const void* v, const float* g,
@@ -150,6 +152,7 @@ int gdr_bwd_with_events(const gdr_bwd_desc_t* d,
  * cu_seqlens: as for gdr_bwd. Outputs (device, fully overwritten):
  *   o           [B,T,H,V]  io_dtype
  *   ht          [N,H,K,V]  fp32 final states; NULL = not written
+ * With T == 0 the token buffers (q, k, v, g, beta, o) may be NULL.
  * workspace:    as for gdr_bwd (gdr_bwd_workspace_bytes(d) bytes); the pass
  *               leaves the per-chunk states h_c in it (region 12).
  * Same descriptor, alignment, ownership and error codes as gdr_bwd.

@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 import oracle
-from gdr_workloads import Workload, head_subset, make_inputs  # noqa: F401
+from gdr_workloads import WORKLOADS, Workload, head_subset, make_inputs, scaled  # noqa: F401
 
 OUTS = ("dq", "dk", "dv", "dg", "db", "dh0")
 
@@ -77,3 +77,15 @@ def parity(w: Workload, hks=None, with_h0=True, with_dht=True):
     sub, hv = head_subset(inp, hks)
     ref = run_oracle(sub, with_h0, with_dht)
     return rel_errors(gpu, ref, real_token_mask(inp), hks=hks, hv=hv)
+
+
+def varlen_with_empty_sequences() -> dict:
+    """Packed T = 128 with sequence lengths [0, 37, 0, 0, 90, 1, 0] (K = V = 64,
+    bf16, per-channel gate); h0 and dht drawn per sequence (seed 41)."""
+    w = scaled(WORKLOADS["kda_fixed_h16"], B=1, T=128, H=2, Hg=2, K=64, V=64, seed=41)
+    inp = make_inputs(w)
+    gen = torch.Generator().manual_seed(41)
+    inp["cu_seqlens"] = torch.tensor([0, 0, 37, 37, 37, 127, 128, 128], dtype=torch.int32)
+    inp["h0"] = torch.randn(7, 2, 64, 64, generator=gen) * 0.1
+    inp["dht"] = torch.randn(7, 2, 64, 64, generator=gen) * 0.1
+    return inp

@@ -96,3 +96,23 @@ def test_fwd_full_gdn_gqa_fp16():
 
 def test_fwd_full_kda_varlen():
     check(VARLEN, hks=[3])
+
+
+def test_fwd_empty_input():
+    """T = 0: o is empty and ht is h0 passed through."""
+    import chunked_gated_delta_gdr_amd as gdr
+    w = scaled(KDA16, B=2, T=0, H=2, Hg=2, K=64, V=64, h0_std=0.1)
+    inp = make_inputs(w)
+    t = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    o, ht = gdr.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], h0=t["h0"], scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert torch.equal(ht.cpu(), inp["h0"])
+
+
+def test_fwd_varlen_with_empty_sequences():
+    inp = tu.varlen_with_empty_sequences()
+    o, ht = run_fwd(inp)
+    ro, rht = ref_fwd(inp)
+    e = errs(o, ht, ro, rht, tu.real_token_mask(inp))
+    assert all(v <= 2e-2 for v in e.values()), e

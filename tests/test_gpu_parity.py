@@ -205,3 +205,27 @@ def test_full_kda_varlen():
 
 def test_full_kda_long():
     _check(tu.parity(WORKLOADS["kda_long"], hks=[7, 30]), 2e-2)
+
+
+# ---------------------------------------------------------------------------
+# empty inputs
+# ---------------------------------------------------------------------------
+
+def test_empty_input_fixed_length():
+    """T = 0: no token outputs, and dh0 is dht passed through (zero without it)."""
+    w = scaled(KDA16, B=2, T=0, H=2, Hg=2, K=64, V=64, h0_std=0.1, dht_std=0.1)
+    inp = make_inputs(w)
+    got = tu.run_gpu(inp)
+    for n in ("dq", "dk", "dv", "dg", "db"):
+        assert got[n].numel() == 0, n
+    assert torch.equal(got["dh0"], inp["dht"])
+    assert torch.count_nonzero(tu.run_gpu(inp, with_dht=False)["dh0"]) == 0
+
+
+def test_varlen_with_empty_sequences():
+    inp = tu.varlen_with_empty_sequences()
+    errs = tu.rel_errors(tu.run_gpu(inp), tu.run_oracle(inp), tu.real_token_mask(inp))
+    _check(errs, 2e-2, "empty sequences")
+    got = tu.run_gpu(inp)
+    for n in (0, 2, 3, 6):   # the empty sequences pass dht through
+        assert torch.equal(got["dh0"][n], inp["dht"][n]), n
