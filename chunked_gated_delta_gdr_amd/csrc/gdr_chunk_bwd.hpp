@@ -422,9 +422,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         // sit in PR consecutive lanes)
 #pragma unroll
         for (int i = 0; i < NPD; ++i) {
-            float x = hdh[i];
-#pragma unroll
-            for (int m = 1; m < PR; m <<= 1) x += __shfl_xor(x, m);
+            static_assert(PR == 4 || PR == 8, "piece rows of 4 or 8 lanes");
+            const float x = PR == 4 ? quad_sum(hdh[i]) : row8_sum(hdh[i]);
             const int e = tid + NT * i;
             if (e < D * PR && e % PR == 0) dGl[e / PR] = kLn2 * pgl[i] * x;
         }
@@ -489,8 +488,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 colk += kv * dki;
             }
             // sum over the 16 rows of this wave (4 in-lane, 4 lane groups)
-            colk += __shfl_xor(colk, 16);
-            colk += __shfl_xor(colk, 32);
+            colk = cross_row_sum(colk);
             if (l < 16) dGlw[rb * D + c] = kLn2 * colk;  // summed in block order later
             const int rr = r0 + acc_row(0, l);
             store4<T>(dwT + c * LC + rr, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
@@ -793,9 +791,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             // db: row sums of the partials over this wave's column half
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x = dbp[i];
-                x += __shfl_xor(x, 1); x += __shfl_xor(x, 2);
-                x += __shfl_xor(x, 4); x += __shfl_xor(x, 8);
+                const float x = row16_sum(dbp[i]);
                 if ((l & 15) == 0) dbS[ch * C + r0 + acc_row(i, l)] = x;
             }
             // dG_last joins the last row of the chunk
@@ -818,8 +814,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 PG[t][1] += PG[t][2];
                 PG[t][0] += PG[t][1];
                 const float tot = PG[t][0];
-                const float u1 = __shfl_down(tot, 16), u2 = __shfl_down(tot, 32), u3 = __shfl_down(tot, 48);
-                const float ex = (lg < 3 ? u1 : 0.f) + (lg < 2 ? u2 : 0.f) + (lg < 1 ? u3 : 0.f);
+                // totals of the later lane groups (rows lg ^ 1, lg ^ 2, lg ^ 3)
+                const float u = xor16(tot, l), v = xor32(tot, l), uv = xor32(u, l);
+                const float ex = lg == 0 ? u + v + uv : lg == 1 ? v + uv : lg == 2 ? u : 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) PG[t][i] += ex;
                 if (lg == 0) btot[rb * D + c] = PG[t][0];
@@ -859,8 +856,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                     float x = 0.f;
 #pragma unroll
                     for (int t = 0; t < NTD; ++t) x += PG[t][i];
-                    x += __shfl_xor(x, 1); x += __shfl_xor(x, 2);
-                    x += __shfl_xor(x, 4); x += __shfl_xor(x, 8);
+                    x = row16_sum(x);
                     if ((l & 15) == 0) dgR[ch * C + r0 + acc_row(i, l)] = x;
                 }
             }

@@ -225,10 +225,78 @@ __device__ __forceinline__ f32x4 mma16(f32x4 acc, const T* A, int lda, int i0, i
     return acc;
 }
 
+// Cross-lane reductions without LDS: DPP moves within the 16-lane rows of the
+// wave (quad_perm xor 1 / xor 2, half-row mirror, row mirror) and gfx950's
+// permlane swaps across rows. Every lane of the group receives the result;
+// all 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// sum over the 4 lanes of a quad, the 8 lanes of a half row, the 16 lanes of a row
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    return x + dpp_mov<kDppXor2>(x);
+}
+__device__ __forceinline__ float row8_sum(float x) {
+    x = quad_sum(x);                       // quads q0, q1 of the half row
+    return x + dpp_mov<kDppHalfMirror>(x); // lane i <- lane 7 - i: the other quad
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x = row8_sum(x);
+    return x + dpp_mov<kDppMirror>(x);     // lane i <- lane 15 - i: the other half
+}
+// v_permlane16_swap on two copies of a leaves (rows 0,0,2,2 of a) in the first
+// register and (rows 1,1,3,3) in the second; v_permlane32_swap leaves (rows
+// 0,1,0,1) and (rows 2,3,2,3) (checked on the device): the two halves of each
+// lane's exchange with row r ^ 1 (r ^ 2). Written as asm with both registers
+// read-write: this toolchain's builtins lose track of the second result. The
+// s_nop gives the two wait states the compiler itself puts before the
+// instruction after a VALU write of its operands.
+__device__ __forceinline__ void swap16(float x, float& lo, float& hi) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    lo = __builtin_bit_cast(float, a);
+    hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    lo = __builtin_bit_cast(float, a);
+    hi = __builtin_bit_cast(float, b);
+}
+// The value of row r ^ 1 (xor16) / r ^ 2 (xor32) at the same lane of the row.
+__device__ __forceinline__ float xor16(float x, int l) {
+    float lo, hi;
+    swap16(x, lo, hi);
+    return (l & 16) ? lo : hi;
+}
+__device__ __forceinline__ float xor32(float x, int l) {
+    float lo, hi;
+    swap32(x, lo, hi);
+    return (l & 32) ? lo : hi;
+}
+// sum over the 4 rows at the same lane of the row
+__device__ __forceinline__ float cross_row_sum(float x) {
+    float lo, hi;
+    swap16(x, lo, hi);
+    x = lo + hi;
+    swap32(x, lo, hi);
+    return lo + hi;
+}
+
 // Maximum over the wave, returned as a wave-uniform (scalar) value.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    x = fmaxf(x, dpp_mov<kDppXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppXor2>(x));
+    x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_mov<kDppMirror>(x));
+    float lo, hi;
+    swap16(x, lo, hi);
+    x = fmaxf(lo, hi);
+    swap32(x, lo, hi);
+    x = fmaxf(lo, hi);
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 

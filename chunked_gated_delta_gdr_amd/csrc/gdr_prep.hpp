@@ -361,9 +361,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
                     E[i0 + i] *= as[i];   // E(r, s-1) = E(r, s) * 2^g_s
                 }
             }
-            pq += __shfl_xor(pq, 1); pk += __shfl_xor(pk, 1);
-            pq += __shfl_xor(pq, 2); pk += __shfl_xor(pk, 2);
-            pq += __shfl_xor(pq, 4); pk += __shfl_xor(pk, 4);
+            pq = row8_sum(pq);   // the 8 d-parts are 8 consecutive lanes
+            pk = row8_sum(pk);
             if (e8 == 0) {
                 if (!is_kk) AqkF[r * LCF + s] = pq;
                 else if (s < r) AkkF[r * LCF + s] = bs[r] * pk;
