@@ -170,11 +170,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     float* btot = reinterpret_cast<float*>(smem + L::BT_OFF);
     char* const U0 = smem + L::U_OFF;
 
-    const int j = blockIdx.x, hk = blockIdx.y;
-    if (j >= p.seq_off[p.N]) return;
-    const ChunkEntry ce = p.ctab[j];
-    const int tok0 = ce.tok0, len = ce.len;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int w = wave_id();
     const int rb = w % NB, ch = w / NB;
     const int r0 = 16 * rb;                   // this wave's rows
     const int cd0 = ch * DH2, cc0 = ch * CH2, cv0 = ch * VH2;  // its column halves
@@ -184,17 +180,80 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     const T* dout = static_cast<const T*>(p.dout);
     const T* beta = static_cast<const T*>(p.beta);
 
-    // q, k rows of this chunk, requested first (zero past the sequence end);
-    // they reach LDS in the first head, after that head's own requests
+    // What a head needs before its first slice: the chunk's q, k rows (first
+    // head only), the first slice's pieces, the row fragments of scale Aqk^T and
+    // A^T, A (staged in LDS for dA A^T), beta and 2^G_last. They are requested
+    // together, so that one wait covers them all; the persistent (non-grouped)
+    // kernel requests them for its next item during the current item's epilogue.
+    using Frag = typename Mfma<T>::frag;
+    constexpr int KS = kstep<T>(), NKC = C / KS;
     constexpr int NQP = C * (D / V8) / NT;
     static_assert(NQP * NT == C * (D / V8), "piece split");
+    constexpr int PR = BVS / V8;                              // 16-byte pieces per slice row
+    constexpr int NPC = (C * PR + NT - 1) / NT, NPD = (D * PR + NT - 1) / NT;
+    constexpr int NAM = (C * (C / V8) + NT - 1) / NT;
     Vec16 qv[NQP], kv[NQP];
+    Vec16 pdo[NPC], pv[NPC], px[NPC], pt[NPC], ph[NPD], pdh[NPD];
+    Frag fAq[NKC], fAT[NKC];   // rows r0.. of scale Aqk^T and A^T (A^T again in 2c, 2e)
+    Vec16 pam[NAM];
+    float pbeta, pgl[NPD];
+    // rows past the sequence end read its last row (zeroed at use)
+    auto request_qk = [&](const ChunkEntry& e2, const int hk2, const int tid) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NQP; ++i) {
-        const int e = tid + i * NT, r = min(e / (D / V8), len - 1), d0 = (e % (D / V8)) * V8;
-        qv[i] = ld16(q + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-        kv[i] = ld16(k + ((size_t)(tok0 + r) * p.Hg + hk) * D + d0);
-    }
+        for (int i = 0; i < NQP; ++i) {
+            const int e = tid + i * NT, r = min(e / (D / V8), e2.len - 1), d0 = (e % (D / V8)) * V8;
+            qv[i] = ld16(q + ((size_t)(e2.tok0 + r) * p.Hg + hk2) * D + d0);
+            kv[i] = ld16(k + ((size_t)(e2.tok0 + r) * p.Hg + hk2) * D + d0);
+        }
+    };
+    // slice pieces of value columns v0 .. v0 + BVS: unconditional loads (spare
+    // threads and rows past the sequence end read valid duplicates, zeroed at
+    // use), so no load waits on a branch
+    auto request_slice = [&](const ChunkEntry& e2, const size_t jh2, const int h2, const int v0,
+                             const int tid) __attribute__((always_inline)) {
+        const T* xb = static_cast<const T*>(p.xbuf) + jh2 * C * D;
+        const T* tb = static_cast<const T*>(p.tbuf) + jh2 * C * D;
+        const T* hb = static_cast<const T*>(p.hbuf) + jh2 * D * D;
+        const T* dhb = static_cast<const T*>(p.dhbuf) + jh2 * D * D;
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int e = min(tid + NT * i, C * PR - 1);
+            const int r = e / PR, c = (e % PR) * V8, rt = min(r, e2.len - 1);
+            const size_t row = ((size_t)(e2.tok0 + rt) * p.H + h2) * D + v0 + c;
+            pdo[i] = ld16(dout + row);
+            pv[i] = ld16(v + row);
+            px[i] = ld16(xb + (size_t)v0 * C + r * BVS + c);   // V-tiled
+            pt[i] = ld16(tb + (size_t)v0 * C + r * BVS + c);
+        }
+#pragma unroll
+        for (int i = 0; i < NPD; ++i) {
+            const int e = min(tid + NT * i, D * PR - 1);
+            const int d = e / PR, c = (e % PR) * V8;
+            ph[i] = ld16(hb + (size_t)v0 * D + d * BVS + c);   // V-tiled
+            pdh[i] = ld16(dhb + (size_t)v0 * D + d * BVS + c);
+        }
+    };
+    auto request_head = [&](const ChunkEntry& e2, const int j2, const int h2, const int tid,
+                            const int l) __attribute__((always_inline)) {
+        const size_t jh2 = (size_t)j2 * p.H + h2;
+        const T* Am = static_cast<const T*>(p.Am) + jh2 * C * C;
+        const T* AT = static_cast<const T*>(p.AT) + jh2 * C * C;
+        const T* sAqkT = static_cast<const T*>(p.sAqkT) + jh2 * C * C;
+        pbeta = to_f32(beta[(size_t)(e2.tok0 + min(tid, e2.len - 1)) * p.H + h2]);
+#pragma unroll
+        for (int i = 0; i < NAM; ++i) {
+            const int e = min(tid + NT * i, C * (C / V8) - 1);
+            pam[i] = ld16(Am + (size_t)e * V8);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NKC; ++k2) {
+            fAq[k2] = frag_kc(sAqkT, C, r0, k2 * KS, l);
+            fAT[k2] = frag_kc(AT, C, r0, k2 * KS, l);
+        }
+        request_slice(e2, jh2, h2, 0, tid);
+#pragma unroll
+        for (int i = 0; i < NPD; ++i) pgl[i] = p.glast[jh2 * D + min((tid + NT * i) / PR, D - 1)];
+    };
 
     // GROUPED: fp32 group sums of dq, dk in this wave's accumulator tiles
     f32x4 dq_tot[GROUPED ? NTD : 1], dk_tot[GROUPED ? NTD : 1];
@@ -207,35 +266,30 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
     // a loop around this body lets the compiler hoist the (lane-dependent)
     // address arithmetic of every unrolled LDS access out of it and keep it
     // live across iterations, which costs hundreds of registers.
-    auto head = [&](const int gi, const bool first) __attribute__((always_inline)) {
+    auto head = [&](const int j, const int hk, const int gi, const ChunkEntry ce, const bool first,
+                    auto&& at_epilogue) __attribute__((always_inline)) {
         const int l = opaque_lane_id();  // fresh per head: see above
+        const int tid = [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }();
+        // the wave's rows and column halves, also fresh per head (shadowing the
+        // kernel-scope ones), so that no address derived from them is kept
+        // live across the items of the persistent kernel
+        const int w = [] {
+            int t = __builtin_amdgcn_readfirstlane(wave_id());
+            asm volatile("" : "+s"(t));
+            return t;
+        }();
+        const int rb = w % NB, ch = w / NB;
+        const int r0 = 16 * rb;
+        const int cd0 = ch * DH2, cc0 = ch * CH2, cv0 = ch * VH2;
+        const int tok0 = ce.tok0, len = ce.len;
         char* U = U0;
         T* qL = qL0;
         T* kL = kL0;
         const int h = hk * p.G + gi;
         const size_t jh = (size_t)j * p.H + h;
-        const T* AT = static_cast<const T*>(p.AT) + jh * C * C;
-        const T* Am = static_cast<const T*>(p.Am) + jh * C * C;
-        const T* sAqkT = static_cast<const T*>(p.sAqkT) + jh * C * C;
-        const T* xb = static_cast<const T*>(p.xbuf) + jh * C * D;
-        const T* tb = static_cast<const T*>(p.tbuf) + jh * C * D;
-        const T* hb = static_cast<const T*>(p.hbuf) + jh * D * D;
-        const T* dhb = static_cast<const T*>(p.dhbuf) + jh * D * D;
-        const T* dorow = dout + ((size_t)tok0 * p.H + h) * D;   // row r at dorow + r*H*D
         const long ldo = (long)p.H * D;
 
         __syncthreads();  // previous head's LDS use is over
-        // The head's small inputs are requested together with its first slice
-        // (below), so that one wait covers them all: beta, 2^G_last, A (staged
-        // in LDS for dA A^T); each thread holds at most a few values.
-        constexpr int NAM = (C * (C / V8) + NT - 1) / NT;
-        const float pbeta = to_f32(beta[(size_t)(tok0 + min(tid, len - 1)) * p.H + h]);
-        Vec16 pam[NAM];
-#pragma unroll
-        for (int i = 0; i < NAM; ++i) {
-            const int e = min(tid + NT * i, C * (C / V8) - 1);
-            pam[i] = ld16(Am + (size_t)e * V8);
-        }
 
         // ================= phase 1: state products over V slices =================
         // The slice pieces (rows of do, v, X, T and of h, dh') are loaded one
@@ -259,45 +313,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         T* TL = reinterpret_cast<T*>(U + L::P1_TL);
         T* dvS = reinterpret_cast<T*>(U + L::DVS);
 
-        using Frag = typename Mfma<T>::frag;
-        constexpr int KS = kstep<T>(), NKC = C / KS;
-        Frag fAq[NKC], fAT[NKC];   // rows r0.. of scale Aqk^T and A^T (A^T again in 2c, 2e)
-#pragma unroll
-        for (int k2 = 0; k2 < NKC; ++k2) {
-            fAq[k2] = frag_kc(sAqkT, C, r0, k2 * KS, l);
-            fAT[k2] = frag_kc(AT, C, r0, k2 * KS, l);
-        }
-
-        constexpr int PR = BVS / V8;                              // 16-byte pieces per slice row
-        constexpr int NPC = (C * PR + NT - 1) / NT, NPD = (D * PR + NT - 1) / NT;
-        Vec16 pdo[NPC], pv[NPC], px[NPC], pt[NPC], ph[NPD], pdh[NPD];
         float hdh[NPD];                                           // partial rowsum(h dh') per piece row
 #pragma unroll
         for (int i = 0; i < NPD; ++i) hdh[i] = 0.f;
-        // unconditional loads (spare threads and rows past the sequence end read
-        // valid duplicates, zeroed at use), so no load waits on a branch
-        auto load_slice = [&](const int v0) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < NPC; ++i) {
-                const int e = min(tid + NT * i, C * PR - 1);
-                const int r = e / PR, c = (e % PR) * V8, rt = min(r, len - 1);
-                pdo[i] = ld16(dorow + (long)rt * ldo + v0 + c);
-                pv[i] = ld16(v + ((size_t)(tok0 + rt) * p.H + h) * D + v0 + c);
-                px[i] = ld16(xb + (size_t)v0 * C + r * BVS + c);   // V-tiled
-                pt[i] = ld16(tb + (size_t)v0 * C + r * BVS + c);
-            }
-#pragma unroll
-            for (int i = 0; i < NPD; ++i) {
-                const int e = min(tid + NT * i, D * PR - 1);
-                const int d = e / PR, c = (e % PR) * V8;
-                ph[i] = ld16(hb + (size_t)v0 * D + d * BVS + c);   // V-tiled
-                pdh[i] = ld16(dhb + (size_t)v0 * D + d * BVS + c);
-            }
-        };
-        load_slice(0);
-        float pgl[NPD];   // 2^G_last of the row this thread closes in dG_last
-#pragma unroll
-        for (int i = 0; i < NPD; ++i) pgl[i] = p.glast[jh * D + min((tid + NT * i) / PR, D - 1)];
         if (first) {
 #pragma unroll
             for (int i = 0; i < NQP; ++i) {
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
                 }
             }
             if (v0 + BVS < D) {
-                load_slice(v0 + BVS);   // next slice
+                request_slice(ce, jh, h, v0 + BVS, tid);   // next slice
             } else {
 #pragma unroll
                 for (int jj = 0; jj < SR; ++jj) {
@@ -786,6 +804,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
 
         // ================= epilogue (accumulator layout) =================
+        at_epilogue(tid, l);   // the next item's first requests (persistent kernel)
         {
             const int l = opaque_lane_id();
             // db: row sums of the partials over this wave's column half
@@ -876,11 +895,21 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             if constexpr (SCALAR) p.dg[(size_t)(tok0 + tid) * p.H + h] = dgR[tid] + dgR[C + tid];
         }
     };
-    head(0, true);
     if constexpr (GROUPED) {
-        for (int gi = 1; gi < p.G; ++gi) head(gi, false);
-    }
-    if constexpr (GROUPED) {
+        // one workgroup per (chunk, q/k head); its value heads in turn, dq and
+        // dk summed over them in fp32
+        const int j = blockIdx.x, hk = blockIdx.y;
+        if (j >= p.seq_off[p.N]) return;
+        const ChunkEntry ce = p.ctab[j];
+        const int tok0 = ce.tok0, len = ce.len, tid = threadIdx.x, l = lane_id();
+        auto none = [](int, int) {};
+        request_qk(ce, hk, tid);
+        request_head(ce, j, hk * p.G, tid, l);
+        head(j, hk, 0, ce, true, none);
+        for (int gi = 1; gi < p.G; ++gi) {
+            request_head(ce, j, hk * p.G + gi, tid, l);
+            head(j, hk, gi, ce, false, none);
+        }
         // dq, dk group sums: staged in LDS, stored row-contiguous
         __syncthreads();
         T* dqS = reinterpret_cast<T*>(U0 + L::E_DQ);
@@ -897,6 +926,26 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
         __syncthreads();
         store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
+    } else {
+        // persistent: at most one workgroup per CU walks the (chunk, head)
+        // items blockIdx.x, + gridDim.x, ...; the next item's first requests go
+        // out in the current item's epilogue (past the end: a redundant valid one)
+        const int nit = p.seq_off[p.N] * p.Hg;
+        int item = blockIdx.x;
+        if (item >= nit) return;
+        ChunkEntry ce = p.ctab[item / p.Hg];
+        request_qk(ce, item % p.Hg, threadIdx.x);
+        request_head(ce, item / p.Hg, item % p.Hg, threadIdx.x, lane_id());
+#pragma unroll 1
+        for (; item < nit; item += gridDim.x) {
+            const int nxt = min(item + (int)gridDim.x, nit - 1);
+            const ChunkEntry ce_n = p.ctab[nxt / p.Hg];
+            head(item / p.Hg, item % p.Hg, 0, ce, true, [&](const int tid, const int l) __attribute__((always_inline)) {
+                request_qk(ce_n, nxt % p.Hg, tid);
+                request_head(ce_n, nxt / p.Hg, nxt % p.Hg, tid, l);
+            });
+            ce = ce_n;
+        }
     }
 }
 

@@ -57,9 +57,14 @@ template <typename T, int C, int D, bool SCALAR>
 hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
     hipError_t e = launch_front<T, C, D, SCALAR>(p, stream, ev);
     if (p.nc_max > 0) {
-        const dim3 grid(p.nc_max, p.Hg), block(128 * (C / 16));
-        if (p.G > 1) gdr_chunk_bwd<T, C, D, SCALAR, true><<<grid, block, 0, stream>>>(p);
-        else gdr_chunk_bwd<T, C, D, SCALAR, false><<<grid, block, 0, stream>>>(p);
+        const dim3 block(128 * (C / 16));
+        if (p.G > 1) {
+            gdr_chunk_bwd<T, C, D, SCALAR, true><<<dim3(p.nc_max, p.Hg), block, 0, stream>>>(p);
+        } else {   // persistent over (chunk, head) items, at most one workgroup per CU
+            const int items = p.nc_max * p.Hg;
+            gdr_chunk_bwd<T, C, D, SCALAR, false><<<dim3(items < compute_units() ? items : compute_units()),
+                                                     block, 0, stream>>>(p);
+        }
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[4], stream);
     const hipError_t le = hipGetLastError();
