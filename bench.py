@@ -313,8 +313,8 @@ def bench_train(args, w, inp, t, tokens, n_chunks, n_seqs, ws) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="kda_fixed_h16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("bwd", "fwd", "train"), default="bwd",
