@@ -75,6 +75,32 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_kc(const T* p, int ld, in
     return *reinterpret_cast<const typename Mfma<T>::frag*>(q);
 }
 
+// MFMA fragment order of a [R][K] operand matrix with 16-bit elements (the
+// 16x16x32 MFMAs): the 16 x 32 tile (row tile r / 16, k step k / 32) is one
+// contiguous 1 KB block in which lane l's 8 elements (row 16 (r / 16) + l % 16,
+// columns 32 (k / 32) + 8 (l / 16) ..+7) sit at 16 l bytes, so that a wave
+// loads a whole A fragment as one contiguous 1 KB access (whole cache lines).
+// fp32 operands (16x16x4 MFMAs) stay row-major. Element index of (r, k):
+template <typename T, int K>
+__device__ __forceinline__ size_t fo_index(int r, int k) {
+    if constexpr (sizeof(T) == 2) {
+        static_assert(K % 32 == 0, "k steps of 32");
+        return ((size_t)(r >> 4) * (K / 32) + (k >> 5)) * 512 + ((r & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+    } else {
+        return (size_t)r * K + k;
+    }
+}
+// The A fragment (rows i0 .. +15, k0 .. +KS) of such a matrix.
+template <typename T, int K>
+__device__ __forceinline__ typename Mfma<T>::frag frag_fo(const T* p, int i0, int k0, int l = lane_id()) {
+    if constexpr (sizeof(T) == 2) {
+        return *reinterpret_cast<const typename Mfma<T>::frag*>(
+            p + ((size_t)(i0 >> 4) * (K / 32) + (k0 >> 5)) * 512 + l * 8);
+    } else {
+        return frag_kc(p, K, i0, k0, l);
+    }
+}
+
 // Same fragment of a matrix stored with the reduction index as the row:
 // element (i, kk) at p[kk*ld + i].
 template <typename T>
@@ -369,11 +395,12 @@ struct Params {
     void* sAqkT;         // [nc][H][C][C]  scale * Aqk^T
     void* Am;            // [nc][H][C][C]  A = (I + Akk)^-1
     void* AT;            // [nc][H][C][C]  A^T
+    // w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
     void* w;             // [nc][H][C][D]  w = A (beta k 2^G)
     void* wT;            // [nc][H][D][C]
     void* kt;            // [nc][H][C][D]  k 2^(G_last - G)
     void* ktT;           // [nc][H][D][C]
-    void* uT;            // [nc][H][D][C]  u = A (beta v), transposed
+    void* uT;            // [nc][H][D][C]  u = A (beta v), transposed (row-major)
     void* qsT;           // [nc][H][D][C]  scale * (q 2^G - Aqk w), transposed
     float* glast;        // [nc][H][D]     2^G_last
     // V-tiled ([..][D / kTileV][rows][kTileV]): one contiguous block per

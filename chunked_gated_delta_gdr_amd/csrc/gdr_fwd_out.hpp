@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_fwd_out(Params p) {
 
     for (int e = tid; e < D * (C / V8); e += NT) {
         const int d = e / (C / V8), c = (e % (C / V8)) * V8;
-        st16(qsL + d * LC + c, ld16(gq + (size_t)d * C + c));
+        st16(qsL + d * LC + c, ld16(gq + fo_index<T, C>(d, c)));   // fragment order
         st16(uL + d * LC + c, ld16(gu + (size_t)d * C + c));
     }
     for (int e = tid; e < C * (C / V8); e += NT) {

@@ -514,14 +514,14 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             const int d = e / (C / 8), s0 = (e % (C / 8)) * 8;
             float x[8];
             load8<T>(wTL + d * LC + s0, x);
-            store8<T>(gwT + d * C + s0, x);
+            store8<T>(gwT + fo_index<T, C>(d, s0), x);
         }
         for (int e = tid; e < C * (D / 8); e += NT) {
             const int r = e % C, d0 = (e / C) * 8;   // r fastest: the transposed reads conflict-free
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = to_f32(wTL[(d0 + i) * LC + r]);
-            store8<T>(gw + r * D + d0, x);
+            store8<T>(gw + fo_index<T, D>(r, d0), x);
         }
     }
 
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
                 const int r = rb + i;
                 o[i] = p.scale * (to_f32(qL[r * LT + c]) * fast_exp2(Gs[r * LF + c]) - acc[t][i]);
             }
-            store4<T>(gq + c * C + rb, o[0], o[1], o[2], o[3]);
+            store4<T>(gq + fo_index<T, C>(c, rb), o[0], o[1], o[2], o[3]);
         }
     }
     __syncthreads();  // Xb (w^T) -> v^T
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             load8f(Gs + r * LF + d0, g);
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
-            store8<T>(gkt + r * D + d0, x);
+            store8<T>(gkt + fo_index<T, D>(r, d0), x);
         }
         for (int e = tid; e < D * (C / 8); e += NT) {
             const int d = e % D, r0b = (e / D) * 8;   // d fastest (bank-conflict free)
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 x[i] = to_f32(kL[(r0b + i) * LT + d]) * fast_exp2(gl - Gs[(r0b + i) * LF + d]);
-            store8<T>(gktT + d * C + r0b, x);
+            store8<T>(gktT + fo_index<T, C>(d, r0b), x);
         }
         for (int d = tid; d < D; d += NT) p.glast[jh * D + d] = fast_exp2(Gs[(C - 1) * LF + d]);
     }

@@ -69,11 +69,11 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
 #pragma unroll
     for (int i = 0; i < S::XRT; ++i)
 #pragma unroll
-        for (int k = 0; k < D / S::KS; ++k) o.a1[i][k] = frag_kc(A1, D, 16 * S::xrow(w, i), k * S::KS);
+        for (int k = 0; k < D / S::KS; ++k) o.a1[i][k] = frag_fo<T, D>(A1, 16 * S::xrow(w, i), k * S::KS);
 #pragma unroll
     for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
-        for (int k = 0; k < C / S::KS; ++k) o.a2[i][k] = frag_kc(A2, C, 16 * (w * S::SRW + i), k * S::KS);
+        for (int k = 0; k < C / S::KS; ++k) o.a2[i][k] = frag_fo<T, C>(A2, 16 * (w * S::SRW + i), k * S::KS);
     const float* gl = p.glast + jh * D;
 #pragma unroll
     for (int i = 0; i < S::SRW; ++i) o.gl[i] = *reinterpret_cast<const f32x4*>(gl + 16 * (w * S::SRW + i) + acc_row(0));
@@ -92,7 +92,7 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
-            for (int k = 0; k < C / S::KS; ++k) o.a3[i][k] = frag_kc(qsT, C, 16 * (w * S::SRW + i), k * S::KS);
+            for (int k = 0; k < C / S::KS; ++k) o.a3[i][k] = frag_fo<T, C>(qsT, 16 * (w * S::SRW + i), k * S::KS);
         // do rows of the chunk, this thread's 16-byte piece; rows past the
         // sequence end read its last row (always valid) and are zeroed at use
         constexpr int V8 = 16 / sizeof(T);
