@@ -247,8 +247,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
 #pragma unroll
         for (int k2 = 0; k2 < NKC; ++k2) {
-            fAq[k2] = frag_kc(sAqkT, C, r0, k2 * KS, l);
-            fAT[k2] = frag_kc(AT, C, r0, k2 * KS, l);
+            fAq[k2] = frag_fo<T, C>(sAqkT, r0, k2 * KS, l);   // both in fragment order
+            fAT[k2] = frag_fo<T, C>(AT, r0, k2 * KS, l);
         }
         request_slice(e2, jh2, h2, 0, tid);
 #pragma unroll

@@ -395,7 +395,7 @@ struct Params {
     void* sAqkT;         // [nc][H][C][C]  scale * Aqk^T
     void* Am;            // [nc][H][C][C]  A = (I + Akk)^-1
     void* AT;            // [nc][H][C][C]  A^T
-    // w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
+    // scale Aqk^T, A^T, w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
     void* w;             // [nc][H][C][D]  w = A (beta k 2^G)
     void* wT;            // [nc][H][D][C]
     void* kt;            // [nc][H][C][D]  k 2^(G_last - G)

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_fwd_out(Params p) {
     }
     for (int e = tid; e < C * (C / V8); e += NT) {
         const int r = e / (C / V8), c = (e % (C / V8)) * V8;
-        st16(saL + r * LC + c, ld16(ga + (size_t)r * C + c));
+        st16(saL + r * LC + c, ld16(ga + fo_index<T, C>(r, c)));   // fragment order
     }
     for (int e = tid; e < D * (D / V8); e += NT) {   // contiguous in the tiled layout
         const int vt = e / (D * PT), rem = e % (D * PT), d = rem / PT, c = (rem % PT) * V8;

@@ -470,8 +470,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             sq[i] = p.scale * AqkF[(ps5 + i) * LCF + pr5];
         }
         store8<T>(gA + pr5 * C + ps5, av);
-        store8<T>(gAT + pr5 * C + ps5, at);
-        store8<T>(gSq + pr5 * C + ps5, sq);
+        store8<T>(gAT + fo_index<T, C>(pr5, ps5), at);   // fragment order (row fragments of A^T)
+        store8<T>(gSq + fo_index<T, C>(pr5, ps5), sq);
     }
     __syncthreads();
     T* AtL = reinterpret_cast<T*>(smem + L::AF_OFF);    // A   [C][LC], over the dead fp32 A
