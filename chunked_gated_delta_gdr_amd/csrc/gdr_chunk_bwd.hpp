@@ -340,7 +340,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
 #pragma unroll
                 for (int i = 0; i < NAM; ++i) {
                     const int e = min(tid + NT * i, C * (C / V8) - 1);
-                    st16(AmL + (e / (C / V8)) * LC + (e % (C / V8)) * V8, pam[i]);
+                    int ar, ac;   // A is stored in fragment order
+                    fo_piece<T, C>(e, ar, ac);
+                    st16(AmL + ar * LC + ac, pam[i]);
                 }
             }
 #pragma unroll

@@ -90,6 +90,20 @@ __device__ __forceinline__ size_t fo_index(int r, int k) {
         return (size_t)r * K + k;
     }
 }
+// Row and first column of the e-th 16-byte piece of such a matrix (the inverse
+// of fo_index at piece granularity: a lane slot of a tile for 16-bit elements).
+template <typename T, int K>
+__device__ __forceinline__ void fo_piece(int e, int& r, int& c) {
+    if constexpr (sizeof(T) == 2) {
+        const int b = e >> 6, ln = e & 63;
+        r = 16 * (b / (K / 32)) + (ln & 15);
+        c = 32 * (b % (K / 32)) + 8 * (ln >> 4);
+    } else {
+        constexpr int V = 16 / sizeof(T);
+        r = e / (K / V);
+        c = (e % (K / V)) * V;
+    }
+}
 // The A fragment (rows i0 .. +15, k0 .. +KS) of such a matrix.
 template <typename T, int K>
 __device__ __forceinline__ typename Mfma<T>::frag frag_fo(const T* p, int i0, int k0, int l = lane_id()) {
@@ -395,7 +409,7 @@ struct Params {
     void* sAqkT;         // [nc][H][C][C]  scale * Aqk^T
     void* Am;            // [nc][H][C][C]  A = (I + Akk)^-1
     void* AT;            // [nc][H][C][C]  A^T
-    // scale Aqk^T, A^T, w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
+    // scale Aqk^T, A, A^T, w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
     void* w;             // [nc][H][C][D]  w = A (beta k 2^G)
     void* wT;            // [nc][H][D][C]
     void* kt;            // [nc][H][C][D]  k 2^(G_last - G)

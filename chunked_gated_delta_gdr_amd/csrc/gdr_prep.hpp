@@ -469,7 +469,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             at[i] = AF[(ps5 + i) * LCF + pr5];                // A^T[r][s] = A[s][r]
             sq[i] = p.scale * AqkF[(ps5 + i) * LCF + pr5];
         }
-        store8<T>(gA + pr5 * C + ps5, av);
+        store8<T>(gA + fo_index<T, C>(pr5, ps5), av);
         store8<T>(gAT + fo_index<T, C>(pr5, ps5), at);   // fragment order (row fragments of A^T)
         store8<T>(gSq + fo_index<T, C>(pr5, ps5), sq);
     }
@@ -574,7 +574,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         T* gkt = static_cast<T*>(p.kt) + jh * C * D;
         T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
         for (int e = tid; e < C * (D / 8); e += NT) {
-            const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            // 16-bit: row fastest, so the fragment-order stores are contiguous
+            const int r = sizeof(T) == 2 ? e % C : e / (D / 8);
+            const int d0 = sizeof(T) == 2 ? (e / C) * 8 : (e % (D / 8)) * 8;
             float x[8], gl[8], g[8];
             load8<T>(kL + r * LT + d0, x);
             load8f(Gs + (C - 1) * LF + d0, gl);
