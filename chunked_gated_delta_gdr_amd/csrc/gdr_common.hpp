@@ -90,6 +90,16 @@ __device__ __forceinline__ size_t fo_index(int r, int k) {
         return (size_t)r * K + k;
     }
 }
+// Accumulator order of a [R][K] matrix: the 16 x 16 tile (r / 16, k / 16) is one
+// contiguous block of 256 elements in which lane l's 4 elements (row
+// 16 (r / 16) + l % 16, columns 16 (k / 16) + 4 (l / 16) ..+3) sit at 4 l: the
+// order in which an MFMA accumulator tile of the transposed product holds
+// them, so that such a tile is stored, and read back as quads, contiguously.
+template <int K>
+__device__ __forceinline__ size_t ao_index(int r, int k) {
+    static_assert(K % 16 == 0, "k tiles of 16");
+    return ((size_t)(r >> 4) * (K / 16) + (k >> 4)) * 256 + ((r & 15) + 16 * ((k & 15) >> 2)) * 4 + (k & 3);
+}
 // Row and first column of the e-th 16-byte piece of such a matrix (the inverse
 // of fo_index at piece granularity: a lane slot of a tile for 16-bit elements).
 template <typename T, int K>
@@ -414,7 +424,7 @@ struct Params {
     void* wT;            // [nc][H][D][C]
     void* kt;            // [nc][H][C][D]  k 2^(G_last - G)
     void* ktT;           // [nc][H][D][C]
-    void* uT;            // [nc][H][D][C]  u = A (beta v), transposed (row-major)
+    void* uT;            // [nc][H][D][C]  u = A (beta v), transposed, in accumulator order (ao_index)
     void* qsT;           // [nc][H][D][C]  scale * (q 2^G - Aqk w), transposed
     float* glast;        // [nc][H][D]     2^G_last
     // V-tiled ([..][D / kTileV][rows][kTileV]): one contiguous block per

@@ -53,7 +53,17 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_fwd_out(Params p) {
     for (int e = tid; e < D * (C / V8); e += NT) {
         const int d = e / (C / V8), c = (e % (C / V8)) * V8;
         st16(qsL + d * LC + c, ld16(gq + fo_index<T, C>(d, c)));   // fragment order
-        st16(uL + d * LC + c, ld16(gu + (size_t)d * C + c));
+        // u^T in accumulator order: a 16-byte row piece is 4-element quads
+        Vec16 uv;
+        if constexpr (sizeof(T) == 2) {
+            uv.w[0] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c))[0];
+            uv.w[1] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c))[1];
+            uv.w[2] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c + 4))[0];
+            uv.w[3] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c + 4))[1];
+        } else {
+            uv = ld16(gu + ao_index<C>(d, c));
+        }
+        st16(uL + d * LC + c, uv);
     }
     for (int e = tid; e < C * (C / V8); e += NT) {
         const int r = e / (C / V8), c = (e % (C / V8)) * V8;

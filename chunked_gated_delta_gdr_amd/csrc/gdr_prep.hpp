@@ -565,7 +565,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
         for (int t = 0; t < NTH; ++t) {
             const int c = ch0 + 16 * t + acc_col(l), rb = r0 + acc_row(0, l);
-            store4<T>(gu + c * C + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+            store4<T>(gu + ao_index<C>(c, rb), acc[t][0], acc[t][1], acc[t][2], acc[t][3]);   // accumulator order
         }
     }
 

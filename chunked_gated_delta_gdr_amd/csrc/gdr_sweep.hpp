@@ -85,7 +85,7 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
             for (int jj = 0; jj < S::XCT; ++jj) {
                 const int r = 16 * S::xrow(w, i) + acc_row(0);
                 const int c = v0 + 16 * S::xcol(w, jj) + acc_col();
-                o.u[i][jj] = *reinterpret_cast<const Q*>(uT + (size_t)c * C + r);
+                o.u[i][jj] = *reinterpret_cast<const Q*>(uT + ao_index<C>(c, r));   // accumulator order
             }
     } else {
         const T* qsT = static_cast<const T*>(p.qsT) + jh * D * C;

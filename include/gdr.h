@@ -193,7 +193,8 @@ int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d,
  * Per-chunk regions are [chunks][H][..] in io_dtype (2^G_last in fp32);
  * h, X, dh and T are stored in tiles of 32 state columns, [D/32][rows][32];
  * with 16-bit io, scale*Aqk^T, A, A^T, w, w^T, k~, k~^T and scale*q~^T are
- * stored in MFMA fragment order (each 16 x 32 tile one contiguous 1 KB block).
+ * stored in MFMA fragment order (each 16 x 32 tile one contiguous 1 KB block)
+ * and u^T in accumulator order (each 16 x 16 tile one contiguous block).
  * For inspecting intermediates in tests; n must be >= 17.
  * Returns GDR_OK, GDR_EINVAL or GDR_EUNSUPPORTED. Touches no GPU state.
  */
