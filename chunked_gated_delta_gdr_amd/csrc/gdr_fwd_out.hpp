@@ -17,7 +17,10 @@ namespace gdr {
 
 template <typename T, int C, int D>
 struct FwdOutLds {
-    static constexpr int LC = C + pad<T>(), LH = D + pad<T>();
+    // h rows unpadded: its strided B-fragment reads (rows 8 apart) meet the same
+    // banks with or without a pad, and without it the kernel fits 80 KB of LDS,
+    // so that two workgroups share a CU
+    static constexpr int LC = C + pad<T>(), LH = D;
     static constexpr size_t QS = 0;                                  // T [D][LC] scale q~^T
     static constexpr size_t SA = QS + size_t(D) * LC * sizeof(T);    // T [C][LC] scale Aqk^T
     static constexpr size_t UT = SA + size_t(C) * LC * sizeof(T);    // T [D][LC] u^T
@@ -26,6 +29,7 @@ struct FwdOutLds {
     static constexpr size_t OS = 0;                                  // T [C][LH] o, over the dead operands
     static_assert(size_t(C) * LH * sizeof(T) <= HL, "o staging clear of h");
     static_assert(TOTAL <= 163840, "LDS budget of gdr_fwd_out");
+    static_assert(sizeof(T) != 2 || TOTAL <= 81920, "two workgroups per CU (16-bit io)");
 };
 
 template <typename T, int C, int D>
