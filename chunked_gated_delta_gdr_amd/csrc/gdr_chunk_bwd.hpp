@@ -1,7 +1,10 @@
 // gdr_chunk_bwd.hpp -- chunk-parallel gradient kernel.
 //
-// One workgroup per (chunk, q/k head); it loops over the value heads of the
-// GQA group and sums dq / dk over them in fp32. 2 C/16 waves: wave w owns
+// Work item: one (chunk, q/k head). Without GQA the kernel is persistent (at
+// most one workgroup per CU walks the items and requests the next item's
+// first inputs during the current item's epilogue); with GQA one workgroup per
+// item loops over the value heads of the group and sums dq / dk over them in
+// fp32. 2 C/16 waves: wave w owns
 // rows 16 (w % NB) .. +16 (diagonal block w % NB) and the column half w / NB
 // of every [C][*] product, which keeps each wave's accumulators small enough
 // for two waves per SIMD. With h = h_c, dh' = dh_{c+1},
@@ -262,10 +265,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         for (int t = 0; t < NTD; ++t) { dq_tot[t] = zero4(); dk_tot[t] = zero4(); }
     }
 
-    // One value head per call of `head`. With G == 1 there is no loop at all:
-    // a loop around this body lets the compiler hoist the (lane-dependent)
-    // address arithmetic of every unrolled LDS access out of it and keep it
-    // live across iterations, which costs hundreds of registers.
+    // One value head per call of `head`. Around a loop (the item loop, or the
+    // GQA group's heads) the compiler would hoist the lane- and wave-dependent
+    // address arithmetic of every unrolled LDS access out of the body and keep
+    // it live across iterations, which costs hundreds of registers: the body
+    // derives its thread, lane and wave indices from opaque values instead.
     auto head = [&](const int j, const int hk, const int gi, const ChunkEntry ce, const bool first,
                     auto&& at_epilogue) __attribute__((always_inline)) {
         const int l = opaque_lane_id();  // fresh per head: see above
