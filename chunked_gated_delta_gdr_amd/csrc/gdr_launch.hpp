@@ -11,7 +11,10 @@ namespace gdr {
 // first kernel and after each of the four kernels.
 using LaunchFn = hipError_t (*)(const Params&, hipStream_t, hipEvent_t const* ev);
 
-constexpr int kSweepBV = 32;  // V columns of the state per sweep workgroup
+// V columns of the state per sweep workgroup: 32 when both directions run
+// (2 N H D / 32 workgroups), 16 for one direction at C = 64, so that a single
+// sweep still has a workgroup on every CU (each one moving fewer bytes per step)
+constexpr int kSweepBV = 32, kSweepBV1 = 16;
 
 // Compute units of the current device (queried once per device).
 inline int compute_units() {
@@ -46,7 +49,13 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
                                     dim3(128 * (C / 16)), 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(2);
-    gdr_sweep<T, C, D, kSweepBV><<<dim3(p.dirs * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
+    bool narrow = false;
+    if constexpr (C == 64) {
+        narrow = p.dirs == 1;
+        if (narrow) gdr_sweep<T, C, D, kSweepBV1><<<dim3(p.N * p.H * (D / kSweepBV1)), dim3(256), 0, stream>>>(p);
+    }
+    if (!narrow)
+        gdr_sweep<T, C, D, kSweepBV><<<dim3(p.dirs * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(3);
     return e;
 }
