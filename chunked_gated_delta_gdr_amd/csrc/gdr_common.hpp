@@ -154,9 +154,8 @@ __device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda,
     }
 }
 
-// Row-panel products with one operand already in registers (fragments of a
-// C-long reduction): A rows (a[k] for reduction step k) against Bt in memory,
-// or A in memory against Bt fragments b[t][k] of the NT column tiles.
+// Row-panel product with the A operand already in registers (fragments of a
+// C-long reduction): A rows (a[k] for reduction step k) against Bt in memory.
 template <typename T, int NT, int NK>
 __device__ __forceinline__ void panel_mma_ra(f32x4 (&acc)[NT], const typename Mfma<T>::frag (&a)[NK],
                                              const T* Bt, int ldb, int j0, int l) {
@@ -165,28 +164,6 @@ __device__ __forceinline__ void panel_mma_ra(f32x4 (&acc)[NT], const typename Mf
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a[k], frag_kc(Bt, ldb, j0 + 16 * t, k * kstep<T>(), l), acc[t]);
 }
-template <typename T, int NT, int NK>
-__device__ __forceinline__ void panel_mma_rb(f32x4 (&acc)[NT], const T* A, int lda, int i0,
-                                             const typename Mfma<T>::frag (&b)[NT][NK], int l) {
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        const auto a = frag_kc(A, lda, i0, k * kstep<T>(), l);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, b[t][k], acc[t]);
-    }
-}
-
-// Same with a run-time reduction length kd (a multiple of kstep<T>()).
-template <typename T, int NT>
-__device__ __forceinline__ void panel_mma_n(f32x4 (&acc)[NT], const T* A, int lda, int i0,
-                                            const T* Bt, int ldb, int j0, int kd, int l = lane_id()) {
-    for (int k0 = 0; k0 < kd; k0 += kstep<T>()) {
-        auto a = frag_kc(A, lda, i0, k0, l);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0, l), acc[t]);
-    }
-}
-
 // fp32 16x16 tile product on fp32 arrays, reduction length kd (multiple of 4):
 // acc += A[(ai0+i)*lda + ak0 + kk] * B[(bk0+kk)*ldb + bj0 + j].
 __device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* A, int lda, int ai0, int ak0,
@@ -198,17 +175,6 @@ __device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* A, int lda, in
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
     return acc;
-}
-
-// Value idx (0..255) of a 256-float block spread over a wave as lane L ->
-// entries 4L..4L+3, read into a scalar register with v_readlane; idx must be
-// a compile-time constant after unrolling.
-// (The element is picked with an explicit select: indexing the vector inside
-// the readlane argument returned wrong values for elements 1..3 on the device.)
-__device__ __forceinline__ float lane_value(f32x4 v, int idx) {
-    const int j = idx & 3;
-    const float x = j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), idx >> 2));
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
