@@ -12,15 +12,17 @@
 // same recurrence ("dS0 = g_last * dSt", "dS0 += K^T @ dVg", "dS0 += Q^T @
 // dOg"). Columns of the state never mix (Diag acts on K, every product keeps
 // the column), so a V tile per workgroup is exact. dh0 = dh_0 is written in
-// fp32. The two directions are independent and share one grid.
+// fp32. The two directions are independent and share one grid (a pass that
+// needs one direction launches only that one).
 //
 // The per-chunk operands (w, k~, u, q~, 2^G_last) are read straight from
-// global memory as MFMA fragments of the rows each wave owns, NPF chunks
-// ahead into NPF fixed register sets (the chunk loop is unrolled NPF times so
-// that no register copy forces an early wait on a load in flight). Only the
-// state and X / T (and do for the reverse direction) pass through LDS,
-// double-buffered, two barriers per chunk; the stores of h_c and X_c (T_c) to
-// the workspace read those LDS tiles back as 16-byte row pieces.
+// global memory as MFMA fragments of the rows each wave owns (stored in
+// fragment / accumulator order, so each is one contiguous wave load), NPF
+// chunks ahead into NPF fixed register sets (the chunk loop is unrolled NPF
+// times so that no register copy forces an early wait on a load in flight).
+// Only the state and X / T (and do for the reverse direction) pass through
+// LDS, double-buffered, two barriers per chunk; the stores of h_c and X_c
+// (T_c) to the workspace read those LDS tiles back as 16-byte row pieces.
 #pragma once
 #include "gdr_common.hpp"
 
