@@ -236,8 +236,10 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             pdh[i] = ld16(dhb + (size_t)v0 * D + d * BVS + c);
         }
     };
-    auto request_head = [&](const ChunkEntry& e2, const int j2, const int h2, const int tid,
-                            const int l) __attribute__((always_inline)) {
+    // (tid, l, rows: the caller's thread, lane and first row of the wave; the
+    // persistent kernel passes its per-item opaque ones, see `head`)
+    auto request_head = [&](const ChunkEntry& e2, const int j2, const int h2, const int tid, const int l,
+                            const int rows) __attribute__((always_inline)) {
         const size_t jh2 = (size_t)j2 * p.H + h2;
         const T* Am = static_cast<const T*>(p.Am) + jh2 * C * C;
         const T* AT = static_cast<const T*>(p.AT) + jh2 * C * C;
@@ -250,8 +252,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
 #pragma unroll
         for (int k2 = 0; k2 < NKC; ++k2) {
-            fAq[k2] = frag_fo<T, C>(sAqkT, r0, k2 * KS, l);   // both in fragment order
-            fAT[k2] = frag_fo<T, C>(AT, r0, k2 * KS, l);
+            fAq[k2] = frag_fo<T, C>(sAqkT, rows, k2 * KS, l);   // both in fragment order
+            fAT[k2] = frag_fo<T, C>(AT, rows, k2 * KS, l);
         }
         request_slice(e2, jh2, h2, 0, tid);
 #pragma unroll
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
 
         // ================= epilogue (accumulator layout) =================
-        at_epilogue(tid, l);   // the next item's first requests (persistent kernel)
+        at_epilogue(tid, l, r0);   // the next item's first requests (persistent kernel)
         {
             const int l = opaque_lane_id();
             // db: row sums of the partials over this wave's column half
@@ -908,12 +910,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         if (j >= p.seq_off[p.N]) return;
         const ChunkEntry ce = p.ctab[j];
         const int tok0 = ce.tok0, len = ce.len, tid = threadIdx.x, l = lane_id();
-        auto none = [](int, int) {};
+        auto none = [](int, int, int) {};
         request_qk(ce, hk, tid);
-        request_head(ce, j, hk * p.G, tid, l);
+        request_head(ce, j, hk * p.G, tid, l, r0);
         head(j, hk, 0, ce, true, none);
         for (int gi = 1; gi < p.G; ++gi) {
-            request_head(ce, j, hk * p.G + gi, tid, l);
+            request_head(ce, j, hk * p.G + gi, tid, l, r0);
             head(j, hk, gi, ce, false, none);
         }
         // dq, dk group sums: staged in LDS, stored row-contiguous
@@ -941,14 +943,14 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         if (item >= nit) return;
         ChunkEntry ce = p.ctab[item / p.Hg];
         request_qk(ce, item % p.Hg, threadIdx.x);
-        request_head(ce, item / p.Hg, item % p.Hg, threadIdx.x, lane_id());
+        request_head(ce, item / p.Hg, item % p.Hg, threadIdx.x, lane_id(), r0);
 #pragma unroll 1
         for (; item < nit; item += gridDim.x) {
             const int nxt = min(item + (int)gridDim.x, nit - 1);
             const ChunkEntry ce_n = p.ctab[nxt / p.Hg];
-            head(item / p.Hg, item % p.Hg, 0, ce, true, [&](const int tid, const int l) __attribute__((always_inline)) {
+            head(item / p.Hg, item % p.Hg, 0, ce, true, [&](const int tid, const int l, const int rows) __attribute__((always_inline)) {
                 request_qk(ce_n, nxt % p.Hg, tid);
-                request_head(ce_n, nxt / p.Hg, nxt % p.Hg, tid, l);
+                request_head(ce_n, nxt / p.Hg, nxt % p.Hg, tid, l, rows);
             });
             ce = ce_n;
         }
