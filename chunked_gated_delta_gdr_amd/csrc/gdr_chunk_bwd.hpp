@@ -137,12 +137,22 @@ template <typename T, int C, int D, int NT>
 __device__ __forceinline__ void store_rows(const Params& p, const T* dqS, const T* dkS, int tok0, int len,
                                            int hk, int tid) {
     constexpr int V8 = 16 / sizeof(T), LT = D + pad<T>();
-    for (int e = tid; e < C * (D / V8); e += NT) {
-        const int r = e / (D / V8), c = (e % (D / V8)) * V8;
+    constexpr int NS = C * (D / V8) / NT;   // pieces per thread: all read first, one LDS wait
+    static_assert(NS * NT == C * (D / V8), "row piece split");
+    Vec16 a[NS], b[NS];
+#pragma unroll
+    for (int it = 0; it < NS; ++it) {
+        const int e = tid + it * NT, r = e / (D / V8), c = (e % (D / V8)) * V8;
+        a[it] = ld16(dqS + r * LT + c);
+        b[it] = ld16(dkS + r * LT + c);
+    }
+#pragma unroll
+    for (int it = 0; it < NS; ++it) {
+        const int e = tid + it * NT, r = e / (D / V8), c = (e % (D / V8)) * V8;
         if (r < len) {
             const size_t o = ((size_t)(tok0 + r) * p.Hg + hk) * D + c;
-            st16(static_cast<T*>(p.dq) + o, ld16(dqS + r * LT + c));
-            st16(static_cast<T*>(p.dk) + o, ld16(dkS + r * LT + c));
+            st16(static_cast<T*>(p.dq) + o, a[it]);
+            st16(static_cast<T*>(p.dk) + o, b[it]);
         }
     }
 }
@@ -459,9 +469,18 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         // dv rows to the output, 16 bytes per access
         {
             T* dvout = static_cast<T*>(p.dv) + ((size_t)tok0 * p.H + h) * D;
-            for (int e = tid; e < C * (D / V8); e += NT) {
-                const int r = e / (D / V8), c = (e % (D / V8)) * V8;
-                if (r < len) st16(dvout + (size_t)r * ldo + c, ld16(dvS + r * LT + c));
+            constexpr int NS = C * (D / V8) / NT;   // pieces per thread, read first
+            static_assert(NS * NT == C * (D / V8), "row piece split");
+            Vec16 a[NS];
+#pragma unroll
+            for (int it = 0; it < NS; ++it) {
+                const int e = tid + it * NT, r = e / (D / V8), c = (e % (D / V8)) * V8;
+                a[it] = ld16(dvS + r * LT + c);
+            }
+#pragma unroll
+            for (int it = 0; it < NS; ++it) {
+                const int e = tid + it * NT, r = e / (D / V8), c = (e % (D / V8)) * V8;
+                if (r < len) st16(dvout + (size_t)r * ldo + c, a[it]);
             }
         }
         // 2a: G = chunk-local inclusive cumsum of g, one column and NT/D row
@@ -593,26 +612,43 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         T* const qE0 = kE0 + 2 * DH2 * LC;                    // [2][DH2][LC] q_r Ein_r
         T* const bkE0 = qE0 + 2 * DH2 * LC;                   // [2][DH2][LC] beta_r k_r Ein_r
         __syncthreads();  // dA written
-        for (int e = tid; e < D * (C / 4); e += NT) {
-            const int d = e % D, s0 = (e / D) * 4;
-            const int b0 = s0 & ~15;
-            const int nb = b0 + 16 < C ? b0 + 16 : C - 1;  // Eout reference (last block: its last row)
-            const float Gb = Gs[b0 * LF + d], Gn = Gs[nb * LF + d];
-            float ke[4], qe[4], bke[4];
+        {   // all LDS reads of the thread's pieces first (one wait), then the
+            // products and the transposed writes
+            constexpr int NF = D * (C / 4) / NT;
+            static_assert(NF * NT == D * (C / 4), "fill split");
+            float Gv[NF][4], Gb[NF], Gn[NF], kv[NF][4], qv2[NF][4], bv[NF][4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int s = s0 + jj;
-                const float G = Gs[s * LF + d];
-                const float kv = to_f32(kL[s * LT + d]);
-                const float ein = fast_exp2(G - Gb);
-                ke[jj] = kv * fast_exp2(Gn - G);
-                qe[jj] = to_f32(qL[s * LT + d]) * ein;
-                bke[jj] = bs[s] * kv * ein;
+            for (int it = 0; it < NF; ++it) {
+                const int e = tid + it * NT, d = e % D, s0 = (e / D) * 4;
+                const int b0 = s0 & ~15;
+                const int nb = b0 + 16 < C ? b0 + 16 : C - 1;  // Eout reference (last block: its last row)
+                Gb[it] = Gs[b0 * LF + d];
+                Gn[it] = Gs[nb * LF + d];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int s = s0 + jj;
+                    Gv[it][jj] = Gs[s * LF + d];
+                    kv[it][jj] = to_f32(kL[s * LT + d]);
+                    qv2[it][jj] = to_f32(qL[s * LT + d]);
+                    bv[it][jj] = bs[s];
+                }
             }
-            const int o = ((d / DH2) * DH2 + d % DH2) * LC + s0;
-            store4<T>(kE0 + o, ke[0], ke[1], ke[2], ke[3]);
-            store4<T>(qE0 + o, qe[0], qe[1], qe[2], qe[3]);
-            store4<T>(bkE0 + o, bke[0], bke[1], bke[2], bke[3]);
+#pragma unroll
+            for (int it = 0; it < NF; ++it) {
+                const int e = tid + it * NT, d = e % D, s0 = (e / D) * 4;
+                float ke[4], qe[4], bke[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float ein = fast_exp2(Gv[it][jj] - Gb[it]);
+                    ke[jj] = kv[it][jj] * fast_exp2(Gn[it] - Gv[it][jj]);
+                    qe[jj] = qv2[it][jj] * ein;
+                    bke[jj] = bv[it][jj] * kv[it][jj] * ein;
+                }
+                const int o = ((d / DH2) * DH2 + d % DH2) * LC + s0;
+                store4<T>(kE0 + o, ke[0], ke[1], ke[2], ke[3]);
+                store4<T>(qE0 + o, qe[0], qe[1], qe[2], qe[3]);
+                store4<T>(bkE0 + o, bke[0], bke[1], bke[2], bke[3]);
+            }
         }
         __syncthreads();
         // each wave runs its half once, at hf == ch (the loop keeps the compiler
@@ -890,11 +926,18 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             __syncthreads();
             if constexpr (!GROUPED) store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
             if constexpr (!SCALAR) {
-                for (int e = tid; e < C * (D / 4); e += NT) {
-                    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-                    if (r < len)
-                        *reinterpret_cast<f32x4*>(p.dg + ((size_t)(tok0 + r) * p.H + h) * D + c) =
-                            *reinterpret_cast<const f32x4*>(dgS + r * LF + c);
+                constexpr int NS = C * (D / 4) / NT;   // pieces per thread, read first
+                static_assert(NS * NT == C * (D / 4), "row piece split");
+                f32x4 a[NS];
+#pragma unroll
+                for (int it = 0; it < NS; ++it) {
+                    const int e = tid + it * NT, r = e / (D / 4), c = (e % (D / 4)) * 4;
+                    a[it] = *reinterpret_cast<const f32x4*>(dgS + r * LF + c);
+                }
+#pragma unroll
+                for (int it = 0; it < NS; ++it) {
+                    const int e = tid + it * NT, r = e / (D / 4), c = (e % (D / 4)) * 4;
+                    if (r < len) *reinterpret_cast<f32x4*>(p.dg + ((size_t)(tok0 + r) * p.H + h) * D + c) = a[it];
                 }
             }
         }
