@@ -511,34 +511,50 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
         __syncthreads();
 
-        // 2b: post-factors, dw -> LDS
+        // 2b: post-factors, dw -> LDS. The LDS reads of the wave's rows (G, q,
+        // k, beta) come first, in one batch; 2^G and k are kept for 2c.
         T* dwT = reinterpret_cast<T*>(U + L::P2_DWT);
         T* dwL = reinterpret_cast<T*>(U + L::P2_DWL);
         f32x4 Pq[NTD], Pk[NTD], PG[NTD];
+        float eG[NTD][4], kvr[NTD][4], bsr[4];
+        {
+            float Gv[NTD][4], gls[NTD], qvr[NTD][4];
 #pragma unroll
-        for (int t = 0; t < NTD; ++t) {
-            const int c = cd0 + 16 * t + acc_col(l);
-            const float gls = Gs[(C - 1) * LF + c];
-            float colk = 0.f;
+            for (int t = 0; t < NTD; ++t) {
+                const int c = cd0 + 16 * t + acc_col(l);
+                gls[t] = Gs[(C - 1) * LF + c];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = r0 + acc_row(i, l);
-                const float G = Gs[r * LF + c];
-                const float dqi = p.scale * dqh[t][i] * fast_exp2(G);
-                const float dki = dkt_[t][i] * fast_exp2(gls - G);
-                const float qv = to_f32(qL[r * LT + c]), kv = to_f32(kL[r * LT + c]);
-                Pq[t][i] = dqi;
-                Pk[t][i] = dki;
-                PG[t][i] = kLn2 * (qv * dqi - kv * dki);
-                colk += kv * dki;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = r0 + acc_row(i, l);
+                    Gv[t][i] = Gs[r * LF + c];
+                    qvr[t][i] = to_f32(qL[r * LT + c]);
+                    kvr[t][i] = to_f32(kL[r * LT + c]);
+                }
             }
-            // sum over the 16 rows of this wave (4 in-lane, 4 lane groups)
-            colk = cross_row_sum(colk);
-            if (l < 16) dGlw[rb * D + c] = kLn2 * colk;  // summed in block order later
-            const int rr = r0 + acc_row(0, l);
-            store4<T>(dwT + c * LC + rr, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dwL[(rr + i) * LT + c] = from_f32<T>(-dwP[t][i]);
+            for (int i = 0; i < 4; ++i) bsr[i] = bs[r0 + acc_row(i, l)];
+#pragma unroll
+            for (int t = 0; t < NTD; ++t) {
+                const int c = cd0 + 16 * t + acc_col(l);
+                float colk = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    eG[t][i] = fast_exp2(Gv[t][i]);
+                    const float dqi = p.scale * dqh[t][i] * eG[t][i];
+                    const float dki = dkt_[t][i] * fast_exp2(gls[t] - Gv[t][i]);
+                    Pq[t][i] = dqi;
+                    Pk[t][i] = dki;
+                    PG[t][i] = kLn2 * (qvr[t][i] * dqi - kvr[t][i] * dki);
+                    colk += kvr[t][i] * dki;
+                }
+                // sum over the 16 rows of this wave (4 in-lane, 4 lane groups)
+                colk = cross_row_sum(colk);
+                if (l < 16) dGlw[rb * D + c] = kLn2 * colk;  // summed in block order later
+                const int rr = r0 + acc_row(0, l);
+                store4<T>(dwT + c * LC + rr, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dwL[(rr + i) * LT + c] = from_f32<T>(-dwP[t][i]);
+            }
         }
         __syncthreads();
         // 2c: dk^ = A^T dw ; dA' += dw (k 2^G)^T
@@ -549,14 +565,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
             panel_mma_ra<T, NTD, NKC>(dkh, fAT, dwT, LC, cd0, l);
 #pragma unroll
             for (int t = 0; t < NTD; ++t) {
-                const int c = cd0 + 16 * t + acc_col(l);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + acc_row(i, l);
-                    const float gam = fast_exp2(Gs[r * LF + c]);
-                    const float kgv = to_f32(kL[r * LT + c]) * gam;
-                    Pk[t][i] += bs[r] * gam * dkh[t][i];
-                    PG[t][i] += kLn2 * bs[r] * kgv * dkh[t][i];
+                    const float gam = eG[t][i];
+                    const float kgv = kvr[t][i] * gam;
+                    Pk[t][i] += bsr[i] * gam * dkh[t][i];
+                    PG[t][i] += kLn2 * bsr[i] * kgv * dkh[t][i];
                     dbp[i] += dkh[t][i] * kgv;
                 }
             }
@@ -848,7 +862,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
         }
 
         // ================= epilogue (accumulator layout) =================
-        at_epilogue(tid, l, r0);   // the next item's first requests (persistent kernel)
+        {   // the next item's first requests (persistent kernel), addressed from
+            // fresh opaque thread and lane indices, so that no address part is
+            // shared with this item's own requests and kept live until here
+            const int t2 = [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }();
+            at_epilogue(t2, opaque_lane_id(), r0);
+        }
         {
             const int l = opaque_lane_id();
             // db: row sums of the partials over this wave's column half
