@@ -54,28 +54,50 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_fwd_out(Params p) {
     const T* gu = static_cast<const T*>(p.uT) + jh * D * C;
     const T* gh = static_cast<const T*>(p.hbuf) + jh * D * D;   // [D/kTileV][D][kTileV]
 
-    for (int e = tid; e < D * (C / V8); e += NT) {
-        const int d = e / (C / V8), c = (e % (C / V8)) * V8;
-        st16(qsL + d * LC + c, ld16(gq + fo_index<T, C>(d, c)));   // fragment order
+    // every global load of the thread's pieces goes out before the first LDS
+    // write (constant trip counts, unrolled), so the loads overlap
+    constexpr int NQ = D * (C / V8) / NT, NA = C * (C / V8) / NT, NH = D * (D / V8) / NT;
+    static_assert(NQ * NT == D * (C / V8) && NA * NT == C * (C / V8) && NH * NT == D * (D / V8), "piece split");
+    Vec16 qv[NQ], uv[NQ], av[NA], hv[NH];
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+        const int e = tid + it * NT, d = e / (C / V8), c = (e % (C / V8)) * V8;
+        qv[it] = ld16(gq + fo_index<T, C>(d, c));   // fragment order
         // u^T in accumulator order: a 16-byte row piece is 4-element quads
-        Vec16 uv;
         if constexpr (sizeof(T) == 2) {
-            uv.w[0] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c))[0];
-            uv.w[1] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c))[1];
-            uv.w[2] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c + 4))[0];
-            uv.w[3] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c + 4))[1];
+            uv[it].w[0] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c))[0];
+            uv[it].w[1] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c))[1];
+            uv[it].w[2] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c + 4))[0];
+            uv[it].w[3] = reinterpret_cast<const unsigned*>(gu + ao_index<C>(d, c + 4))[1];
         } else {
-            uv = ld16(gu + ao_index<C>(d, c));
+            uv[it] = ld16(gu + ao_index<C>(d, c));
         }
-        st16(uL + d * LC + c, uv);
     }
-    for (int e = tid; e < C * (C / V8); e += NT) {
-        const int r = e / (C / V8), c = (e % (C / V8)) * V8;
-        st16(saL + r * LC + c, ld16(ga + fo_index<T, C>(r, c)));   // fragment order
+#pragma unroll
+    for (int it = 0; it < NA; ++it) {
+        const int e = tid + it * NT, r = e / (C / V8), c = (e % (C / V8)) * V8;
+        av[it] = ld16(ga + fo_index<T, C>(r, c));   // fragment order
     }
-    for (int e = tid; e < D * (D / V8); e += NT) {   // contiguous in the tiled layout
-        const int vt = e / (D * PT), rem = e % (D * PT), d = rem / PT, c = (rem % PT) * V8;
-        st16(hL + d * LH + vt * kTileV + c, ld16(gh + (size_t)vt * D * kTileV + d * kTileV + c));
+#pragma unroll
+    for (int it = 0; it < NH; ++it) {   // contiguous in the tiled layout
+        const int e = tid + it * NT, vt = e / (D * PT), rem = e % (D * PT), d = rem / PT, c = (rem % PT) * V8;
+        hv[it] = ld16(gh + (size_t)vt * D * kTileV + d * kTileV + c);
+    }
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+        const int e = tid + it * NT, d = e / (C / V8), c = (e % (C / V8)) * V8;
+        st16(qsL + d * LC + c, qv[it]);
+        st16(uL + d * LC + c, uv[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < NA; ++it) {
+        const int e = tid + it * NT, r = e / (C / V8), c = (e % (C / V8)) * V8;
+        st16(saL + r * LC + c, av[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < NH; ++it) {
+        const int e = tid + it * NT, vt = e / (D * PT), rem = e % (D * PT), d = rem / PT, c = (rem % PT) * V8;
+        st16(hL + d * LH + vt * kTileV + c, hv[it]);
     }
     __syncthreads();
 
@@ -103,8 +125,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void gdr_fwd_out(Params p) {
         for (int i = 0; i < 4; ++i) oS[(r0 + acc_row(i, l)) * LH + 16 * t + acc_col(l)] = from_f32<T>(acc[t][i]);
     __syncthreads();
     T* go = static_cast<T*>(p.o) + ((size_t)ce.tok0 * p.H + h) * D;
-    for (int e = tid; e < C * (D / V8); e += NT) {
-        const int r = e / (D / V8), c = (e % (D / V8)) * V8;
+    constexpr int NO = C * (D / V8) / NT;
+    static_assert(NO * NT == C * (D / V8), "piece split");
+#pragma unroll
+    for (int it = 0; it < NO; ++it) {
+        const int e = tid + it * NT, r = e / (D / V8), c = (e % (D / V8)) * V8;
         if (r < ce.len) st16(go + (size_t)r * p.H * D + c, ld16(oS + r * LH + c));
     }
 }

@@ -482,13 +482,22 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     }
     // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^): 8 consecutive s per item
     T* khT = Xb;  // [D][LC]
-    for (int e = tid; e < D * (C / 8); e += NT) {
-        const int d = e % D, s0 = (e / D) * 8;   // d fastest: row reads and 16-byte column writes without bank conflicts
-        float x[8];
+    {   // all LDS reads of the thread's pieces first (one wait), then the writes
+        constexpr int NP = D * (C / 8) / NT;
+        static_assert(NP * NT == D * (C / 8), "piece split");
+        float x[NP][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            x[i] = bs[s0 + i] * to_f32(kL[(s0 + i) * LT + d]) * fast_exp2(Gs[(s0 + i) * LF + d]);
-        store8<T>(khT + d * LC + s0, x);
+        for (int it = 0; it < NP; ++it) {
+            const int e = tid + it * NT, d = e % D, s0 = (e / D) * 8;   // d fastest: row reads and 16-byte column writes without bank conflicts
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                x[it][i] = bs[s0 + i] * to_f32(kL[(s0 + i) * LT + d]) * fast_exp2(Gs[(s0 + i) * LF + d]);
+        }
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int e = tid + it * NT, d = e % D, s0 = (e / D) * 8;
+            store8<T>(khT + d * LC + s0, x[it]);
+        }
     }
     __syncthreads();
 
@@ -510,14 +519,18 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     {   // w^T rows out (16-byte pieces), w out through transposing LDS reads
         T* gw = static_cast<T*>(p.w) + jh * C * D;
         T* gwT = static_cast<T*>(p.wT) + jh * D * C;
-        for (int e = tid; e < D * (C / 8); e += NT) {
-            const int d = e / (C / 8), s0 = (e % (C / 8)) * 8;
+        // constant trip counts: unrolled, the LDS reads go out ahead of the stores
+        static_assert(D * (C / 8) % NT == 0, "piece split");
+#pragma unroll
+        for (int it = 0; it < D * (C / 8) / NT; ++it) {
+            const int e = tid + it * NT, d = e / (C / 8), s0 = (e % (C / 8)) * 8;
             float x[8];
             load8<T>(wTL + d * LC + s0, x);
             store8<T>(gwT + fo_index<T, C>(d, s0), x);
         }
-        for (int e = tid; e < C * (D / 8); e += NT) {
-            const int r = e % C, d0 = (e / C) * 8;   // r fastest: the transposed reads conflict-free
+#pragma unroll
+        for (int it = 0; it < C * (D / 8) / NT; ++it) {
+            const int e = tid + it * NT, r = e % C, d0 = (e / C) * 8;   // r fastest: the transposed reads conflict-free
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = to_f32(wTL[(d0 + i) * LC + r]);
@@ -573,7 +586,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     {
         T* gkt = static_cast<T*>(p.kt) + jh * C * D;
         T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
-        for (int e = tid; e < C * (D / 8); e += NT) {
+#pragma unroll
+        for (int it = 0; it < C * (D / 8) / NT; ++it) {
+            const int e = tid + it * NT;
             // 16-bit: row fastest, so the fragment-order stores are contiguous
             const int r = sizeof(T) == 2 ? e % C : e / (D / 8);
             const int d0 = sizeof(T) == 2 ? (e / C) * 8 : (e % (D / 8)) * 8;
@@ -585,8 +600,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
             store8<T>(gkt + fo_index<T, D>(r, d0), x);
         }
-        for (int e = tid; e < D * (C / 8); e += NT) {
-            const int d = e % D, r0b = (e / D) * 8;   // d fastest (bank-conflict free)
+#pragma unroll
+        for (int it = 0; it < D * (C / 8) / NT; ++it) {
+            const int e = tid + it * NT, d = e % D, r0b = (e / D) * 8;   // d fastest (bank-conflict free)
             const float gl = Gs[(C - 1) * LF + d];
             float x[8];
 #pragma unroll
