@@ -54,8 +54,12 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
         narrow = p.dirs == 1;
         if (narrow) gdr_sweep<T, C, D, kSweepBV1><<<dim3(p.N * p.H * (D / kSweepBV1)), dim3(256), 0, stream>>>(p);
     }
-    if (!narrow)
-        gdr_sweep<T, C, D, kSweepBV><<<dim3(p.dirs * p.N * p.H * (D / kSweepBV)), dim3(256), 0, stream>>>(p);
+    if (!narrow) {
+        // C = 32: 64-column V tiles (half the workgroups, each loading the chunk
+        // operands once for twice the columns)
+        constexpr int BVW = C == 32 ? 2 * kSweepBV : kSweepBV;
+        gdr_sweep<T, C, D, BVW><<<dim3(p.dirs * p.N * p.H * (D / BVW)), dim3(256), 0, stream>>>(p);
+    }
     if (e == hipSuccess) e = mark(3);
     return e;
 }

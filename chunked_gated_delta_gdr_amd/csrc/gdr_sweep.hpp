@@ -258,29 +258,27 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
             // the same data): a store on one path only would make the compiler's
             // memory-counter waits for the prefetched loads also wait for it.
             constexpr int NP = D * BV / V8;
-            // this V tile's columns of the stored tile of kTileV columns
-            T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D + (size_t)(v0 / kTileV) * kTileV * D +
-                    v0 % kTileV;
+            T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D;
 #pragma unroll
             for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
                 const int e = (int)(threadIdx.x + 256 * pi) % NP;
-                const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                const int d = e / (BV / V8), c = (e % (BV / V8)) * V8, cc = v0 + c;
                 Vec16 v;
                 T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
                 for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
-                st16(gS + (size_t)d * kTileV + c, v);
+                // column cc of the stored tiles of kTileV columns (a piece never straddles two)
+                st16(gS + (size_t)(cc / kTileV) * kTileV * D + (size_t)d * kTileV + cc % kTileV, v);
             }
         }
         {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
             // (unconditional stores, as above)
             constexpr int NP = C * BV / V8;
-            T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D + (size_t)(v0 / kTileV) * kTileV * C +
-                    v0 % kTileV;
+            T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D;
 #pragma unroll
             for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
                 const int e = (int)(threadIdx.x + 256 * pi) % NP;
-                const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                const int r = e / (BV / V8), c = (e % (BV / V8)) * V8, cc = v0 + c;
                 Vec16 v;
                 T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
@@ -288,7 +286,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                     const T x = sX[(c + q) * LX + r];
                     vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
                 }
-                st16(gX + (size_t)r * kTileV + c, v);
+                st16(gX + (size_t)(cc / kTileV) * kTileV * C + (size_t)r * kTileV + cc % kTileV, v);
             }
         }
     };
@@ -330,8 +328,9 @@ template <typename T, int C, int D, int BV>
 __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     constexpr int LS = D + pad<T>();
     constexpr int LX = C + pad<T>();
-    constexpr int NPF = 3;                           // chunks of operands in flight
-    static_assert(kTileV % BV == 0, "a sweep V tile lies within one stored tile of kTileV columns");
+    constexpr int NPF = C == 32 ? 2 : 3;             // chunks of operands in flight
+    static_assert(kTileV % BV == 0 || BV % kTileV == 0, "sweep V tiles and stored tiles nest");
+    static_assert(kTileV % (16 / sizeof(T)) == 0, "a 16-byte piece lies within one stored tile");
     __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
     __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
