@@ -163,8 +163,18 @@ __device__ __forceinline__ void store_rows(const Params& p, const T* dqS, const 
 template <typename T>
 constexpr float diag_guard() { return __is_same(T, _Float16) ? 8.f : 64.f; }
 
+// Workgroups of the preparation and gradient kernels one CU holds at once: at
+// C = 64 their LDS (about 157 KB) allows one; at C = 32 with 16-bit operands
+// (under 80 KB each) two, when the gradient kernel's four waves keep to 256
+// registers; fp32 operands at C = 32 need over 80 KB, so one.
+template <typename T, int C>
+constexpr int resident_per_cu() { return C == 32 && sizeof(T) == 2 ? 2 : 1; }
+
+// Waves per SIMD of the gradient kernel (caps its registers): its C / 8 waves
+// times the workgroups a CU holds, over 4 SIMDs.
 template <typename T, int C, int D, bool SCALAR, bool GROUPED>
-__global__ __launch_bounds__(128 * (C / 16)) void gdr_chunk_bwd(Params p) {
+__global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
+    C / 32 * resident_per_cu<T, C>(), C / 32 * resident_per_cu<T, C>()))) void gdr_chunk_bwd(Params p) {
     using L = BwdLds<T, C, D>;
     constexpr int NB = L::NB, NW = 2 * NB, NT = 64 * NW, BVS = L::BVS;
     constexpr int LT = L::LT, LC = L::LC, LB = L::LB, LF = L::LF;

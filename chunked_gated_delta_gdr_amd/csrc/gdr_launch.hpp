@@ -16,6 +16,7 @@ using LaunchFn = hipError_t (*)(const Params&, hipStream_t, hipEvent_t const* ev
 // sweep still has a workgroup on every CU (each one moving fewer bytes per step)
 constexpr int kSweepBV = 32, kSweepBV1 = 16;
 
+
 // Compute units of the current device (queried once per device).
 inline int compute_units() {
     static int cached[64] = {0};
@@ -43,10 +44,9 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     gdr_chunk_table<C><<<dim3(1), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(1);
     if (p.dir0 == 0 && p.nc_max > 0) {
-        // persistent: at most one workgroup per compute unit (its LDS allows no more)
-        const int items = p.nc_max * p.H;
-        gdr_prep<T, C, D, SCALAR><<<dim3(items < compute_units() ? items : compute_units()),
-                                    dim3(128 * (C / 16)), 0, stream>>>(p);
+        // persistent: as many workgroups as the CUs hold at once
+        const int items = p.nc_max * p.H, slots = compute_units() * resident_per_cu<T, C>();
+        gdr_prep<T, C, D, SCALAR><<<dim3(items < slots ? items : slots), dim3(128 * (C / 16)), 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(2);
     bool narrow = false;
@@ -73,10 +73,9 @@ hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
         const dim3 block(128 * (C / 16));
         if (p.G > 1) {
             gdr_chunk_bwd<T, C, D, SCALAR, true><<<dim3(p.nc_max, p.Hg), block, 0, stream>>>(p);
-        } else {   // persistent over (chunk, head) items, at most one workgroup per CU
-            const int items = p.nc_max * p.Hg;
-            gdr_chunk_bwd<T, C, D, SCALAR, false><<<dim3(items < compute_units() ? items : compute_units()),
-                                                     block, 0, stream>>>(p);
+        } else {   // persistent over (chunk, head) items, as many workgroups as the CUs hold
+            const int items = p.nc_max * p.Hg, slots = compute_units() * resident_per_cu<T, C>();
+            gdr_chunk_bwd<T, C, D, SCALAR, false><<<dim3(items < slots ? items : slots), block, 0, stream>>>(p);
         }
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[4], stream);
