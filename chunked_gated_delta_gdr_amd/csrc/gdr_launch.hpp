@@ -11,10 +11,11 @@ namespace gdr {
 // first kernel and after each of the four kernels.
 using LaunchFn = hipError_t (*)(const Params&, hipStream_t, hipEvent_t const* ev);
 
-// V columns of the state per sweep workgroup: 32 when both directions run
-// (2 N H D / 32 workgroups), 16 for one direction at C = 64, so that a single
-// sweep still has a workgroup on every CU (each one moving fewer bytes per step)
-constexpr int kSweepBV = 32, kSweepBV1 = 16;
+// V columns of the state per sweep workgroup (chosen per launch, below): 32;
+// 16 for one direction at C = 64, so that a single sweep still has a workgroup
+// on every CU (each one moving fewer bytes per step); 64 when there are enough
+// (sequence, head) pairs to fill the CUs twice over with 32-column tiles
+constexpr int kSweepBV = 32, kSweepBV1 = 16, kSweepBVW = 64;
 
 
 // Compute units of the current device (queried once per device).
@@ -49,16 +50,20 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
         gdr_prep<T, C, D, SCALAR><<<dim3(items < slots ? items : slots), dim3(128 * (C / 16)), 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(2);
-    bool narrow = false;
-    if constexpr (C == 64) {
-        narrow = p.dirs == 1;
-        if (narrow) gdr_sweep<T, C, D, kSweepBV1><<<dim3(p.N * p.H * (D / kSweepBV1)), dim3(256), 0, stream>>>(p);
-    }
-    if (!narrow) {
-        // C = 32: 64-column V tiles (half the workgroups, each loading the chunk
-        // operands once for twice the columns)
-        constexpr int BVW = C == 32 ? 2 * kSweepBV : kSweepBV;
-        gdr_sweep<T, C, D, BVW><<<dim3(p.dirs * p.N * p.H * (D / BVW)), dim3(256), 0, stream>>>(p);
+    // V tile of the sweep: 64 columns when 32-column tiles would need two or
+    // more rounds of the CUs (each workgroup then loads the chunk operands once
+    // for twice the columns); else 16 for a single direction at C = 64 (one
+    // round either way, fewer bytes per workgroup); else 32
+    const int tiles32 = p.dirs * p.N * p.H * (D / kSweepBV);
+    if (tiles32 >= 2 * compute_units()) {
+        gdr_sweep<T, C, D, kSweepBVW><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
+    } else {
+        bool narrow = false;
+        if constexpr (C == 64) {
+            narrow = p.dirs == 1;
+            if (narrow) gdr_sweep<T, C, D, kSweepBV1><<<dim3(p.N * p.H * (D / kSweepBV1)), dim3(256), 0, stream>>>(p);
+        }
+        if (!narrow) gdr_sweep<T, C, D, kSweepBV><<<dim3(tiles32), dim3(256), 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(3);
     return e;

@@ -108,6 +108,17 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
     }
 }
 
+// Offset of (row r, column v0 + c) in a matrix of R rows stored as tiles of
+// kTileV columns ([D / kTileV][R][kTileV]); a 16-byte piece never straddles
+// two tiles. A V tile of BV <= kTileV columns lies in one stored tile, whose
+// offset is then uniform over the workgroup.
+template <int R, int BV>
+__device__ __forceinline__ size_t tiled_index(int r, int v0, int c) {
+    if constexpr (BV <= kTileV) return (size_t)(v0 / kTileV) * kTileV * R + v0 % kTileV + (size_t)r * kTileV + c;
+    const int cc = v0 + c;
+    return (size_t)(cc / kTileV) * kTileV * R + (size_t)r * kTileV + cc % kTileV;
+}
+
 // One direction of the sweep for (sequence n, value head h, V tile at v0).
 template <typename T, int C, int D, int BV, int DIR, int NPF>
 __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS0, T* sS1, T* sX0, T* sX1, T* sDo0,
@@ -262,13 +273,12 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
             for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
                 const int e = (int)(threadIdx.x + 256 * pi) % NP;
-                const int d = e / (BV / V8), c = (e % (BV / V8)) * V8, cc = v0 + c;
+                const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
                 Vec16 v;
                 T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
                 for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
-                // column cc of the stored tiles of kTileV columns (a piece never straddles two)
-                st16(gS + (size_t)(cc / kTileV) * kTileV * D + (size_t)d * kTileV + cc % kTileV, v);
+                st16(gS + tiled_index<D, BV>(d, v0, c), v);
             }
         }
         {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
@@ -278,7 +288,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
             for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
                 const int e = (int)(threadIdx.x + 256 * pi) % NP;
-                const int r = e / (BV / V8), c = (e % (BV / V8)) * V8, cc = v0 + c;
+                const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
                 Vec16 v;
                 T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
@@ -286,7 +296,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                     const T x = sX[(c + q) * LX + r];
                     vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
                 }
-                st16(gX + (size_t)(cc / kTileV) * kTileV * C + (size_t)r * kTileV + cc % kTileV, v);
+                st16(gX + tiled_index<C, BV>(r, v0, c), v);
             }
         }
     };
@@ -328,7 +338,7 @@ template <typename T, int C, int D, int BV>
 __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     constexpr int LS = D + pad<T>();
     constexpr int LX = C + pad<T>();
-    constexpr int NPF = C == 32 ? 2 : 3;             // chunks of operands in flight
+    constexpr int NPF = C == 32 || BV == 64 ? 2 : 3;   // chunks of operands in flight
     static_assert(kTileV % BV == 0 || BV % kTileV == 0, "sweep V tiles and stored tiles nest");
     static_assert(kTileV % (16 / sizeof(T)) == 0, "a 16-byte piece lies within one stored tile");
     __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];

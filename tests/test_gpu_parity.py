@@ -183,6 +183,36 @@ def test_linear_in_output_gradients():
         assert (r3[n].double() - comb).abs().max() <= 1e-4 * comb.abs().max(), n
 
 
+# Enough (sequence, head) pairs that the sweep takes 64-column V tiles (when
+# 2 N H D / 32 >= 2 x 256 CUs), at every (io, K, chunk) form; every element
+# compared, backward and forward.
+WIDE = {
+    "fp32_d64_c64": scaled(TINY, B=10, T=90, H=16, Hg=16, h0_std=0.1, dht_std=0.1, seed=21),
+    "fp32_d64_c32_gdn": scaled(TINY, B=10, T=70, H=16, Hg=8, chunk=32, gate="gdn", dht_std=0.1, seed=22),
+    "bf16_d64_c64": scaled(KDA16, B=10, T=100, H=16, Hg=16, K=64, V=64, dht_std=0.1, seed=23),
+    "bf16_d128_c64": scaled(KDA16, B=5, T=100, H=16, Hg=16, dht_std=0.1, seed=24),
+    "f16_d128_c32_gqa": scaled(GDN, B=5, T=70, H=16, Hg=8, h0_std=0.1, seed=25),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE))
+def test_wide_sweep_tiles(name):
+    w = WIDE[name]
+    assert 2 * w.B * w.H * (w.V // 32) >= 512
+    _check(tu.parity(w), tu.tolerance(w), name)
+    import chunked_gated_delta_gdr_amd as gdr
+    import oracle
+    inp = make_inputs(w)
+    t = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    o, ht = gdr.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], h0=t["h0"], scale=inp["scale"], chunk_size=w.chunk)
+    torch.cuda.synchronize()
+    r = oracle.run(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], None, inp["h0"], None, None,
+                   inp["scale"], w.gate, backward=False, forward_out=True)
+    for nm, g, ref in (("o", o.cpu().double().numpy(), r["o"]), ("ht", ht.cpu().double().numpy(), r["ht"])):
+        err = np.abs(g - ref).max() / np.abs(ref).max()
+        assert err <= tu.tolerance(w), f"{name}: forward {nm} {err}"
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled heads
 # ---------------------------------------------------------------------------
