@@ -164,15 +164,22 @@ __device__ __forceinline__ void panel_mma_ra(f32x4 (&acc)[NT], const typename Mf
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a[k], frag_kc(Bt, ldb, j0 + 16 * t, k * kstep<T>(), l), acc[t]);
 }
-// fp32 16x16 tile product on fp32 arrays, reduction length kd (multiple of 4):
+// fp32 16x16 tile product on fp32 arrays, reduction length kd (multiple of 16):
 // acc += A[(ai0+i)*lda + ak0 + kk] * B[(bk0+kk)*ldb + bj0 + j].
 __device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* A, int lda, int ai0, int ak0,
                                           const float* B, int ldb, int bk0, int bj0, int kd,
                                           int l = lane_id()) {
-    for (int k = 0; k < kd; k += 4) {
-        float a = A[(ai0 + (l & 15)) * lda + ak0 + k + (l >> 4)];
-        float b = B[(bk0 + k + (l >> 4)) * ldb + bj0 + (l & 15)];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    // kd is a multiple of 16: the 8 LDS reads of four steps go out together
+    for (int k0 = 0; k0 < kd; k0 += 16) {
+        float a[4], b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + 4 * j;
+            a[j] = A[(ai0 + (l & 15)) * lda + ak0 + k + (l >> 4)];
+            b[j] = B[(bk0 + k + (l >> 4)) * ldb + bj0 + (l & 15)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
     }
     return acc;
 }

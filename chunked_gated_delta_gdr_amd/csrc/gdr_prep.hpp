@@ -263,16 +263,22 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         static_assert(NT % D == 0 || NT < D, "cumsum split");
         float* segtot = scr;  // [NSEG][D]
         const int d = tid % D, sg = tid / D;
+        // the segment's SR values read at once and scanned in registers, kept
+        // there for the offset pass
+        float gv[SR];
         if (sg < NSEG) {
-            float s = 0.f;
-            for (int r = sg * SR; r < (sg + 1) * SR; ++r) { s += Gs[r * LF + d]; Gs[r * LF + d] = s; }
-            segtot[sg * D + d] = s;
+#pragma unroll
+            for (int i = 0; i < SR; ++i) gv[i] = Gs[(sg * SR + i) * LF + d];
+#pragma unroll
+            for (int i = 1; i < SR; ++i) gv[i] += gv[i - 1];
+            segtot[sg * D + d] = gv[SR - 1];
         }
         __syncthreads();
-        if (sg < NSEG && sg > 0) {
+        if (sg < NSEG) {
             float off = 0.f;
             for (int s2 = 0; s2 < sg; ++s2) off += segtot[s2 * D + d];
-            for (int r = sg * SR; r < (sg + 1) * SR; ++r) Gs[r * LF + d] += off;
+#pragma unroll
+            for (int i = 0; i < SR; ++i) Gs[(sg * SR + i) * LF + d] = gv[i] + off;
         }
         __syncthreads();
     }
@@ -294,13 +300,31 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             const int d0 = k0 + (l >> 4) * KL;
             F fa, fi;
             const T* arow = (is_kk ? kL : qL) + r * LT;
+            // the lane's KL consecutive elements of each row, one vector read per row
+            float gq[KL], gb[KL];
+            T ar[KL], kr[KL];
+            if constexpr (KL == 4) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gs + r * LF + d0);
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(Gs + b0 * LF + d0);
+                const uint2 a2 = *reinterpret_cast<const uint2*>(arow + d0);
+                const uint2 k2 = *reinterpret_cast<const uint2*>(kL + r * LT + d0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { gq[i] = g4[i]; gb[i] = b4[i]; }
+                __builtin_memcpy(ar, &a2, sizeof(a2));
+                __builtin_memcpy(kr, &k2, sizeof(k2));
+            } else {
+#pragma unroll
+                for (int i = 0; i < KL; ++i) {
+                    gq[i] = Gs[r * LF + d0 + i]; gb[i] = Gs[b0 * LF + d0 + i];
+                    ar[i] = arow[d0 + i]; kr[i] = kL[r * LT + d0 + i];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
-                const int d = d0 + i;
-                const float x = Gs[r * LF + d] - Gs[b0 * LF + d];
+                const float x = gq[i] - gb[i];
                 rmax = fmaxf(rmax, fabsf(x));
                 const float e = fast_exp2(x), ei = fast_exp2(fminf(-x, guard));
-                const float av = to_f32(arow[d]), kv = to_f32(kL[r * LT + d]);
+                const float av = to_f32(ar[i]), kv = to_f32(kr[i]);
                 if constexpr (KL == 1) {
                     fa = av * e; fi = kv * ei;
                 } else {
@@ -378,24 +402,34 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         T* qb = Xb;                 // [16][LT]  q_r 2^(G_r - G_rho), r in block ib
         T* kqb = Xb + 16 * LT;      // [16][LT]  k_r 2^(G_r - G_rho)
         T* kb = Xb + 32 * LT;       // [rho][LT] k_s 2^(G_rho - G_s), s < rho
-        for (int e = tid; e < (32 + rho) * (D / 8); e += NT) {
-            const int rr = e / (D / 8), d0 = (e % (D / 8)) * 8;
-            float gr[8], gx[8], x[8];
+        {   // every LDS read of the thread's pieces first (one wait), then the
+            // scaled rows; a thread's pieces share one column group (NT is a
+            // multiple of D / 8), so the boundary row's G is read once
+            static_assert(NT % (D / 8) == 0, "one column group per thread");
+            constexpr int NFP = ((32 + 16 * (NB - 1)) * (D / 8) + NT - 1) / NT;
+            const int np = (32 + rho) * (D / 8), d0 = (tid % (D / 8)) * 8;
+            struct Raw8 { T v[8]; };   // 8 elements as stored (16 or 32 bytes)
+            float gr[8], gx[NFP][8];
+            Raw8 xr[NFP];
             load8f(Gs + rho * LF + d0, gr);
-            if (rr < 32) {
-                const int r = rho + (rr & 15);
-                load8f(Gs + r * LF + d0, gx);
-                load8<T>((rr < 16 ? qL : kL) + r * LT + d0, x);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gx[i] - gr[i]);
-            } else {
-                const int s2 = rr - 32;
-                load8f(Gs + s2 * LF + d0, gx);
-                load8<T>(kL + s2 * LT + d0, x);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gr[i] - gx[i]);
+            for (int it = 0; it < NFP; ++it) {
+                const int rr = min(tid + it * NT, np - 1) / (D / 8);   // spare pieces: a valid duplicate
+                const int r = rr < 32 ? rho + (rr & 15) : rr - 32;
+                load8f(Gs + r * LF + d0, gx[it]);
+                xr[it] = *reinterpret_cast<const Raw8*>((rr < 16 ? qL : kL) + r * LT + d0);
             }
-            store8<T>(Xb + rr * LT + d0, x);
+#pragma unroll
+            for (int it = 0; it < NFP; ++it) {
+                const int e = tid + it * NT, rr = e / (D / 8);
+                if (e < np) {
+                    float x[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)   // exponents <= 0 on both sides of the boundary
+                        x[i] = to_f32(xr[it].v[i]) * fast_exp2(rr < 32 ? gx[it][i] - gr[i] : gr[i] - gx[it][i]);
+                    store8<T>(Xb + rr * LT + d0, x);
+                }
+            }
         }
         __syncthreads();
         // tiles: (which in {Aqk, Akk}) x (rho/16 column tiles)
