@@ -397,55 +397,74 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     __syncthreads();
 
     // ---- phase 3: off-diagonal blocks through the boundary rho = 16 i (MFMA) ----
-    for (int ib = 1; ib < NB; ++ib) {
-        const int rho = 16 * ib;
-        T* qb = Xb;                 // [16][LT]  q_r 2^(G_r - G_rho), r in block ib
-        T* kqb = Xb + 16 * LT;      // [16][LT]  k_r 2^(G_r - G_rho)
-        T* kb = Xb + 32 * LT;       // [rho][LT] k_s 2^(G_rho - G_s), s < rho
-        {   // every LDS read of the thread's pieces first (one wait), then the
-            // scaled rows; a thread's pieces share one column group (NT is a
-            // multiple of D / 8), so the boundary row's G is read once
-            static_assert(NT % (D / 8) == 0, "one column group per thread");
-            constexpr int NFP = ((32 + 16 * (NB - 1)) * (D / 8) + NT - 1) / NT;
-            const int np = (32 + rho) * (D / 8), d0 = (tid % (D / 8)) * 8;
+    // For boundary i: q_r 2^(G_r - G_rho) and k_r 2^(G_r - G_rho) of block i,
+    // k_s 2^(G_rho - G_s) of the rows s < rho, then the block products. Two
+    // boundaries share a pass (one fill, one product round, two barriers) when
+    // their rows fit the X region together.
+    {
+        constexpr int XROWS = int(L::X_BYTES / (size_t(LT) * sizeof(T)));
+        constexpr bool PAIR = NB == 4 && (32 + 16) + (32 + 32) <= XROWS;
+        auto pass = [&](auto nib_c, const int ib0) __attribute__((always_inline)) {
+            constexpr int NIB = decltype(nib_c)::value;
+            // rows of boundary ib0 + j start at base(j) in the X region
+            auto base = [&](int j) { return j == 0 ? 0 : 32 + 16 * ib0; };
+            const int rows = base(NIB - 1) + 32 + 16 * (ib0 + NIB - 1);
+            const int np = rows * (D / 8);
+            constexpr int MAXROWS = NIB == 2 ? (32 + 16) + (32 + 32) : 32 + 16 * (NB - 1);
+            constexpr int NFP = (MAXROWS * (D / 8) + NT - 1) / NT;
             struct Raw8 { T v[8]; };   // 8 elements as stored (16 or 32 bytes)
-            float gr[8], gx[NFP][8];
+            float grv[NFP][8], gx[NFP][8];
             Raw8 xr[NFP];
-            load8f(Gs + rho * LF + d0, gr);
+            // every LDS read of the thread's pieces first (one wait); spare
+            // pieces read a valid duplicate and store nothing
 #pragma unroll
             for (int it = 0; it < NFP; ++it) {
-                const int rr = min(tid + it * NT, np - 1) / (D / 8);   // spare pieces: a valid duplicate
+                const int e = min(tid + it * NT, np - 1), g = e / (D / 8), d0 = (e % (D / 8)) * 8;
+                const int j = NIB == 2 && g >= base(1) ? 1 : 0, rr = g - base(j), rho = 16 * (ib0 + j);
                 const int r = rr < 32 ? rho + (rr & 15) : rr - 32;
+                load8f(Gs + rho * LF + d0, grv[it]);
                 load8f(Gs + r * LF + d0, gx[it]);
                 xr[it] = *reinterpret_cast<const Raw8*>((rr < 16 ? qL : kL) + r * LT + d0);
             }
 #pragma unroll
             for (int it = 0; it < NFP; ++it) {
-                const int e = tid + it * NT, rr = e / (D / 8);
+                const int e = tid + it * NT, g = e / (D / 8), d0 = (e % (D / 8)) * 8;
+                const int j = NIB == 2 && g >= base(1) ? 1 : 0, rr = g - base(j);
                 if (e < np) {
                     float x[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i)   // exponents <= 0 on both sides of the boundary
-                        x[i] = to_f32(xr[it].v[i]) * fast_exp2(rr < 32 ? gx[it][i] - gr[i] : gr[i] - gx[it][i]);
-                    store8<T>(Xb + rr * LT + d0, x);
+                        x[i] = to_f32(xr[it].v[i]) *
+                               fast_exp2(rr < 32 ? gx[it][i] - grv[it][i] : grv[it][i] - gx[it][i]);
+                    store8<T>(Xb + g * LT + d0, x);
                 }
             }
-        }
-        __syncthreads();
-        // tiles: (which in {Aqk, Akk}) x (rho/16 column tiles)
-        const int ntile = 2 * ib;
-        for (int t = w; t < ntile; t += L::NW) {
-            const int which = t / ib, ct = t % ib;
-            f32x4 acc[1] = {zero4()};
-            panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct, l);
+            __syncthreads();
+            // tiles: per boundary ib, (which in {Aqk, Akk}) x (ib column tiles)
+            const int ntile = NIB == 2 ? 2 * ib0 + 2 * (ib0 + 1) : 2 * ib0;
+            for (int t = w; t < ntile; t += L::NW) {
+                const int j = NIB == 2 && t >= 2 * ib0 ? 1 : 0, tt = t - (j ? 2 * ib0 : 0), ib = ib0 + j;
+                const int which = tt / ib, ct = tt % ib, rho = 16 * ib;
+                const T* qb = Xb + base(j) * LT;   // [16][LT]  q_r 2^(G_r - G_rho), r in block ib
+                const T* kqb = qb + 16 * LT;       // [16][LT]  k_r 2^(G_r - G_rho)
+                const T* kb = qb + 32 * LT;        // [rho][LT] k_s 2^(G_rho - G_s), s < rho
+                f32x4 acc[1] = {zero4()};
+                panel_mma<T, 1, D>(acc, which ? kqb : qb, LT, 0, kb, LT, 16 * ct, l);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = rho + acc_row(i, l), s2 = 16 * ct + acc_col(l);
-                if (which) AkkF[r * LCF + s2] = bs[r] * acc[0][i];
-                else AqkF[r * LCF + s2] = acc[0][i];
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rho + acc_row(i, l), s2 = 16 * ct + acc_col(l);
+                    if (which) AkkF[r * LCF + s2] = bs[r] * acc[0][i];
+                    else AqkF[r * LCF + s2] = acc[0][i];
+                }
             }
+            __syncthreads();
+        };
+        if constexpr (PAIR) {
+            pass(std::integral_constant<int, 2>{}, 1);
+            pass(std::integral_constant<int, 1>{}, 3);
+        } else {
+            for (int ib = 1; ib < NB; ++ib) pass(std::integral_constant<int, 1>{}, ib);
         }
-        __syncthreads();
     }
 
     // ---- phase 4: A = (I + Akk)^-1 ----
