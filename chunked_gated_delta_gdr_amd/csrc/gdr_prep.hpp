@@ -396,6 +396,26 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     }
     __syncthreads();
 
+    // 4a (of the inverse below): the diagonal blocks of A = (I + Akk)^-1 by
+    // forward substitution, one column per lane (lanes 0..C-1 of the wave that
+    // calls it). It needs only the diagonal blocks of Akk, so the last wave runs
+    // it during the first product round of phase 3, where it has no tile.
+    auto diag_inverse = [&](const int lane) __attribute__((always_inline)) {
+        if (lane < C) {
+            const int m = lane >> 4, jj = lane & 15, b0 = 16 * m;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == jj) ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc -= AkkF[(b0 + r) * LCF + b0 + s2] * x[s2];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) AF[(b0 + r) * LCF + b0 + jj] = x[r];
+        }
+    };
+
     // ---- phase 3: off-diagonal blocks through the boundary rho = 16 i (MFMA) ----
     // For boundary i: q_r 2^(G_r - G_rho) and k_r 2^(G_r - G_rho) of block i,
     // k_s 2^(G_rho - G_s) of the rows s < rho, then the block products. Two
@@ -404,7 +424,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     {
         constexpr int XROWS = int(L::X_BYTES / (size_t(LT) * sizeof(T)));
         constexpr bool PAIR = NB == 4 && (32 + 16) + (32 + 32) <= XROWS;
-        auto pass = [&](auto nib_c, const int ib0) __attribute__((always_inline)) {
+        auto pass = [&](auto nib_c, const int ib0, const bool first) __attribute__((always_inline)) {
             constexpr int NIB = decltype(nib_c)::value;
             // rows of boundary ib0 + j start at base(j) in the X region
             auto base = [&](int j) { return j == 0 ? 0 : 32 + 16 * ib0; };
@@ -457,52 +477,47 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
                     else AqkF[r * LCF + s2] = acc[0][i];
                 }
             }
+            if (first && w == L::NW - 1) diag_inverse(tid - (NT - 64));
             __syncthreads();
         };
+        // the last wave has no tile in the first product round (at most
+        // 2 + 4 tiles there), which is where it inverts the diagonal blocks
+        static_assert(L::NW - 1 >= (PAIR ? 6 : 2), "a free wave in the first product round");
         if constexpr (PAIR) {
-            pass(std::integral_constant<int, 2>{}, 1);
-            pass(std::integral_constant<int, 1>{}, 3);
+            pass(std::integral_constant<int, 2>{}, 1, true);
+            pass(std::integral_constant<int, 1>{}, 3, false);
         } else {
-            for (int ib = 1; ib < NB; ++ib) pass(std::integral_constant<int, 1>{}, ib);
+            for (int ib = 1; ib < NB; ++ib) pass(std::integral_constant<int, 1>{}, ib, ib == 1);
         }
     }
 
-    // ---- phase 4: A = (I + Akk)^-1 ----
-    // 4a: diagonal blocks by forward substitution, one column per lane
-    if (tid < C) {
-        const int m = tid >> 4, jj = tid & 15, b0 = 16 * m;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == jj) ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < r; ++s2) acc -= AkkF[(b0 + r) * LCF + b0 + s2] * x[s2];
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) AF[(b0 + r) * LCF + b0 + jj] = x[r];
-    }
-    __syncthreads();
-    // 4b: block rows: A_ij = -A_ii * sum_{kb=j}^{i-1} L_i,kb A_kb,j  (fp32 MFMA)
-    for (int bi = 1; bi < NB; ++bi) {
+    // ---- phase 4: A = (I + Akk)^-1 (4a, the diagonal blocks, ran in phase 3) ----
+    // 4b: block rows: A_ij = -A_ii * sum_{kb=j}^{i-1} L_i,kb A_kb,j  (fp32 MFMA).
+    // Wave w < NB - 1 owns block column j = w and walks its rows i = j+1, ...
+    // in order; besides Akk and the diagonal blocks of A it reads only blocks
+    // of its own column, so only the wave's own LDS writes must be ordered (a
+    // wave-level fence) until the workgroup barrier at the end.
+    if (w < NB - 1) {
+        const int bj = w;
         float* sc = scr + w * 16 * 20;
-        if (w < bi) {
-            const int bj = w;
+        auto wave_fence = [] {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        };
+        for (int bi = bj + 1; bi < NB; ++bi) {
             f32x4 acc = zero4();
             acc = tile_f32(acc, AkkF, LCF, 16 * bi, 16 * bj, AF, LCF, 16 * bj, 16 * bj, 16 * (bi - bj), l);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sc[acc_row(i, l) * 20 + acc_col(l)] = acc[i];
-        }
-        __syncthreads();
-        if (w < bi) {
-            const int bj = w;
-            f32x4 acc = zero4();
+            wave_fence();   // sc written by all lanes before any lane reads it
+            acc = zero4();
             acc = tile_f32(acc, AF, LCF, 16 * bi, 16 * bi, sc, 20, 0, 0, 16, l);
 #pragma unroll
             for (int i = 0; i < 4; ++i) AF[(16 * bi + acc_row(i, l)) * LCF + 16 * bj + acc_col(l)] = -acc[i];
+            wave_fence();   // A_ij and the sc reads done before the next row reuses them
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- phase 5: A, A^T and scale Aqk^T to the workspace in 8-element row
     //      pieces; A and Aqk in place as MFMA operands in LDS ----
