@@ -684,6 +684,8 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             T* const qET = qE0 + ch * DH2 * LC;
             T* const bkET = bkE0 + ch * DH2 * LC;
             const int l = opaque_lane_id();  // see the head body
+            using F16 = typename Mfma16<T>::frag;
+            constexpr int ST = Mfma16<T>::STEPS;
             // G of this wave's rows and of its block's first row; the guard
             // also covers the next block's first row (the diagonal's Eout reference)
             float gr[NTD][4], grho[NTD];
@@ -707,21 +709,51 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 f32x4 aq[NTD], ak[NTD];
 #pragma unroll
                 for (int t = 0; t < NTD; ++t) { aq[t] = zero4(); ak[t] = zero4(); }
-                for (int b1 = 0; b1 < rb; ++b1) {
-                    if (b1 > 0) {
-#pragma unroll
-                        for (int t = 0; t < NTD; ++t) {
-                            const int c = cd0 + 16 * t + acc_col(l);
-                            const float ph = fast_exp2(Gs[16 * (b1 + 1) * LF + c] - Gs[16 * b1 * LF + c]);
-                            aq[t] *= ph;
-                            ak[t] *= ph;
-                        }
-                    }
+                // the operands of block b1 (the two G rows of its decay factor,
+                // the dAqk / dAkk fragments, the k Eout fragments) are read one
+                // block ahead, so each step waits only on reads issued a step
+                // earlier (the last read is a redundant valid one); with GQA,
+                // whose group sums hold more registers, at the top of the step
+                struct RowOps {
+                    float g1[NTD], g0[NTD];
+                    F16 fq[ST], fk[ST], fb[ST][NTD];
+                };
+                auto read_row = [&](RowOps& o, const int b1) __attribute__((always_inline)) {
 #pragma unroll
                     for (int t = 0; t < NTD; ++t) {
-                        aq[t] = mma16<T, false>(aq[t], dAqL, LC, r0, 16 * b1, kET, LC, 16 * t, 16 * b1, l);
-                        ak[t] = mma16<T, false>(ak[t], dAkL, LC, r0, 16 * b1, kET, LC, 16 * t, 16 * b1, l);
+                        const int c = cd0 + 16 * t + acc_col(l);
+                        o.g1[t] = Gs[16 * (b1 + 1) * LF + c];
+                        o.g0[t] = Gs[16 * b1 * LF + c];
                     }
+#pragma unroll
+                    for (int st = 0; st < ST; ++st) {
+                        o.fq[st] = frag16_kc(dAqL, LC, r0, 16 * b1, st, l);
+                        o.fk[st] = frag16_kc(dAkL, LC, r0, 16 * b1, st, l);
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) o.fb[st][t] = frag16_kc(kET, LC, 16 * t, 16 * b1, st, l);
+                    }
+                };
+                RowOps cur, nxt;
+                if constexpr (!GROUPED) {
+                    if (rb > 0) read_row(cur, 0);
+                }
+                for (int b1 = 0; b1 < rb; ++b1) {
+                    if constexpr (GROUPED) read_row(cur, b1);
+                    else read_row(nxt, b1 + 1 < rb ? b1 + 1 : b1);
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) {
+                        const float ph = fast_exp2(b1 > 0 ? cur.g1[t] - cur.g0[t] : 0.f);
+                        aq[t] *= ph;
+                        ak[t] *= ph;
+                    }
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t)
+#pragma unroll
+                        for (int st = 0; st < ST; ++st) {
+                            aq[t] = Mfma16<T>::mma(cur.fq[st], cur.fb[st][t], aq[t]);
+                            ak[t] = Mfma16<T>::mma(cur.fk[st], cur.fb[st][t], ak[t]);
+                        }
+                    if constexpr (!GROUPED) cur = nxt;
                 }
                 // reference of the sum: G_16rb for the cross part alone; with the
                 // diagonal on MFMA (sources k Eout, reference G_nb) the cross part
@@ -794,19 +826,46 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 f32x4 dk[NTD];
 #pragma unroll
                 for (int t = 0; t < NTD; ++t) dk[t] = zero4();
-                for (int b2 = NB - 1; b2 > rb; --b2) {
-                    if (b2 < NB - 1) {
-#pragma unroll
-                        for (int t = 0; t < NTD; ++t) {
-                            const int c = cd0 + 16 * t + acc_col(l);
-                            dk[t] *= fast_exp2(Gs[16 * (b2 + 1) * LF + c] - Gs[16 * b2 * LF + c]);
-                        }
-                    }
+                // operands one block ahead, as on the row side
+                struct ColOps {
+                    float g1[NTD], g0[NTD];
+                    F16 fq[ST], fk[ST], fbq[ST][NTD], fbk[ST][NTD];
+                };
+                auto read_col = [&](ColOps& o, const int b2) __attribute__((always_inline)) {
 #pragma unroll
                     for (int t = 0; t < NTD; ++t) {
-                        dk[t] = mma16<T, true>(dk[t], dAqL, LC, r0, 16 * b2, qET, LC, 16 * t, 16 * b2, l);
-                        dk[t] = mma16<T, true>(dk[t], dAkL, LC, r0, 16 * b2, bkET, LC, 16 * t, 16 * b2, l);
+                        const int c = cd0 + 16 * t + acc_col(l);
+                        o.g1[t] = Gs[(16 * (b2 + 1) < C ? 16 * (b2 + 1) : C - 1) * LF + c];
+                        o.g0[t] = Gs[16 * b2 * LF + c];
                     }
+#pragma unroll
+                    for (int st = 0; st < ST; ++st) {
+                        o.fq[st] = frag16_ks(dAqL, LC, r0, 16 * b2, st, l);
+                        o.fk[st] = frag16_ks(dAkL, LC, r0, 16 * b2, st, l);
+#pragma unroll
+                        for (int t = 0; t < NTD; ++t) {
+                            o.fbq[st][t] = frag16_kc(qET, LC, 16 * t, 16 * b2, st, l);
+                            o.fbk[st][t] = frag16_kc(bkET, LC, 16 * t, 16 * b2, st, l);
+                        }
+                    }
+                };
+                ColOps cur, nxt;
+                if constexpr (!GROUPED) {
+                    if (rb < NB - 1) read_col(cur, NB - 1);
+                }
+                for (int b2 = NB - 1; b2 > rb; --b2) {
+                    if constexpr (GROUPED) read_col(cur, b2);
+                    else read_col(nxt, b2 - 1 > rb ? b2 - 1 : b2);
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) dk[t] *= fast_exp2(b2 < NB - 1 ? cur.g1[t] - cur.g0[t] : 0.f);
+#pragma unroll
+                    for (int t = 0; t < NTD; ++t) {
+#pragma unroll
+                        for (int st = 0; st < ST; ++st) dk[t] = Mfma16<T>::mma(cur.fq[st], cur.fbq[st][t], dk[t]);
+#pragma unroll
+                        for (int st = 0; st < ST; ++st) dk[t] = Mfma16<T>::mma(cur.fk[st], cur.fbk[st][t], dk[t]);
+                    }
+                    if constexpr (!GROUPED) cur = nxt;
                 }
                 if (diag_mfma) {
                     if (rb < NB - 1) {
