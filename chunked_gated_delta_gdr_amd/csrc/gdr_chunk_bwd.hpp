@@ -508,15 +508,22 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 gl[jj] = run;
             }
             segt[sg * D + d] = run;
+            T kr[SR];   // the segment's k column, read before any write below
+#pragma unroll
+            for (int jj = 0; jj < SR; ++jj) kr[jj] = kL[(rs0 + jj) * LT + d];
             __syncthreads();
-            float off = 0.f;
-            for (int s2 = 0; s2 < sg; ++s2) off += segt[s2 * D + d];
+            float off = 0.f;   // all segment totals read (one wait), the earlier ones summed
+#pragma unroll
+            for (int s2 = 0; s2 < NSEG - 1; ++s2) {
+                const float x = segt[s2 * D + d];
+                off += s2 < sg ? x : 0.f;
+            }
 #pragma unroll
             for (int jj = 0; jj < SR; ++jj) {
                 const int r = rs0 + jj;
                 const float G = gl[jj] + off;
                 Gs[r * LF + d] = G;
-                kgL[r * LT + d] = from_f32<T>(to_f32(kL[r * LT + d]) * fast_exp2(G));
+                kgL[r * LT + d] = from_f32<T>(to_f32(kr[jj]) * fast_exp2(G));
             }
         }
         __syncthreads();
@@ -976,8 +983,12 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int t = 0; t < NTD; ++t) {
                 const int c = cd0 + 16 * t + acc_col(l);
-                float suf = 0.f;
-                for (int b2 = rb + 1; b2 < NB; ++b2) suf += btot[b2 * D + c];
+                float suf = 0.f;   // all NB totals read (one wait), the later blocks' summed
+#pragma unroll
+                for (int b2 = 1; b2 < NB; ++b2) {
+                    const float x = btot[b2 * D + c];
+                    suf += b2 > rb ? x : 0.f;
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) PG[t][i] += suf;
             }
