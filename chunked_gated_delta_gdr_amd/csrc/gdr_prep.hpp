@@ -275,8 +275,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         }
         __syncthreads();
         if (sg < NSEG) {
-            float off = 0.f;
-            for (int s2 = 0; s2 < sg; ++s2) off += segtot[s2 * D + d];
+            float off = 0.f;   // all segment totals read (one wait), the earlier ones summed
+#pragma unroll
+            for (int s2 = 0; s2 < NSEG - 1; ++s2) {
+                const float x = segtot[s2 * D + d];
+                off += s2 < sg ? x : 0.f;
+            }
 #pragma unroll
             for (int i = 0; i < SR; ++i) Gs[(sg * SR + i) * LF + d] = gv[i] + off;
         }
