@@ -125,13 +125,31 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_fo(const T* p, int i0, in
     }
 }
 
+// Four 16-bit elements (i0 + (l & 15), kk0 + gs (l >> 4) + q), q = 0..3, of
+// a matrix stored with the reduction index as the row (element (i, kk) at
+// p[kk*ld + i], p in LDS), in one gfx950 transpose load (ds_read_b64_tr_b16).
+// Within each 16-lane group the load hands lane j element j % 4 of the 64-bit
+// chunks that lanes 4q + j / 4 of the group address (q = 0..3; measured on
+// the device), so lane l addresses row kk0 + gs (l >> 4) + (l & 15) / 4 at
+// columns i0 + 4 (l % 4) .. + 3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 ks_tr4(const void* p, int ld, int i0, int kk0, int gs, int l) {
+    const short* q = static_cast<const short*>(p) + (kk0 + gs * (l >> 4) + ((l & 15) >> 2)) * ld + i0 + 4 * (l & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q));
+}
+
 // Same fragment of a matrix stored with the reduction index as the row:
-// element (i, kk) at p[kk*ld + i].
+// element (i, kk) at p[kk*ld + i], p in LDS (16-bit: two transpose loads, for
+// kk = k0 + 8 (l >> 4) + 0..3 and + 4..7).
 template <typename T>
 __device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, int i0, int k0,
                                                           int l = lane_id()) {
     typename Mfma<T>::frag f;
-    if constexpr (Mfma<T>::KL == 1) {
+    if constexpr (sizeof(T) == 2) {
+        const i16x4 a = ks_tr4(p, ld, i0, k0, 8, l), b = ks_tr4(p, ld, i0, k0 + 4, 8, l);
+        const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        __builtin_memcpy(&f, v, sizeof(f));
+    } else if constexpr (Mfma<T>::KL == 1) {
         f = p[(long)(k0 + (l >> 4)) * ld + i0 + (l & 15)];
     } else {
 #pragma unroll
@@ -229,9 +247,9 @@ __device__ __forceinline__ typename Mfma16<T>::frag frag16_ks(const T* p, int ld
     typename M::frag f;
     if constexpr (M::KL == 1) {
         f = p[(k0 + 4 * st + (l >> 4)) * ld + i0 + (l & 15)];
-    } else {
-#pragma unroll
-        for (int j = 0; j < M::KL; ++j) f[j] = p[(k0 + (l >> 4) * M::KL + j) * ld + i0 + (l & 15)];
+    } else {   // 16-bit, p in LDS: one transpose load
+        const i16x4 a = ks_tr4(p, ld, i0, k0, 4, l);
+        __builtin_memcpy(&f, &a, sizeof(f));
     }
     return f;
 }
