@@ -66,12 +66,10 @@ struct BwdLds {
     static constexpr size_t AM_OFF = BT_OFF + size_t(NB) * D * 4;            // T [C][LC] A of the head
     static constexpr size_t U_OFF = AM_OFF + sz(C, LC, sizeof(T));           // union region
     // phase 1 (state products, one V slice)
-    static constexpr size_t P1_DOT = 0;                                      // T [BVS][LC]
-    static constexpr size_t P1_XL = P1_DOT + sz(BVS, LC, sizeof(T));         // T [C][LB]
+    static constexpr size_t P1_XL = 0;                                       // T [C][LB]
     static constexpr size_t P1_HL = P1_XL + sz(C, LB, sizeof(T));            // T [D][LB]
     static constexpr size_t P1_DHL = P1_HL + sz(D, LB, sizeof(T));           // T [D][LB]
-    static constexpr size_t P1_DXL = P1_DHL + sz(D, LB, sizeof(T));          // T [C][LB]
-    static constexpr size_t P1_DXT = P1_DXL + sz(C, LB, sizeof(T));          // T [BVS][LC]
+    static constexpr size_t P1_DXT = P1_DHL + sz(D, LB, sizeof(T));          // T [BVS][LC] dX^T
     static constexpr size_t P1_VL = P1_DXT + sz(BVS, LC, sizeof(T));         // T [C][LB]
     static constexpr size_t P1_DOL = P1_VL + sz(C, LB, sizeof(T));          // T [C][LB] do rows
     static constexpr size_t P1_TL = P1_DOL + sz(C, LB, sizeof(T));           // T [C][LB] T = k~ dh'
@@ -81,8 +79,7 @@ struct BwdLds {
     static constexpr size_t P2_A = P2_GS + sz(C, LF, 4);
     //   2a-2e
     static constexpr size_t P2_DWT = P2_A;                                   // T [D][LC]
-    static constexpr size_t P2_DWL = P2_DWT + sz(D, LC, sizeof(T));          // T [C][LT]
-    static constexpr size_t P2_KG = P2_DWL + sz(C, LT, sizeof(T));           // T [C][LT]
+    static constexpr size_t P2_KG = P2_DWT + sz(D, LC, sizeof(T));           // T [C][LT]
     static constexpr size_t P2_DAL = P2_KG + sz(C, LT, sizeof(T));           // T [C][LC]
     static constexpr size_t P2_T1T = P2_DAL + sz(C, LC, sizeof(T));          // T [C][LC]
     static constexpr size_t P2_B_END = P2_T1T + sz(C, LC, sizeof(T));
@@ -328,11 +325,9 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         for (int t = 0; t < NTC; ++t) { dAq[t] = zero4(); dAp[t] = zero4(); }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};   // partial db of rows r0 + acc_row(i, l)
 
-        T* doT = reinterpret_cast<T*>(U + L::P1_DOT);
         T* XL = reinterpret_cast<T*>(U + L::P1_XL);
         T* hL = reinterpret_cast<T*>(U + L::P1_HL);
         T* dhL = reinterpret_cast<T*>(U + L::P1_DHL);
-        T* dXL = reinterpret_cast<T*>(U + L::P1_DXL);
         T* dXT = reinterpret_cast<T*>(U + L::P1_DXT);
         T* vL = reinterpret_cast<T*>(U + L::P1_VL);
         T* doL = reinterpret_cast<T*>(U + L::P1_DOL);
@@ -378,9 +373,6 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                     const int r = e / PR, c = (e % PR) * V8;
                     const bool real = r < len;
                     const Vec16 dv = real ? pdo[i] : Vec16{}, vv = real ? pv[i] : Vec16{};
-                    const T* dp = reinterpret_cast<const T*>(&dv);
-#pragma unroll
-                    for (int q2 = 0; q2 < V8; ++q2) doT[(c + q2) * LC + r] = dp[q2];
                     st16(doL + r * LB + c, dv);
                     st16(vL + r * LB + c, vv);
                     st16(XL + r * LB + c, px[i]);
@@ -421,12 +413,10 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 for (int i = 0; i < 4; ++i)
                     dX[t][i] = to_f32(TL[(r0 + acc_row(i, l)) * LB + cv0 + 16 * t + acc_col(l)]);
             }
-            panel_mma_ra<T, NTV, NKC>(dX, fAq, doT, LC, cv0, l);
+            panel_mma_ra<T, NTV, NKC, true>(dX, fAq, doL, LB, cv0, l);   // do rows as B (transposed loads)
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
                 const int c = cv0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dXL[(rr + i) * LB + c] = from_f32<T>(dX[t][i]);
                 store4<T>(dXT + c * LC + rr, dX[t][0], dX[t][1], dX[t][2], dX[t][3]);
             }
             __syncthreads();
@@ -434,7 +424,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             for (int k0 = 0; k0 < BVS; k0 += KS) {
                 const auto a_do = frag_kc(doL, LB, r0, k0, l);
                 const auto a_x = frag_kc(XL, LB, r0, k0, l);
-                const auto a_dx = frag_kc(dXL, LB, r0, k0, l);
+                const auto a_dx = frag_ks(dXT, LC, r0, k0, l);   // dX rows from dX^T (transposed loads)
 #pragma unroll
                 for (int t = 0; t < NTC; ++t) {
                     dAq[t] = Mfma<T>::mma(a_do, frag_kc(XL, LB, cc0 + 16 * t, k0, l), dAq[t]);
@@ -531,7 +521,6 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         // 2b: post-factors, dw -> LDS. The LDS reads of the wave's rows (G, q,
         // k, beta) come first, in one batch; 2^G and k are kept for 2c.
         T* dwT = reinterpret_cast<T*>(U + L::P2_DWT);
-        T* dwL = reinterpret_cast<T*>(U + L::P2_DWL);
         f32x4 Pq[NTD], Pk[NTD], PG[NTD];
         float eG[NTD][4], kvr[NTD][4], bsr[4];
         {
@@ -569,8 +558,6 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 if (l < 16) dGlw[rb * D + c] = kLn2 * colk;  // summed in block order later
                 const int rr = r0 + acc_row(0, l);
                 store4<T>(dwT + c * LC + rr, -dwP[t][0], -dwP[t][1], -dwP[t][2], -dwP[t][3]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dwL[(rr + i) * LT + c] = from_f32<T>(-dwP[t][i]);
             }
         }
         __syncthreads();
@@ -592,7 +579,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 }
             }
         }
-        panel_mma<T, NTC, D>(dAp, dwL, LT, r0, kgL, LT, cc0, l);
+        panel_mma<T, NTC, D, true>(dAp, dwT, LC, r0, kgL, LT, cc0, l);   // dw rows from dw^T (transposed loads)
         // dA = dA' Diag(beta); T1 = dA A^T
         T* dAL = reinterpret_cast<T*>(U + L::P2_DAL);
         T* T1T = reinterpret_cast<T*>(U + L::P2_T1T);

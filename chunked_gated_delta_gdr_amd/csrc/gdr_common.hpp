@@ -161,12 +161,13 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, in
 
 // Row-panel product: acc[t] += A[i0..i0+16, 0..KD) * Bt[j0+16t .. +16, 0..KD)^T
 // with both operands stored reduction-contiguous (A[i*lda+kk], Bt[j*ldb+kk]).
-template <typename T, int NT, int KD>
+// AKS: A stored with the reduction index as the row (A[kk*lda + i], in LDS).
+template <typename T, int NT, int KD, bool AKS = false>
 __device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda, int i0,
                                           const T* Bt, int ldb, int j0, int l = lane_id()) {
 #pragma unroll
     for (int k0 = 0; k0 < KD; k0 += kstep<T>()) {
-        auto a = frag_kc(A, lda, i0, k0, l);
+        const auto a = AKS ? frag_ks(A, lda, i0, k0, l) : frag_kc(A, lda, i0, k0, l);
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0, l), acc[t]);
     }
@@ -174,13 +175,17 @@ __device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda,
 
 // Row-panel product with the A operand already in registers (fragments of a
 // C-long reduction): A rows (a[k] for reduction step k) against Bt in memory.
-template <typename T, int NT, int NK>
+// BKS: B stored with the reduction index as the row (B[kk*ldb + j], in LDS)
+// instead of transposed (Bt[j*ldb + kk]).
+template <typename T, int NT, int NK, bool BKS = false>
 __device__ __forceinline__ void panel_mma_ra(f32x4 (&acc)[NT], const typename Mfma<T>::frag (&a)[NK],
                                              const T* Bt, int ldb, int j0, int l) {
 #pragma unroll
     for (int k = 0; k < NK; ++k)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a[k], frag_kc(Bt, ldb, j0 + 16 * t, k * kstep<T>(), l), acc[t]);
+        for (int t = 0; t < NT; ++t)
+            acc[t] = Mfma<T>::mma(a[k], BKS ? frag_ks(Bt, ldb, j0 + 16 * t, k * kstep<T>(), l)
+                                            : frag_kc(Bt, ldb, j0 + 16 * t, k * kstep<T>(), l), acc[t]);
 }
 // fp32 16x16 tile product on fp32 arrays, reduction length kd (multiple of 16):
 // acc += A[(ai0+i)*lda + ak0 + kk] * B[(bk0+kk)*ldb + bj0 + j].
