@@ -161,15 +161,18 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, in
 
 // Row-panel product: acc[t] += A[i0..i0+16, 0..KD) * Bt[j0+16t .. +16, 0..KD)^T
 // with both operands stored reduction-contiguous (A[i*lda+kk], Bt[j*ldb+kk]).
-// AKS: A stored with the reduction index as the row (A[kk*lda + i], in LDS).
-template <typename T, int NT, int KD, bool AKS = false>
+// AKS: A stored with the reduction index as the row (A[kk*lda + i], in LDS);
+// BKS: B likewise (B[kk*ldb + j], in LDS) instead of transposed (Bt[j*ldb + kk]).
+template <typename T, int NT, int KD, bool AKS = false, bool BKS = false>
 __device__ __forceinline__ void panel_mma(f32x4 (&acc)[NT], const T* A, int lda, int i0,
                                           const T* Bt, int ldb, int j0, int l = lane_id()) {
 #pragma unroll
     for (int k0 = 0; k0 < KD; k0 += kstep<T>()) {
         const auto a = AKS ? frag_ks(A, lda, i0, k0, l) : frag_kc(A, lda, i0, k0, l);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = Mfma<T>::mma(a, frag_kc(Bt, ldb, j0 + 16 * t, k0, l), acc[t]);
+        for (int t = 0; t < NT; ++t)
+            acc[t] = Mfma<T>::mma(a, BKS ? frag_ks(Bt, ldb, j0 + 16 * t, k0, l) : frag_kc(Bt, ldb, j0 + 16 * t, k0, l),
+                                  acc[t]);
     }
 }
 

@@ -600,13 +600,32 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             load8<T>(wTL + d * LC + s0, x);
             store8<T>(gwT + fo_index<T, C>(d, s0), x);
         }
+        if constexpr (sizeof(T) == 2) {
+            // w in 16 x 32 fragment-order tiles: per tile two transposed loads
+            // give lane l row 16 rt + l % 16 at columns 32 dt + 8 (l / 16) + 0..7,
+            // exactly its 16-byte piece of the tile's contiguous 1 KB
+            constexpr int NTL = (C / 16) * (D / 32) / L::NW;
+            static_assert(NTL * L::NW == (C / 16) * (D / 32), "tiles per wave");
 #pragma unroll
-        for (int it = 0; it < C * (D / 8) / NT; ++it) {
-            const int e = tid + it * NT, r = e % C, d0 = (e / C) * 8;   // r fastest: the transposed reads conflict-free
-            float x[8];
+            for (int it = 0; it < NTL; ++it) {
+                const int tl = w + L::NW * it, rt = tl / (D / 32), dt = tl % (D / 32);
+                const i16x4 a = ks_tr4(wTL, LC, 16 * rt, 32 * dt, 8, l), b = ks_tr4(wTL, LC, 16 * rt, 32 * dt + 4, 8, l);
+                Vec16 v;
+                v.w[0] = (unsigned)(unsigned short)a[0] | ((unsigned)(unsigned short)a[1] << 16);
+                v.w[1] = (unsigned)(unsigned short)a[2] | ((unsigned)(unsigned short)a[3] << 16);
+                v.w[2] = (unsigned)(unsigned short)b[0] | ((unsigned)(unsigned short)b[1] << 16);
+                v.w[3] = (unsigned)(unsigned short)b[2] | ((unsigned)(unsigned short)b[3] << 16);
+                st16(gw + fo_index<T, D>(16 * rt + (l & 15), 32 * dt + 8 * (l >> 4)), v);
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = to_f32(wTL[(d0 + i) * LC + r]);
-            store8<T>(gw + fo_index<T, D>(r, d0), x);
+            for (int it = 0; it < C * (D / 8) / NT; ++it) {
+                const int e = tid + it * NT, r = e % C, d0 = (e / C) * 8;   // r fastest: the transposed reads conflict-free
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = to_f32(wTL[(d0 + i) * LC + r]);
+                store8<T>(gw + fo_index<T, D>(r, d0), x);
+            }
         }
     }
 
@@ -631,20 +650,23 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     __syncthreads();  // Xb (w^T) -> v^T
 
     // ---- phase 8: u = A (beta v) ----
-    T* vhT = Xb;  // [D][LC]
+    T* vh = Xb;  // [C][LT] beta v, rows as loaded (the product reads them through transposed loads)
 #pragma unroll
     for (int i5 = 0; i5 < NQP; ++i5) {
         const int e = tid + i5 * NT, s2 = e % C, d0 = (e / C) * V8;   // as loaded: token fastest
         const Vec16 vv = s2 < len ? vpre[i5] : Vec16{};
         const T* vp = reinterpret_cast<const T*>(&vv);
+        Vec16 o;
+        T* op = reinterpret_cast<T*>(&o);
 #pragma unroll
-        for (int i = 0; i < V8; ++i) vhT[(d0 + i) * LC + s2] = from_f32<T>(bs[s2] * to_f32(vp[i]));
+        for (int i = 0; i < V8; ++i) op[i] = from_f32<T>(bs[s2] * to_f32(vp[i]));
+        st16(vh + s2 * LT + d0, o);
     }
     load_v(nxt, ce_n);  // the next item's v
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NTH; ++t) acc[t] = zero4();
-    panel_mma<T, NTH, C>(acc, AtL, LC, r0, vhT, LC, ch0, l);
+    panel_mma<T, NTH, C, false, true>(acc, AtL, LC, r0, vh, LT, ch0, l);
     {
         T* gu = static_cast<T*>(p.uT) + jh * D * C;
 #pragma unroll
@@ -658,6 +680,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     {
         T* gkt = static_cast<T*>(p.kt) + jh * C * D;
         T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
+        // 16-bit: k~ rows also staged over the dead Aqk / Akk (for k~^T below)
+        T* ktS = reinterpret_cast<T*>(smem + L::AQK_OFF);
+        static_assert(size_t(C) * LT * sizeof(T) <= 2 * size_t(C) * LCF * 4, "k~ staging fits over Aqk, Akk");
 #pragma unroll
         for (int it = 0; it < C * (D / 8) / NT; ++it) {
             const int e = tid + it * NT;
@@ -671,16 +696,37 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
             store8<T>(gkt + fo_index<T, D>(r, d0), x);
+            if constexpr (sizeof(T) == 2) store8<T>(ktS + r * LT + d0, x);
         }
+        if constexpr (sizeof(T) == 2) {
+            // k~^T in 16 x 32 fragment-order tiles from the staged k~ rows: two
+            // transposed loads give lane l row d = 16 dt + l % 16 at columns
+            // 32 rt + 8 (l / 16) + 0..7, its 16-byte piece of the tile
+            __syncthreads();
+            constexpr int NTL = (D / 16) * (C / 32) / L::NW;
+            static_assert(NTL * L::NW == (D / 16) * (C / 32), "tiles per wave");
 #pragma unroll
-        for (int it = 0; it < D * (C / 8) / NT; ++it) {
-            const int e = tid + it * NT, d = e % D, r0b = (e / D) * 8;   // d fastest (bank-conflict free)
-            const float gl = Gs[(C - 1) * LF + d];
-            float x[8];
+            for (int it = 0; it < NTL; ++it) {
+                const int tl = w + L::NW * it, dt = tl / (C / 32), rt = tl % (C / 32);
+                const i16x4 a = ks_tr4(ktS, LT, 16 * dt, 32 * rt, 8, l), b = ks_tr4(ktS, LT, 16 * dt, 32 * rt + 4, 8, l);
+                Vec16 v;
+                v.w[0] = (unsigned)(unsigned short)a[0] | ((unsigned)(unsigned short)a[1] << 16);
+                v.w[1] = (unsigned)(unsigned short)a[2] | ((unsigned)(unsigned short)a[3] << 16);
+                v.w[2] = (unsigned)(unsigned short)b[0] | ((unsigned)(unsigned short)b[1] << 16);
+                v.w[3] = (unsigned)(unsigned short)b[2] | ((unsigned)(unsigned short)b[3] << 16);
+                st16(gktT + fo_index<T, C>(16 * dt + (l & 15), 32 * rt + 8 * (l >> 4)), v);
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                x[i] = to_f32(kL[(r0b + i) * LT + d]) * fast_exp2(gl - Gs[(r0b + i) * LF + d]);
-            store8<T>(gktT + fo_index<T, C>(d, r0b), x);
+            for (int it = 0; it < D * (C / 8) / NT; ++it) {
+                const int e = tid + it * NT, d = e % D, r0b = (e / D) * 8;   // d fastest (bank-conflict free)
+                const float gl = Gs[(C - 1) * LF + d];
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    x[i] = to_f32(kL[(r0b + i) * LT + d]) * fast_exp2(gl - Gs[(r0b + i) * LF + d]);
+                store8<T>(gktT + fo_index<T, C>(d, r0b), x);
+            }
         }
         for (int d = tid; d < D; d += NT) p.glast[jh * D + d] = fast_exp2(Gs[(C - 1) * LF + d]);
     }
