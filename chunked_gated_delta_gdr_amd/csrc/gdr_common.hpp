@@ -137,6 +137,12 @@ __device__ __forceinline__ i16x4 ks_tr4(const void* p, int ld, int i0, int kk0, 
     const short* q = static_cast<const short*>(p) + (kk0 + gs * (l >> 4) + ((l & 15) >> 2)) * ld + i0 + 4 * (l & 3);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q));
 }
+// The same four elements as one 64-bit value, for callers that take them apart
+// one by one: reading single elements of the builtin's vector result lets the
+// compiler confuse them (it has used element 0 for all four).
+__device__ __forceinline__ uint64_t ks_tr4_bits(const void* p, int ld, int i0, int kk0, int gs, int l) {
+    return __builtin_bit_cast(uint64_t, ks_tr4(p, ld, i0, kk0, gs, l));
+}
 
 // Same fragment of a matrix stored with the reduction index as the row:
 // element (i, kk) at p[kk*ld + i], p in LDS (16-bit: two transpose loads, for

@@ -552,23 +552,27 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         store8<T>(AtL + pr5 * LC + ps5, av);
         store8<T>(AqkL + pr5 * LC + ps5, qv);
     }
-    // k^T[d][s] = beta_s k_sd 2^G_sd  (B operand of w = A k^): 8 consecutive s per item
-    T* khT = Xb;  // [D][LC]
+    // k^[s][d] = beta_s k_sd 2^G_sd, row-major (the B operand of w = A k^,
+    // read through transposed loads): 16-byte row pieces
+    T* kh = Xb;  // [C][LT]
     {   // all LDS reads of the thread's pieces first (one wait), then the writes
-        constexpr int NP = D * (C / 8) / NT;
-        static_assert(NP * NT == D * (C / 8), "piece split");
+        constexpr int NP = C * (D / 8) / NT;
+        static_assert(NP * NT == C * (D / 8), "piece split");
         float x[NP][8];
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
-            const int e = tid + it * NT, d = e % D, s0 = (e / D) * 8;   // d fastest: row reads and 16-byte column writes without bank conflicts
+            const int e = tid + it * NT, s0 = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            float kv[8], gv[8];
+            load8<T>(kL + s0 * LT + d0, kv);
+            load8f(Gs + s0 * LF + d0, gv);
+            const float b = bs[s0];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                x[it][i] = bs[s0 + i] * to_f32(kL[(s0 + i) * LT + d]) * fast_exp2(Gs[(s0 + i) * LF + d]);
+            for (int i = 0; i < 8; ++i) x[it][i] = b * kv[i] * fast_exp2(gv[i]);
         }
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
-            const int e = tid + it * NT, d = e % D, s0 = (e / D) * 8;
-            store8<T>(khT + d * LC + s0, x[it]);
+            const int e = tid + it * NT, s0 = e / (D / 8), d0 = (e % (D / 8)) * 8;
+            store8<T>(kh + s0 * LT + d0, x[it]);
         }
     }
     __syncthreads();
@@ -579,8 +583,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     f32x4 acc[NTH];
 #pragma unroll
     for (int t = 0; t < NTH; ++t) acc[t] = zero4();
-    panel_mma<T, NTH, C>(acc, AtL, LC, r0, khT, LC, ch0, l);
-    __syncthreads();  // khT is about to be overwritten by w^T
+    panel_mma<T, NTH, C, false, true>(acc, AtL, LC, r0, kh, LT, ch0, l);
+    __syncthreads();  // k^ is about to be overwritten by w^T
     T* wTL = Xb;  // [D][LC]
 #pragma unroll
     for (int t = 0; t < NTH; ++t) {
@@ -609,12 +613,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int it = 0; it < NTL; ++it) {
                 const int tl = w + L::NW * it, rt = tl / (D / 32), dt = tl % (D / 32);
-                const i16x4 a = ks_tr4(wTL, LC, 16 * rt, 32 * dt, 8, l), b = ks_tr4(wTL, LC, 16 * rt, 32 * dt + 4, 8, l);
-                Vec16 v;
-                v.w[0] = (unsigned)(unsigned short)a[0] | ((unsigned)(unsigned short)a[1] << 16);
-                v.w[1] = (unsigned)(unsigned short)a[2] | ((unsigned)(unsigned short)a[3] << 16);
-                v.w[2] = (unsigned)(unsigned short)b[0] | ((unsigned)(unsigned short)b[1] << 16);
-                v.w[3] = (unsigned)(unsigned short)b[2] | ((unsigned)(unsigned short)b[3] << 16);
+                const uint64_t a = ks_tr4_bits(wTL, LC, 16 * rt, 32 * dt, 8, l), b = ks_tr4_bits(wTL, LC, 16 * rt, 32 * dt + 4, 8, l);
+                const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
                 st16(gw + fo_index<T, D>(16 * rt + (l & 15), 32 * dt + 8 * (l >> 4)), v);
             }
         } else {
@@ -638,11 +638,20 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
         for (int t = 0; t < NTH; ++t) {
             const int c = ch0 + 16 * t + acc_col(l), rb = r0 + acc_row(0, l);
-            float o[4];
+            float qv4[4], o[4];
+            if constexpr (sizeof(T) == 2) {   // the lane's 4 rows of column c: one transposed load
+                const uint64_t u = ks_tr4_bits(qL, LT, ch0 + 16 * t, r0, 4, l);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    qv4[i] = to_f32(__builtin_bit_cast(T, static_cast<unsigned short>(u >> (16 * i))));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qv4[i] = to_f32(qL[(rb + i) * LT + c]);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
-                o[i] = p.scale * (to_f32(qL[r * LT + c]) * fast_exp2(Gs[r * LF + c]) - acc[t][i]);
+                o[i] = p.scale * (qv4[i] * fast_exp2(Gs[r * LF + c]) - acc[t][i]);
             }
             store4<T>(gq + fo_index<T, C>(c, rb), o[0], o[1], o[2], o[3]);
         }
@@ -708,12 +717,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int it = 0; it < NTL; ++it) {
                 const int tl = w + L::NW * it, dt = tl / (C / 32), rt = tl % (C / 32);
-                const i16x4 a = ks_tr4(ktS, LT, 16 * dt, 32 * rt, 8, l), b = ks_tr4(ktS, LT, 16 * dt, 32 * rt + 4, 8, l);
-                Vec16 v;
-                v.w[0] = (unsigned)(unsigned short)a[0] | ((unsigned)(unsigned short)a[1] << 16);
-                v.w[1] = (unsigned)(unsigned short)a[2] | ((unsigned)(unsigned short)a[3] << 16);
-                v.w[2] = (unsigned)(unsigned short)b[0] | ((unsigned)(unsigned short)b[1] << 16);
-                v.w[3] = (unsigned)(unsigned short)b[2] | ((unsigned)(unsigned short)b[3] << 16);
+                const uint64_t a = ks_tr4_bits(ktS, LT, 16 * dt, 32 * rt, 8, l), b = ks_tr4_bits(ktS, LT, 16 * dt, 32 * rt + 4, 8, l);
+                const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
                 st16(gktT + fo_index<T, C>(16 * dt + (l & 15), 32 * rt + 8 * (l >> 4)), v);
             }
         } else {
