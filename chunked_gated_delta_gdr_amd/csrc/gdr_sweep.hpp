@@ -268,35 +268,68 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
             // Stores are never behind a branch (spare threads repeat a piece with
             // the same data): a store on one path only would make the compiler's
             // memory-counter waits for the prefetched loads also wait for it.
-            constexpr int NP = D * BV / V8;
             T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D;
+            if constexpr (sizeof(T) == 2 && BV == 32) {
+                // 16 rows x 32 columns per wave and tile: two transposed loads
+                // give lane l row 16 dt + l % 16 at columns 32 ct + 8 (l / 16) + 0..7
+                // (with 64-column tiles, at C = 32, the 16-bit reads below
+                // measured faster)
+                constexpr int NTL = (D / 16) * (BV / 32);
+                static_assert(NTL % 4 == 0, "tiles per wave");
+                const int l = lane_id();
 #pragma unroll
-            for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
-                const int e = (int)(threadIdx.x + 256 * pi) % NP;
-                const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
-                Vec16 v;
-                T* vp = reinterpret_cast<T*>(&v);
+                for (int it = 0; it < NTL / 4; ++it) {
+                    const int tl = w + 4 * it, dt = tl % (D / 16), ct = tl / (D / 16);
+                    const uint64_t a = ks_tr4_bits(sS, LS, 16 * dt, 32 * ct, 8, l);
+                    const uint64_t b = ks_tr4_bits(sS, LS, 16 * dt, 32 * ct + 4, 8, l);
+                    const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
+                    st16(gS + tiled_index<D, BV>(16 * dt + (l & 15), v0, 32 * ct + 8 * (l >> 4)), v);
+                }
+            } else {
+                constexpr int NP = D * BV / V8;
 #pragma unroll
-                for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
-                st16(gS + tiled_index<D, BV>(d, v0, c), v);
+                for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
+                    const int e = (int)(threadIdx.x + 256 * pi) % NP;
+                    const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                    Vec16 v;
+                    T* vp = reinterpret_cast<T*>(&v);
+#pragma unroll
+                    for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
+                    st16(gS + tiled_index<D, BV>(d, v0, c), v);
+                }
             }
         }
         {   // X (T) of this chunk to the workspace, row-major pieces of 8 columns
             // (unconditional stores, as above)
-            constexpr int NP = C * BV / V8;
             T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D;
+            constexpr int NTL = (C / 16) * (BV / 32);
+            if constexpr (sizeof(T) == 2 && BV == 32 && NTL % 4 == 0) {
+                // as for the state; the reverse direction stores -T (sign flips)
+                const int l = lane_id();
+                constexpr uint64_t kNeg = DIR == 0 ? 0 : 0x8000800080008000ull;
 #pragma unroll
-            for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
-                const int e = (int)(threadIdx.x + 256 * pi) % NP;
-                const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
-                Vec16 v;
-                T* vp = reinterpret_cast<T*>(&v);
-#pragma unroll
-                for (int q = 0; q < V8; ++q) {
-                    const T x = sX[(c + q) * LX + r];
-                    vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
+                for (int it = 0; it < NTL / 4; ++it) {
+                    const int tl = w + 4 * it, rt = tl % (C / 16), ct = tl / (C / 16);
+                    const uint64_t a = ks_tr4_bits(sX, LX, 16 * rt, 32 * ct, 8, l) ^ kNeg;
+                    const uint64_t b = ks_tr4_bits(sX, LX, 16 * rt, 32 * ct + 4, 8, l) ^ kNeg;
+                    const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
+                    st16(gX + tiled_index<C, BV>(16 * rt + (l & 15), v0, 32 * ct + 8 * (l >> 4)), v);
                 }
-                st16(gX + tiled_index<C, BV>(r, v0, c), v);
+            } else {
+                constexpr int NP = C * BV / V8;
+#pragma unroll
+                for (int pi = 0; pi < (NP + 255) / 256; ++pi) {
+                    const int e = (int)(threadIdx.x + 256 * pi) % NP;
+                    const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                    Vec16 v;
+                    T* vp = reinterpret_cast<T*>(&v);
+#pragma unroll
+                    for (int q = 0; q < V8; ++q) {
+                        const T x = sX[(c + q) * LX + r];
+                        vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
+                    }
+                    st16(gX + tiled_index<C, BV>(r, v0, c), v);
+                }
             }
         }
     };
