@@ -354,6 +354,15 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
 
 #pragma unroll
         for (int v0 = 0; v0 < D; v0 += BVS) {
+            // GQA (whose group sums hold more registers): fresh opaque thread and
+            // lane indices per slice, so that the slice's LDS and global
+            // addresses are recomputed here instead of being kept live from the
+            // head's start (29 -> 3 spilled registers at C = 32). Without GQA
+            // the kept addresses measured faster.
+            const int tid_h = tid, l_h = l;
+            const int tid = GROUPED ? [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }()
+                                    : tid_h;
+            const int l = GROUPED ? opaque_lane_id() : l_h;
             __syncthreads();  // the previous slice's LDS reads are over
             if (v0 == 0) {
                 if (tid < C) bs[tid] = tid < len ? pbeta : 0.f;
