@@ -209,13 +209,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         }
         bpre = to_f32(beta[(size_t)(e2.tok0 + min(tid, e2.len - 1)) * p.H + hh]);
     };
-    // v pieces go token-fastest (one 16-byte piece per token row and lane), so
-    // that their transposed LDS writes in the u product hit distinct banks
+    // v pieces as q and k: whole rows (16 lanes cover a 256-byte row)
     auto load_v = [&](const int it, const ChunkEntry& e2) __attribute__((always_inline)) {
         const int hh = it % p.H;
 #pragma unroll
         for (int i = 0; i < NQP; ++i) {
-            const int e = tid + i * NT, r = e % C, d0 = (e / C) * V8, rt = min(r, e2.len - 1);
+            const int e = tid + i * NT, r = e / (D / V8), d0 = (e % (D / V8)) * V8, rt = min(r, e2.len - 1);
             vpre[i] = ld16(v + ((size_t)(e2.tok0 + rt) * p.H + hh) * D + d0);
         }
     };
@@ -662,7 +661,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     T* vh = Xb;  // [C][LT] beta v, rows as loaded (the product reads them through transposed loads)
 #pragma unroll
     for (int i5 = 0; i5 < NQP; ++i5) {
-        const int e = tid + i5 * NT, s2 = e % C, d0 = (e / C) * V8;   // as loaded: token fastest
+        const int e = tid + i5 * NT, s2 = e / (D / V8), d0 = (e % (D / V8)) * V8;   // as loaded
         const Vec16 vv = s2 < len ? vpre[i5] : Vec16{};
         const T* vp = reinterpret_cast<const T*>(&vv);
         Vec16 o;
