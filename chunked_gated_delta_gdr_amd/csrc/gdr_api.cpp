@@ -39,7 +39,8 @@ void layout(const gdr_bwd_desc_t* d, size_t off[WS_COUNT + 1]) {
     size_t sz[WS_COUNT];
     sz[WS_CTAB] = nc * sizeof(gdr::ChunkEntry);
     sz[WS_SEQOFF] = (N + 1) * sizeof(int);
-    sz[WS_SAQKT] = sz[WS_AM] = sz[WS_AT] = nc * H * C * C * es;
+    sz[WS_SAQKT] = sz[WS_AM] = nc * H * C * C * es;
+    sz[WS_AT] = 0;   // kept in the order, empty: A^T is read from the staged A
     sz[WS_W] = sz[WS_WT] = sz[WS_KT] = sz[WS_KTT] = sz[WS_UT] = sz[WS_QST] = nc * H * C * D * es;
     sz[WS_GLAST] = nc * H * D * 4;
     sz[WS_H] = sz[WS_DH] = nc * H * D * D * es;
@@ -129,7 +130,6 @@ static int fill_params(const gdr_bwd_desc_t* d, const int32_t* cu_seqlens, void*
     p.seq_off = reinterpret_cast<int*>(ws + off[WS_SEQOFF]);
     p.sAqkT = ws + off[WS_SAQKT];
     p.Am = ws + off[WS_AM];
-    p.AT = ws + off[WS_AT];
     p.w = ws + off[WS_W];
     p.wT = ws + off[WS_WT];
     p.kt = ws + off[WS_KT];

@@ -201,8 +201,9 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     const T* beta = static_cast<const T*>(p.beta);
 
     // What a head needs before its first slice: the chunk's q, k rows (first
-    // head only), the first slice's pieces, the row fragments of scale Aqk^T and
-    // A^T, A (staged in LDS for dA A^T), beta and 2^G_last. They are requested
+    // head only), the first slice's pieces, the row fragments of scale Aqk^T,
+    // A (staged in LDS: the B operand of dA A^T, and through transposed loads
+    // the A operand of every A^T product), beta and 2^G_last. They are requested
     // together, so that one wait covers them all; the persistent (non-grouped)
     // kernel requests them for its next item during the current item's epilogue.
     using Frag = typename Mfma<T>::frag;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     constexpr int NAM = (C * (C / V8) + NT - 1) / NT;
     Vec16 qv[NQP], kv[NQP];
     Vec16 pdo[NPC], pv[NPC], px[NPC], pt[NPC], ph[NPD], pdh[NPD];
-    Frag fAq[NKC], fAT[NKC];   // rows r0.. of scale Aqk^T and A^T (A^T again in 2c, 2e)
+    Frag fAq[NKC];             // rows r0.. of scale Aqk^T
     Vec16 pam[NAM];
     float pbeta, pgl[NPD];
     // rows past the sequence end read its last row (zeroed at use)
@@ -259,7 +260,6 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                             const int rows) __attribute__((always_inline)) {
         const size_t jh2 = (size_t)j2 * p.H + h2;
         const T* Am = static_cast<const T*>(p.Am) + jh2 * C * C;
-        const T* AT = static_cast<const T*>(p.AT) + jh2 * C * C;
         const T* sAqkT = static_cast<const T*>(p.sAqkT) + jh2 * C * C;
         pbeta = to_f32(beta[(size_t)(e2.tok0 + min(tid, e2.len - 1)) * p.H + h2]);
 #pragma unroll
@@ -268,10 +268,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             pam[i] = ld16(Am + (size_t)e * V8);
         }
 #pragma unroll
-        for (int k2 = 0; k2 < NKC; ++k2) {
-            fAq[k2] = frag_fo<T, C>(sAqkT, rows, k2 * KS, l);   // both in fragment order
-            fAT[k2] = frag_fo<T, C>(AT, rows, k2 * KS, l);
-        }
+        for (int k2 = 0; k2 < NKC; ++k2) fAq[k2] = frag_fo<T, C>(sAqkT, rows, k2 * KS, l);   // fragment order
         request_slice(e2, jh2, h2, 0, tid);
 #pragma unroll
         for (int i = 0; i < NPD; ++i) pgl[i] = p.glast[jh2 * D + min((tid + NT * i) / PR, D - 1)];
@@ -317,7 +314,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         // ================= phase 1: state products over V slices =================
         // The slice pieces (rows of do, v, X, T and of h, dh') are loaded one
         // slice ahead into registers; every MFMA operand then comes from LDS or
-        // from the row fragments of scale Aqk^T and A^T held in registers.
+        // from the row fragments of scale Aqk^T held in registers.
         f32x4 dqh[NTD], dkt_[NTD], dwP[NTD], dAq[NTC], dAp[NTC];
 #pragma unroll
         for (int t = 0; t < NTD; ++t) { dqh[t] = zero4(); dkt_[t] = zero4(); dwP[t] = zero4(); }
@@ -333,6 +330,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         T* doL = reinterpret_cast<T*>(U + L::P1_DOL);
         T* TL = reinterpret_cast<T*>(U + L::P1_TL);
         T* dvS = reinterpret_cast<T*>(U + L::DVS);
+        const T* AmL = reinterpret_cast<const T*>(smem + L::AM_OFF);   // A [C][LC]; A^T through transposed loads
 
         float hdh[NPD];                                           // partial rowsum(h dh') per piece row
 #pragma unroll
@@ -366,13 +364,13 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();  // the previous slice's LDS reads are over
             if (v0 == 0) {
                 if (tid < C) bs[tid] = tid < len ? pbeta : 0.f;
-                T* AmL = reinterpret_cast<T*>(smem + L::AM_OFF);
+                T* AmW = reinterpret_cast<T*>(smem + L::AM_OFF);
 #pragma unroll
                 for (int i = 0; i < NAM; ++i) {
                     const int e = min(tid + NT * i, C * (C / V8) - 1);
                     int ar, ac;   // A is stored in fragment order
                     fo_piece<T, C>(e, ar, ac);
-                    st16(AmL + ar * LC + ac, pam[i]);
+                    st16(AmW + ar * LC + ac, pam[i]);
                 }
             }
 #pragma unroll
@@ -451,7 +449,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             f32x4 dvh[NTV];
 #pragma unroll
             for (int t = 0; t < NTV; ++t) dvh[t] = zero4();
-            panel_mma_ra<T, NTV, NKC>(dvh, fAT, dXT, LC, cv0, l);
+            panel_mma<T, NTV, C, true>(dvh, AmL, LC, r0, dXT, LC, cv0, l);
 #pragma unroll
             for (int t = 0; t < NTV; ++t) {
                 const int c = cv0 + 16 * t + acc_col(l);
@@ -575,7 +573,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             f32x4 dkh[NTD];
 #pragma unroll
             for (int t = 0; t < NTD; ++t) dkh[t] = zero4();
-            panel_mma_ra<T, NTD, NKC>(dkh, fAT, dwT, LC, cd0, l);
+            panel_mma<T, NTD, C, true>(dkh, AmL, LC, r0, dwT, LC, cd0, l);
 #pragma unroll
             for (int t = 0; t < NTD; ++t) {
 #pragma unroll
@@ -603,7 +601,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             f32x4 t1[NTC];
 #pragma unroll
             for (int t = 0; t < NTC; ++t) t1[t] = zero4();
-            panel_mma<T, NTC, C>(t1, dAL, LC, r0, reinterpret_cast<const T*>(smem + L::AM_OFF), LC, cc0, l);
+            panel_mma<T, NTC, C>(t1, dAL, LC, r0, AmL, LC, cc0, l);
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
                 const int c = cc0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
@@ -619,7 +617,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             f32x4 dAk[NTC];
 #pragma unroll
             for (int t = 0; t < NTC; ++t) dAk[t] = zero4();
-            panel_mma_ra<T, NTC, NKC>(dAk, fAT, T1T, LC, cc0, l);
+            panel_mma<T, NTC, C, true>(dAk, AmL, LC, r0, T1T, LC, cc0, l);
             __syncthreads();  // T1T reads done before the dA operands overwrite dead buffers
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {

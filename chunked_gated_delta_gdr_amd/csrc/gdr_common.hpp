@@ -423,8 +423,7 @@ struct Params {
     int* seq_off;        // [N+1] first chunk of each sequence; seq_off[N] = chunk count
     void* sAqkT;         // [nc][H][C][C]  scale * Aqk^T
     void* Am;            // [nc][H][C][C]  A = (I + Akk)^-1
-    void* AT;            // [nc][H][C][C]  A^T
-    // scale Aqk^T, A, A^T, w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
+    // scale Aqk^T, A, w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)
     void* w;             // [nc][H][C][D]  w = A (beta k 2^G)
     void* wT;            // [nc][H][D][C]
     void* kt;            // [nc][H][C][D]  k 2^(G_last - G)

@@ -522,26 +522,22 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     }
     __syncthreads();
 
-    // ---- phase 5: A, A^T and scale Aqk^T to the workspace in 8-element row
-    //      pieces; A and Aqk in place as MFMA operands in LDS ----
+    // ---- phase 5: A and scale Aqk^T to the workspace in 8-element row
+    //      pieces (the gradient kernel takes A^T from its LDS copy of A through
+    //      transposed loads); A and Aqk in place as MFMA operands in LDS ----
     float av[8], qv[8];   // this thread's piece of A and Aqk (at most one: C <= 64)
     static_assert(C * (C / 8) <= NT, "one piece of a C x C matrix per thread");
     const bool has_piece = tid < C * (C / 8);
     const int pr5 = tid % C, ps5 = (tid / C) * 8;   // row fastest: transposed reads conflict-free
     if (has_piece) {
         T* gA = static_cast<T*>(p.Am) + jh * C * C;
-        T* gAT = static_cast<T*>(p.AT) + jh * C * C;
         T* gSq = static_cast<T*>(p.sAqkT) + jh * C * C;
-        float at[8], sq[8];
+        float sq[8];
         load8f(AF + pr5 * LCF + ps5, av);
         load8f(AqkF + pr5 * LCF + ps5, qv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            at[i] = AF[(ps5 + i) * LCF + pr5];                // A^T[r][s] = A[s][r]
-            sq[i] = p.scale * AqkF[(ps5 + i) * LCF + pr5];
-        }
+        for (int i = 0; i < 8; ++i) sq[i] = p.scale * AqkF[(ps5 + i) * LCF + pr5];
         store8<T>(gA + fo_index<T, C>(pr5, ps5), av);
-        store8<T>(gAT + fo_index<T, C>(pr5, ps5), at);   // fragment order (row fragments of A^T)
         store8<T>(gSq + fo_index<T, C>(pr5, ps5), sq);
     }
     __syncthreads();

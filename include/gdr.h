@@ -186,13 +186,14 @@ int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d,
 
 /*
  * Byte offsets of the workspace regions for descriptor d, in this order:
- *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A, 4 A^T,
+ *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A,
+ *   4 (empty: A^T is taken from A; kept so that the numbering holds),
  *   5 w, 6 w^T, 7 k~, 8 k~^T, 9 u^T, 10 scale*q~^T, 11 2^G_last,
  *   12 h (state before each chunk), 13 X, 14 dh (state gradient at each
  *   chunk end), 15 T = k~ dh, 16 = total bytes.
  * Per-chunk regions are [chunks][H][..] in io_dtype (2^G_last in fp32);
  * h, X, dh and T are stored in tiles of 32 state columns, [D/32][rows][32];
- * with 16-bit io, scale*Aqk^T, A, A^T, w, w^T, k~, k~^T and scale*q~^T are
+ * with 16-bit io, scale*Aqk^T, A, w, w^T, k~, k~^T and scale*q~^T are
  * stored in MFMA fragment order (each 16 x 32 tile one contiguous 1 KB block)
  * and u^T in accumulator order (each 16 x 16 tile one contiguous block).
  * For inspecting intermediates in tests; n must be >= 17.
