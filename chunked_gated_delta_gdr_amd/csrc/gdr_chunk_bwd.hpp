@@ -45,7 +45,11 @@ namespace gdr {
 template <typename T, int C, int D>
 struct BwdLds {
     static constexpr int NB = C / 16;
-    static constexpr int BVS = kTileV;  // V slice of the state products (the stored tile)
+    // V slice of the state products: two stored tiles at C = 64 with 16-bit
+    // operands (half as many slice loads, each twice as large, so that fewer
+    // round trips to memory sit between the slices), else one
+    static constexpr int BVS = C == 64 && sizeof(T) == 2 ? 2 * kTileV : kTileV;
+    static_assert(BVS % kTileV == 0 && D % BVS == 0, "slices of whole stored tiles");
     static constexpr int LT = D + pad<T>();
     static constexpr int LC = C + pad<T>();
     static constexpr int LB = BVS + pad<T>();
@@ -243,15 +247,17 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             const size_t row = ((size_t)(e2.tok0 + rt) * p.H + h2) * D + v0 + c;
             pdo[i] = ld16(dout + row);
             pv[i] = ld16(v + row);
-            px[i] = ld16(xb + (size_t)v0 * C + r * BVS + c);   // V-tiled
-            pt[i] = ld16(tb + (size_t)v0 * C + r * BVS + c);
+            const int col = v0 + c;   // V-tiled: tile col / kTileV, column col % kTileV
+            px[i] = ld16(xb + (size_t)(col / kTileV) * kTileV * C + r * kTileV + col % kTileV);
+            pt[i] = ld16(tb + (size_t)(col / kTileV) * kTileV * C + r * kTileV + col % kTileV);
         }
 #pragma unroll
         for (int i = 0; i < NPD; ++i) {
             const int e = min(tid + NT * i, D * PR - 1);
             const int d = e / PR, c = (e % PR) * V8;
-            ph[i] = ld16(hb + (size_t)v0 * D + d * BVS + c);   // V-tiled
-            pdh[i] = ld16(dhb + (size_t)v0 * D + d * BVS + c);
+            const int col = v0 + c;   // V-tiled, as above
+            ph[i] = ld16(hb + (size_t)(col / kTileV) * kTileV * D + d * kTileV + col % kTileV);
+            pdh[i] = ld16(dhb + (size_t)(col / kTileV) * kTileV * D + d * kTileV + col % kTileV);
         }
     };
     // (tid, l, rows: the caller's thread, lane and first row of the wave; the
