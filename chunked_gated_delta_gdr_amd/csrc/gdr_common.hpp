@@ -114,6 +114,11 @@ __device__ __forceinline__ void fo_piece(int e, int& r, int& c) {
         c = (e % (K / V)) * V;
     }
 }
+// 16-bit operands at K = 128: the sweep forms its k~^T and w^T fragments from
+// k~ and w (staged in LDS, read through transposed loads), so the preparation
+// stores only k~ and w.
+template <typename T, int D>
+constexpr bool sweep_transposes_a2() { return sizeof(T) == 2 && D == 128; }
 // The A fragment (rows i0 .. +15, k0 .. +KS) of such a matrix.
 template <typename T, int K>
 __device__ __forceinline__ typename Mfma<T>::frag frag_fo(const T* p, int i0, int k0, int l = lane_id()) {

@@ -587,17 +587,20 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         store4<T>(wTL + c * LC + rb, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     }
     __syncthreads();
-    {   // w^T rows out (16-byte pieces), w out through transposing LDS reads
+    {   // w^T rows out (16-byte pieces; not needed where the sweep transposes
+        // w itself), w out through transposing LDS reads
         T* gw = static_cast<T*>(p.w) + jh * C * D;
         T* gwT = static_cast<T*>(p.wT) + jh * D * C;
         // constant trip counts: unrolled, the LDS reads go out ahead of the stores
         static_assert(D * (C / 8) % NT == 0, "piece split");
+        if constexpr (!sweep_transposes_a2<T, D>()) {
 #pragma unroll
-        for (int it = 0; it < D * (C / 8) / NT; ++it) {
-            const int e = tid + it * NT, d = e / (C / 8), s0 = (e % (C / 8)) * 8;
-            float x[8];
-            load8<T>(wTL + d * LC + s0, x);
-            store8<T>(gwT + fo_index<T, C>(d, s0), x);
+            for (int it = 0; it < D * (C / 8) / NT; ++it) {
+                const int e = tid + it * NT, d = e / (C / 8), s0 = (e % (C / 8)) * 8;
+                float x[8];
+                load8<T>(wTL + d * LC + s0, x);
+                store8<T>(gwT + fo_index<T, C>(d, s0), x);
+            }
         }
         if constexpr (sizeof(T) == 2) {
             // w in 16 x 32 fragment-order tiles: per tile two transposed loads
@@ -680,7 +683,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         }
     }
 
-    // ---- phase 9: k~ = k 2^(G_last - G) (row-major and transposed), 2^G_last ----
+    // ---- phase 9: k~ = k 2^(G_last - G) (fragment order, and transposed where
+    //      the sweep does not transpose it itself), 2^G_last ----
     {
         T* gkt = static_cast<T*>(p.kt) + jh * C * D;
         T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
@@ -700,9 +704,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
             store8<T>(gkt + fo_index<T, D>(r, d0), x);
-            if constexpr (sizeof(T) == 2) store8<T>(ktS + r * LT + d0, x);
+            if constexpr (sizeof(T) == 2 && !sweep_transposes_a2<T, D>()) store8<T>(ktS + r * LT + d0, x);
         }
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (sweep_transposes_a2<T, D>()) {
+            // k~^T is formed by the sweep
+        } else if constexpr (sizeof(T) == 2) {
             // k~^T in 16 x 32 fragment-order tiles from the staged k~ rows: two
             // transposed loads give lane l row d = 16 dt + l % 16 at columns
             // 32 rt + 8 (l / 16) + 0..7, its 16-byte piece of the tile

@@ -51,8 +51,14 @@ struct SweepOps {
     using F = typename Mfma<T>::frag;
     using Q = typename Mfma<T>::quad;
     static constexpr int NDO = (C * (BV / (16 / sizeof(T))) + 255) / 256;
+    // the state update's A operand k~^T (fwd) or w^T (rev): read as such, or
+    // (TRA2) as the wave's 32-column block of k~ or w in fragment order, one
+    // 1 KB tile per 16 rows, transposed in LDS at use
+    static constexpr bool TRA2 = sweep_transposes_a2<T, D>();
+    static_assert(!TRA2 || S::SRW == 2, "a wave's state rows: one 32-column block");
     F a1[S::XRT][D / S::KS];                  // chunk-row product A operand: w (fwd) or k~ (rev)
-    F a2[S::SRW][C / S::KS];                  // state update A operand: k~^T (fwd) or w^T (rev)
+    F a2[TRA2 ? 1 : S::SRW][TRA2 ? 1 : C / S::KS];
+    Vec16 a2r[TRA2 ? C / 16 : 1];
     F a3[DIR == 1 ? S::SRW : 1][C / S::KS];   // reverse: (scale q~)^T
     Q u[DIR == 0 ? S::XRT : 1][S::XCT];       // forward: u at this lane's X elements
     f32x4 gl[S::SRW];                         // 2^G_last at this lane's state rows
@@ -72,10 +78,17 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
     for (int i = 0; i < S::XRT; ++i)
 #pragma unroll
         for (int k = 0; k < D / S::KS; ++k) o.a1[i][k] = frag_fo<T, D>(A1, 16 * S::xrow(w, i), k * S::KS);
+    if constexpr (SweepOps<T, C, D, BV, DIR>::TRA2) {
+        const T* A2r = static_cast<const T*>(DIR == 0 ? p.kt : p.w) + jh * C * D;
+        const int l = lane_id();
 #pragma unroll
-    for (int i = 0; i < S::SRW; ++i)
+        for (int ct = 0; ct < C / 16; ++ct) o.a2r[ct] = ld16(A2r + fo_index<T, D>(16 * ct + (l & 15), 32 * w + 8 * (l >> 4)));
+    } else {
 #pragma unroll
-        for (int k = 0; k < C / S::KS; ++k) o.a2[i][k] = frag_fo<T, C>(A2, 16 * (w * S::SRW + i), k * S::KS);
+        for (int i = 0; i < S::SRW; ++i)
+#pragma unroll
+            for (int k = 0; k < C / S::KS; ++k) o.a2[i][k] = frag_fo<T, C>(A2, 16 * (w * S::SRW + i), k * S::KS);
+    }
     const float* gl = p.glast + jh * D;
 #pragma unroll
     for (int i = 0; i < S::SRW; ++i) o.gl[i] = *reinterpret_cast<const f32x4*>(gl + 16 * (w * S::SRW + i) + acc_row(0));
@@ -119,10 +132,30 @@ __device__ __forceinline__ size_t tiled_index(int r, int v0, int c) {
     return (size_t)(cc / kTileV) * kTileV * R + (size_t)r * kTileV + cc % kTileV;
 }
 
+// A fragment (rows i0 .. +15, reduction k0 + 8 (l / 16) + 0..7) of M^T, where
+// a 32-column block of the C x D matrix M sits in LDS as 16 x 32 tiles in
+// fragment order (tile t: rows 16 t .. +15, 512 elements, lane slot
+// s = row % 16 + 16 (column / 8) at 8 s): the 4-element pieces the transposed
+// loads take are halves of those slots (as in frag_ks, with that addressing).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag frag_fo_tr(const T* tiles, int i0, int k0, int l) {
+    static_assert(sizeof(T) == 2, "16-bit transposed loads");
+    auto piece = [&](int kk) {   // lane: row kk + (l % 16) / 4, columns i0 + 4 (l % 4) .. + 3
+        const int c = kk + ((l & 15) >> 2), d = i0 + 4 * (l & 3);
+        const T* q = tiles + (c >> 4) * 512 + ((c & 15) + 16 * (d >> 3)) * 8 + (d & 7);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q));
+    };
+    const i16x4 a = piece(k0 + 8 * (l >> 4)), b = piece(k0 + 8 * (l >> 4) + 4);
+    const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    typename Mfma<T>::frag f;
+    __builtin_memcpy(&f, v, sizeof(f));
+    return f;
+}
+
 // One direction of the sweep for (sequence n, value head h, V tile at v0).
 template <typename T, int C, int D, int BV, int DIR, int NPF>
 __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS0, T* sS1, T* sX0, T* sX1, T* sDo0,
-                                          T* sDo1) {
+                                          T* sDo1, T* sA2) {
     using S = SweepTiles<T, C, D, BV>;
     using Ops = SweepOps<T, C, D, BV, DIR>;
     constexpr int SCT = S::SCT, KS = S::KS;
@@ -190,6 +223,11 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 }
             }
         }
+        if constexpr (Ops::TRA2) {   // the wave's k~ / w tiles to its own LDS block
+            const int l = lane_id();
+#pragma unroll
+            for (int ct = 0; ct < C / 16; ++ct) st16(sA2 + (w * (C / 16) + ct) * 512 + 8 * l, cur.a2r[ct]);
+        }
         __syncthreads();
 
         // 2. chunk-row product: X = u - w h (fwd) or T = k~ dh (rev); forward
@@ -197,12 +235,23 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
         //    B fragments are read before the first product (the scheduling
         //    barrier keeps the compiler from sinking each read to its use, which
         //    would expose one LDS round trip per MFMA).
+        // (TRA2: the update's A fragments, transposed from the staged tiles, are
+        // read here too, ahead of both products)
+        typename Mfma<T>::frag a2f[Ops::TRA2 ? S::SRW : 1][Ops::TRA2 ? C / KS : 1];
         {
             typename Mfma<T>::frag bx[S::XCT][D / KS];
 #pragma unroll
             for (int jj = 0; jj < S::XCT; ++jj)
 #pragma unroll
                 for (int k2 = 0; k2 < D / KS; ++k2) bx[jj][k2] = frag_kc(sS, LS, 16 * S::xcol(w, jj), k2 * KS);
+            if constexpr (Ops::TRA2) {
+                const int l = lane_id();
+#pragma unroll
+                for (int i = 0; i < S::SRW; ++i)
+#pragma unroll
+                    for (int k2 = 0; k2 < C / KS; ++k2)
+                        a2f[i][k2] = frag_fo_tr(sA2 + w * (C / 16) * 512, 16 * i, k2 * KS, l);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < S::XRT; ++i) {
@@ -252,7 +301,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
                     for (int ct = 0; ct < SCT; ++ct)
-                        st[i][ct] = Mfma<T>::mma(cur.a2[i][k2], bxs[ct][k2], st[i][ct]);
+                        st[i][ct] = Mfma<T>::mma(Ops::TRA2 ? a2f[i][k2] : cur.a2[i][k2], bxs[ct][k2], st[i][ct]);
             if constexpr (DIR == 1) {
 #pragma unroll
                 for (int k2 = 0; k2 < C / KS; ++k2)
@@ -377,6 +426,8 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
     __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
+    // per wave: its 32-column block of k~ / w (C / 16 fragment-order tiles)
+    __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, D>() ? 4 * (C / 16) * 512 : 8];
 
     // Block order: the V tile varies slowest. Workgroups are dispatched to the
     // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the D/BV
@@ -388,8 +439,8 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     const int h = bid % p.H; bid /= p.H;
     const int n = bid % p.N;
     const int dir = p.dir0 + bid / p.N;
-    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1]);
-    else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1]);
+    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
+    else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
 }
 
 }  // namespace gdr
