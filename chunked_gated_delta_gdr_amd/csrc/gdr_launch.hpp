@@ -44,18 +44,26 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     // chunk table (device-side, so varlen needs no host sync)
     gdr_chunk_table<C><<<dim3(1), dim3(256), 0, stream>>>(p);
     if (e == hipSuccess) e = mark(1);
-    if (p.dir0 == 0 && p.nc_max > 0) {
-        // persistent: as many workgroups as the CUs hold at once
-        const int items = p.nc_max * p.H, slots = compute_units() * resident_per_cu<T, C>();
-        gdr_prep<T, C, D, SCALAR><<<dim3(items < slots ? items : slots), dim3(128 * (C / 16)), 0, stream>>>(p);
-    }
-    if (e == hipSuccess) e = mark(2);
     // V tile of the sweep: 64 columns when 32-column tiles would need two or
     // more rounds of the CUs (each workgroup then loads the chunk operands once
     // for twice the columns); else 16 for a single direction at C = 64 (one
-    // round either way, fewer bytes per workgroup); else 32
+    // round either way, fewer bytes per workgroup); else 32. The preparation
+    // stores k~^T and w^T when that sweep does not form them itself (the same
+    // rule decides for the backward after a forward pass: both take dirs = 1).
     const int tiles32 = p.dirs * p.N * p.H * (D / kSweepBV);
-    if (tiles32 >= 2 * compute_units()) {
+    const bool wide = tiles32 >= 2 * compute_units();
+    const bool store_a2t = wide ? !sweep_transposes_a2<T, C, D, kSweepBVW>() : !sweep_transposes_a2<T, C, D, kSweepBV>();
+    static_assert(sweep_transposes_a2<T, C, D, kSweepBV>() == sweep_transposes_a2<T, C, D, kSweepBV1>(),
+                  "16- and 32-column sweeps take the same operands");
+    if (p.dir0 == 0 && p.nc_max > 0) {
+        // persistent: as many workgroups as the CUs hold at once
+        const int items = p.nc_max * p.H, slots = compute_units() * resident_per_cu<T, C>();
+        const dim3 grid(items < slots ? items : slots), block(128 * (C / 16));
+        if (store_a2t) gdr_prep<T, C, D, SCALAR, true><<<grid, block, 0, stream>>>(p);
+        else gdr_prep<T, C, D, SCALAR, false><<<grid, block, 0, stream>>>(p);
+    }
+    if (e == hipSuccess) e = mark(2);
+    if (wide) {
         gdr_sweep<T, C, D, kSweepBVW><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
     } else {
         bool narrow = false;

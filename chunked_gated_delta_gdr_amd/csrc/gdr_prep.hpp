@@ -151,7 +151,8 @@ __device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
     for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[i + 4] = b[i]; }
 }
 
-template <typename T, int C, int D, bool SCALAR>
+// STORE_A2T: also store w^T and k~^T (for a sweep that does not form them).
+template <typename T, int C, int D, bool SCALAR, bool STORE_A2T>
 __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     using L = PrepLds<T, C, D>;
     constexpr int NB = L::NB, NT = L::NT, LT = L::LT, LC = L::LC, LF = L::LF, LCF = L::LCF;
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         T* gwT = static_cast<T*>(p.wT) + jh * D * C;
         // constant trip counts: unrolled, the LDS reads go out ahead of the stores
         static_assert(D * (C / 8) % NT == 0, "piece split");
-        if constexpr (!sweep_transposes_a2<T, D>()) {
+        if constexpr (STORE_A2T) {
 #pragma unroll
             for (int it = 0; it < D * (C / 8) / NT; ++it) {
                 const int e = tid + it * NT, d = e / (C / 8), s0 = (e % (C / 8)) * 8;
@@ -704,9 +705,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
             store8<T>(gkt + fo_index<T, D>(r, d0), x);
-            if constexpr (sizeof(T) == 2 && !sweep_transposes_a2<T, D>()) store8<T>(ktS + r * LT + d0, x);
+            if constexpr (sizeof(T) == 2 && STORE_A2T) store8<T>(ktS + r * LT + d0, x);
         }
-        if constexpr (sweep_transposes_a2<T, D>()) {
+        if constexpr (!STORE_A2T) {
             // k~^T is formed by the sweep
         } else if constexpr (sizeof(T) == 2) {
             // k~^T in 16 x 32 fragment-order tiles from the staged k~ rows: two

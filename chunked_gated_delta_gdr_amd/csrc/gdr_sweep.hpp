@@ -54,7 +54,7 @@ struct SweepOps {
     // the state update's A operand k~^T (fwd) or w^T (rev): read as such, or
     // (TRA2) as the wave's 32-column block of k~ or w in fragment order, one
     // 1 KB tile per 16 rows, transposed in LDS at use
-    static constexpr bool TRA2 = sweep_transposes_a2<T, D>();
+    static constexpr bool TRA2 = sweep_transposes_a2<T, C, D, BV>();
     static_assert(!TRA2 || S::SRW == 2, "a wave's state rows: one 32-column block");
     F a1[S::XRT][D / S::KS];                  // chunk-row product A operand: w (fwd) or k~ (rev)
     F a2[TRA2 ? 1 : S::SRW][TRA2 ? 1 : C / S::KS];
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
     __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
     // per wave: its 32-column block of k~ / w (C / 16 fragment-order tiles)
-    __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, D>() ? 4 * (C / 16) * 512 : 8];
+    __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, C, D, BV>() ? 4 * (C / 16) * 512 : 8];
 
     // Block order: the V tile varies slowest. Workgroups are dispatched to the
     // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the D/BV
