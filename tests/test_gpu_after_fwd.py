@@ -31,6 +31,10 @@ CASES = {
     "f16_gdn_gqa_c32": scaled(GDN, B=2, T=100, H=4, Hg=2, h0_std=0.1),
     "bf16_varlen": scaled(VARLEN, T=300, H=2, Hg=2, n_seqs=5),
     "f16_gdn_varlen_c32": scaled(GDN, B=1, T=333, H=2, Hg=1, n_seqs=6, seed=9),
+    # enough (sequence, head) pairs that even the one-direction sweeps take
+    # 64-column tiles (N H D / 32 >= 2 x 256 CUs), which at C = 64 read the w^T
+    # and k~^T the forward pass's preparation must then have stored
+    "bf16_kda_wide_c64": scaled(KDA16, B=10, T=70, H=16, Hg=16, dht_std=0.1, seed=11),
 }
 
 
