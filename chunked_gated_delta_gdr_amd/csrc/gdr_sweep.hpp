@@ -152,6 +152,18 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_fo_tr(const T* tiles, int
     return f;
 }
 
+// Row pitch (elements) of the do rows in LDS: 16-byte aligned rows whose
+// transposed loads (four rows by four 8-byte column pieces per 16 lanes) fall
+// in distinct banks.
+template <typename T, int BV>
+constexpr int do_pitch() { return BV + (sizeof(T) == 2 ? 16 : 4); }
+// Whether the reverse direction keeps do rows as loaded (one 16-byte LDS write
+// per piece, do^T fragments through transposed loads) instead of writing do^T
+// element by element: measured faster at C = 32 (GDN GQA sweep 1.20 -> 1.17
+// ms), slower at C = 64 (125.8 -> 128.3 us).
+template <typename T, int C>
+constexpr bool do_rows() { return sizeof(T) == 2 && C == 32; }
+
 // One direction of the sweep for (sequence n, value head h, V tile at v0).
 template <typename T, int C, int D, int BV, int DIR, int NPF>
 __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS0, T* sS1, T* sX0, T* sX1, T* sDo0,
@@ -161,6 +173,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
     constexpr int SCT = S::SCT, KS = S::KS;
     constexpr int LS = D + pad<T>();                 // state^T rows [BV][LS]
     constexpr int LX = C + pad<T>();                 // X^T / -T^T / do^T rows [BV][LX]
+    constexpr int LDO = do_pitch<T, BV>();           // do rows as loaded [C][LDO] (do_rows)
     constexpr int V8 = 16 / sizeof(T);
     const int w = wave_id();
     const int c0 = p.seq_off[n], c1 = p.seq_off[n + 1];
@@ -213,13 +226,18 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 const int e = threadIdx.x + 256 * pi;
                 if (e < C * (BV / V8)) {
                     const int r = e / (BV / V8), cc = (e % (BV / V8)) * V8;
-                    // opaque here: keeps the element extraction (and the wait
-                    // for the load) from being hoisted to the previous chunk
-                    Vec16 dv = cur.dov[pi];
-                    asm volatile("" : "+v"(dv.w[0]), "+v"(dv.w[1]), "+v"(dv.w[2]), "+v"(dv.w[3]));
-                    const T* xp = reinterpret_cast<const T*>(&dv);
+                    if constexpr (do_rows<T, C>()) {
+                        // rows as loaded (the product reads them through transposed loads)
+                        st16(sDo + r * LDO + cc, r < len ? cur.dov[pi] : Vec16{});
+                    } else {
+                        // opaque here: keeps the element extraction (and the wait
+                        // for the load) from being hoisted to the previous chunk
+                        Vec16 dv = cur.dov[pi];
+                        asm volatile("" : "+v"(dv.w[0]), "+v"(dv.w[1]), "+v"(dv.w[2]), "+v"(dv.w[3]));
+                        const T* xp = reinterpret_cast<const T*>(&dv);
 #pragma unroll
-                    for (int q = 0; q < V8; ++q) sDo[(cc + q) * LX + r] = r < len ? xp[q] : T(0.f);
+                        for (int q = 0; q < V8; ++q) sDo[(cc + q) * LX + r] = r < len ? xp[q] : T(0.f);
+                    }
                 }
             }
         }
@@ -286,7 +304,9 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
                 for (int k2 = 0; k2 < C / KS; ++k2) {
                     bxs[ct][k2] = frag_kc(sX, LX, 16 * ct, k2 * KS);
-                    if constexpr (DIR == 1) bdo[ct][k2] = frag_kc(sDo, LX, 16 * ct, k2 * KS);
+                    if constexpr (DIR == 1)
+                        bdo[ct][k2] = do_rows<T, C>() ? frag_ks(sDo, LDO, 16 * ct, k2 * KS)    // do^T from do rows
+                                                      : frag_kc(sDo, LX, 16 * ct, k2 * KS);
                 }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -425,7 +445,7 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     static_assert(kTileV % (16 / sizeof(T)) == 0, "a 16-byte piece lies within one stored tile");
     __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
-    __shared__ __attribute__((aligned(16))) T sDo[2][BV * LX];
+    __shared__ __attribute__((aligned(16))) T sDo[2][do_rows<T, C>() ? C * do_pitch<T, BV>() : BV * LX];
     // per wave: its 32-column block of k~ / w (C / 16 fragment-order tiles)
     __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, C, D, BV>() ? 4 * (C / 16) * 512 : 8];
 
