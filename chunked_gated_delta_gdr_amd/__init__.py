@@ -13,8 +13,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["bwd", "bwd_after_fwd", "fwd", "workspace_bytes", "workspace_offsets", "library_path", "Desc",
-           "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError"]
+__all__ = ["bwd", "bwd_after_fwd", "fwd", "workspace_bytes", "workspace_offsets",
+           "library_path", "Desc", "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -110,11 +110,13 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype, shape):
+def _need(t: torch.Tensor, name: str, dtype, shape, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if t.device.type != "cuda":
         raise GdrError(f"{name} must be on the GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise GdrError(f"{name} is on {t.device}, the inputs on {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -124,6 +126,66 @@ def _need(t: torch.Tensor, name: str, dtype, shape):
 
 
 STAGES = ("chunk_table", "prep", "sweep", "chunk_bwd")
+
+
+def _workspace(desc: Desc, workspace: Optional[torch.Tensor], device) -> torch.Tensor:
+    """The caller's workspace after checks, or a new one of the required size."""
+    nbytes = workspace_bytes(desc)
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 torch tensor")
+    if workspace.device != device:
+        raise GdrError(f"workspace is on {workspace.device}, the inputs on {device}")
+    if not workspace.is_contiguous() or workspace.numel() < nbytes:
+        raise ValueError(f"workspace must be contiguous with >= {nbytes} bytes")
+    return workspace
+
+
+def _grad_outputs(q, k, v, g, beta, N, H, K, V, out):
+    """(dq, dk, dv, dg, db, dh0): new tensors, or the caller's after checks."""
+    if out is None:
+        return (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+                torch.empty_like(beta), torch.empty((N, H, K, V), dtype=torch.float32, device=q.device))
+    if len(out) != 6:
+        raise ValueError("out: (dq, dk, dv, dg, db, dh0)")
+    for name, t, ref in zip(("dq", "dk", "dv", "dg", "db"), out[:5], (q, k, v, g, beta)):
+        _need(t, f"out {name}", ref.dtype, ref.shape, q.device)
+    _need(out[5], "out dh0", torch.float32, (N, H, K, V), q.device)
+    return tuple(out)
+
+
+def _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size):
+    """Checks the backward's inputs; returns (descriptor, N, H, K, V)."""
+    io = q.dtype
+    if io not in _DTYPES:
+        raise TypeError(f"unsupported io dtype {io}")
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    gate = GATE_PER_CHANNEL if g.dim() == 4 else GATE_SCALAR
+    n_seqs = 0
+    N = B
+    dev = q.device
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.shape[0],), dev)
+        n_seqs = cu_seqlens.shape[0] - 1
+        N = n_seqs
+    _need(q, "q", io, (B, T, Hg, K))
+    _need(k, "k", io, (B, T, Hg, K), dev)
+    _need(v, "v", io, (B, T, H, V), dev)
+    _need(do, "do", io, (B, T, H, V), dev)
+    _need(beta, "beta", io, (B, T, H), dev)
+    _need(g, "g", torch.float32, (B, T, H, K) if gate == GATE_PER_CHANNEL else (B, T, H), dev)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, H, K, V), dev)
+    if dht is not None:
+        _need(dht, "dht", torch.float32, (N, H, K, V), dev)
+    desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
+                     io_dtype=io, scale=float(scale) if scale is not None else 0.0)
+    rc = check(desc)
+    if rc != 0:
+        raise _err(rc)
+    return desc, N, H, K, V
 
 
 def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
@@ -143,49 +205,11 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
     :func:`bwd_after_fwd`.
     """
     lib = _load()
-    io = q.dtype
-    if io not in _DTYPES:
-        raise TypeError(f"unsupported io dtype {io}")
-    B, T, Hg, K = q.shape
-    H, V = v.shape[2], v.shape[3]
-    gate = GATE_PER_CHANNEL if g.dim() == 4 else GATE_SCALAR
-    n_seqs = 0
-    N = B
-    if cu_seqlens is not None:
-        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.shape[0],))
-        n_seqs = cu_seqlens.shape[0] - 1
-        N = n_seqs
-    _need(q, "q", io, (B, T, Hg, K))
-    _need(k, "k", io, (B, T, Hg, K))
-    _need(v, "v", io, (B, T, H, V))
-    _need(do, "do", io, (B, T, H, V))
-    _need(beta, "beta", io, (B, T, H))
-    _need(g, "g", torch.float32, (B, T, H, K) if gate == GATE_PER_CHANNEL else (B, T, H))
-    if h0 is not None:
-        _need(h0, "h0", torch.float32, (N, H, K, V))
-    if dht is not None:
-        _need(dht, "dht", torch.float32, (N, H, K, V))
     if after_fwd and (h0 is not None or workspace is None or stage_events is not None):
         raise ValueError("after_fwd: pass the forward's workspace, and no h0 or stage_events")
-    desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
-                     io_dtype=io, scale=float(scale) if scale is not None else 0.0)
-    rc = check(desc)
-    if rc != 0:
-        raise _err(rc)
-    nbytes = workspace_bytes(desc)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    elif workspace.numel() < nbytes or workspace.dtype != torch.uint8:
-        raise ValueError(f"workspace must be uint8 with >= {nbytes} bytes")
-    if out is None:
-        dq = torch.empty_like(q)
-        dk = torch.empty_like(k)
-        dv = torch.empty_like(v)
-        dg = torch.empty_like(g)
-        db = torch.empty_like(beta)
-        dh0 = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
-    else:
-        dq, dk, dv, dg, db, dh0 = out
+    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size)
+    workspace = _workspace(desc, workspace, q.device)
+    dq, dk, dv, dg, db, dh0 = _grad_outputs(q, k, v, g, beta, N, H, K, V, out)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(h0), _ptr(do), _ptr(dht), _ptr(cu_seqlens),
@@ -235,30 +259,31 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk_size: int 
     gate = GATE_PER_CHANNEL if g.dim() == 4 else GATE_SCALAR
     n_seqs, N = 0, B
     if cu_seqlens is not None:
-        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.shape[0],))
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.shape[0],), q.device)
         n_seqs = N = cu_seqlens.shape[0] - 1
     _need(q, "q", io, (B, T, Hg, K))
-    _need(k, "k", io, (B, T, Hg, K))
-    _need(v, "v", io, (B, T, H, V))
-    _need(beta, "beta", io, (B, T, H))
-    _need(g, "g", torch.float32, (B, T, H, K) if gate == GATE_PER_CHANNEL else (B, T, H))
+    _need(k, "k", io, (B, T, Hg, K), q.device)
+    _need(v, "v", io, (B, T, H, V), q.device)
+    _need(beta, "beta", io, (B, T, H), q.device)
+    _need(g, "g", torch.float32, (B, T, H, K) if gate == GATE_PER_CHANNEL else (B, T, H), q.device)
     if h0 is not None:
-        _need(h0, "h0", torch.float32, (N, H, K, V))
+        _need(h0, "h0", torch.float32, (N, H, K, V), q.device)
     desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
                      io_dtype=io, scale=float(scale) if scale is not None else 0.0)
     rc = check(desc)
     if rc != 0:
         raise _err(rc)
-    nbytes = workspace_bytes(desc)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    elif workspace.numel() < nbytes or workspace.dtype != torch.uint8:
-        raise ValueError(f"workspace must be uint8 with >= {nbytes} bytes")
+    workspace = _workspace(desc, workspace, q.device)
     if out is None:
         o = torch.empty_like(v)
         ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device) if final_state else None
     else:
+        if len(out) != 2:
+            raise ValueError("out: (o, ht)")
         o, ht = out
+        _need(o, "out o", v.dtype, v.shape, q.device)
+        if ht is not None:
+            _need(ht, "out ht", torch.float32, (N, H, K, V), q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib.gdr_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                      _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),

@@ -10,13 +10,14 @@
 // for two waves per SIMD. With h = h_c, dh' = dh_{c+1},
 // X = u - w h (forward sweep) and T = k~ dh' (reverse sweep):
 //   dX  = scale Aqk^T do + T
-//   dAqk = scale Lower_incl(do X^T)          (the FlashQLA page's dP step)
+//   dAqk = scale Lower_incl(do X^T)
 //   dq^  = scale do h^T  -> dq += dq^ 2^G
 //   dk~  = X dh'^T       -> dk += dk~ 2^(G_last - G)
 //   dw   = -dX h^T;  dv^ = A^T dX -> dv = beta dv^
 //   dk^  = A^T dw       -> dk += beta 2^G dk^
 //   dA   = (dX v^T + dw (k 2^G)^T) Diag(beta)
-//   dAkk = -StrictLower(A^T dA A^T)          (the page's "dA = -Ar^T @ dAr @ Ar^T")
+//   dAkk = -StrictLower(A^T dA A^T)          (gradient through the inverse,
+//                                             CONSUMER_A of fused_bwd.py)
 // then the intra-chunk gradient of Aqk / Akk (the bwd_intra page):
 //   accq_r = sum_{s<=r} dAqk[r,s] k_s 2^(G_r-G_s),  acck_r = sum_{s<r} dAkk[r,s] k_s 2^(G_r-G_s)
 //   dkt_s  = sum_{r>=s} (dAqk[r,s] q_r + dAkk[r,s] beta_r k_r) 2^(G_r-G_s)

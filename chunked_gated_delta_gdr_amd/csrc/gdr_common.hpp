@@ -159,8 +159,8 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, in
                                                           int l = lane_id()) {
     typename Mfma<T>::frag f;
     if constexpr (sizeof(T) == 2) {
-        const i16x4 a = ks_tr4(p, ld, i0, k0, 8, l), b = ks_tr4(p, ld, i0, k0 + 4, 8, l);
-        const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        // the two loads' 64-bit values, not their elements (see ks_tr4_bits)
+        const uint64_t v[2] = {ks_tr4_bits(p, ld, i0, k0, 8, l), ks_tr4_bits(p, ld, i0, k0 + 4, 8, l)};
         __builtin_memcpy(&f, v, sizeof(f));
     } else if constexpr (Mfma<T>::KL == 1) {
         f = p[(long)(k0 + (l >> 4)) * ld + i0 + (l & 15)];
@@ -269,7 +269,7 @@ __device__ __forceinline__ typename Mfma16<T>::frag frag16_ks(const T* p, int ld
     if constexpr (M::KL == 1) {
         f = p[(k0 + 4 * st + (l >> 4)) * ld + i0 + (l & 15)];
     } else {   // 16-bit, p in LDS: one transpose load
-        const i16x4 a = ks_tr4(p, ld, i0, k0, 4, l);
+        const uint64_t a = ks_tr4_bits(p, ld, i0, k0, 4, l);
         __builtin_memcpy(&f, &a, sizeof(f));
     }
     return f;
@@ -445,5 +445,22 @@ struct Params {
     void* dhbuf;         // [nc][H][D/kTileV][D][kTileV]  dL/dS at the chunk end
     void* tbuf;          // [nc][H][D/kTileV][C][kTileV]  k~ dh
 };
+
+// First token (flattened b*T + t) and length of sequence n. Varlen offsets
+// are clamped to [0, T], each end to at least its start, so that no
+// cu_seqlens content can address a token outside the buffers; the chunk table
+// and the sweeps both take a sequence's span from here.
+__device__ __forceinline__ void seq_span(const Params& p, int n, int& tok0, int& len) {
+    if (p.varlen) {
+        const int T = (int)p.T;
+        const int a = min(max(p.cu[n], 0), T);
+        const int b = min(max(p.cu[n + 1], a), T);
+        tok0 = a;
+        len = b - a;
+    } else {
+        tok0 = (int)(n * p.T);
+        len = (int)p.T;
+    }
+}
 
 }  // namespace gdr

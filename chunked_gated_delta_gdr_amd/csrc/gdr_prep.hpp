@@ -43,15 +43,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
     for (int n0 = 0; n0 < p.N; n0 += 256) {
         const int n = n0 + tid;
         int len = 0, tok0 = 0;
-        if (n < p.N) {
-            if (p.varlen) {
-                tok0 = p.cu[n];
-                len = p.cu[n + 1] - p.cu[n];
-            } else {
-                tok0 = (int)(n * p.T);
-                len = (int)p.T;
-            }
-        }
+        if (n < p.N) seq_span(p, n, tok0, len);
         const int nch = (len + C - 1) / C;
         s_scan[tid] = nch;
         s_tok[tid] = tok0;

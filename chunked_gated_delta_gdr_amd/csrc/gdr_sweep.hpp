@@ -8,9 +8,9 @@
 //     store dh_{c+1};  T_c = k~_c dh_{c+1};  store T_c;
 //     dh_c = Diag(2^G_last) dh_{c+1} - w_c^T T_c + (scale q~_c)^T do_c
 // with q~ = q 2^G - Aqk w, so that scale (q 2^G)^T do - w^T (scale Aqk^T do)
-// collapses into one term; the FlashQLA page's CONSUMER_S role carries the
-// same recurrence ("dS0 = g_last * dSt", "dS0 += K^T @ dVg", "dS0 += Q^T @
-// dOg"). Columns of the state never mix (Diag acts on K, every product keeps
+// collapses into one term (the state-gradient recurrence of the CONSUMER_S
+// role of fused_bwd.py on the FlashQLA issue #30 page: decay by the chunk's
+// last gate, plus the key-side and query-side products). Columns of the state never mix (Diag acts on K, every product keeps
 // the column), so a V tile per workgroup is exact. dh0 = dh_0 is written in
 // fp32. The two directions are independent and share one grid (a pass that
 // needs one direction launches only that one).
@@ -143,10 +143,11 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_fo_tr(const T* tiles, int
     auto piece = [&](int kk) {   // lane: row kk + (l % 16) / 4, columns i0 + 4 (l % 4) .. + 3
         const int c = kk + ((l & 15) >> 2), d = i0 + 4 * (l & 3);
         const T* q = tiles + (c >> 4) * 512 + ((c & 15) + 16 * (d >> 3)) * 8 + (d & 7);
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q));
+        return __builtin_bit_cast(
+            uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q)));
     };
-    const i16x4 a = piece(k0 + 8 * (l >> 4)), b = piece(k0 + 8 * (l >> 4) + 4);
-    const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    // the two loads' 64-bit values, not their elements (see ks_tr4_bits)
+    const uint64_t v[2] = {piece(k0 + 8 * (l >> 4)), piece(k0 + 8 * (l >> 4) + 4)};
     typename Mfma<T>::frag f;
     __builtin_memcpy(&f, v, sizeof(f));
     return f;
@@ -180,8 +181,8 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
     const int nch = c1 - c0;
     // chunk geometry of the sequence (the chunk table's, computed here so that
     // no load of it sits between a prefetch and its use)
-    const int stok0 = p.varlen ? p.cu[n] : (int)(n * p.T);
-    const int slen = p.varlen ? p.cu[n + 1] - p.cu[n] : (int)p.T;
+    int stok0, slen;
+    seq_span(p, n, stok0, slen);
     const size_t sh = ((size_t)n * p.H + h) * D * D;
 
     f32x4 st[S::SRW][SCT];
