@@ -13,14 +13,15 @@ from typing import Optional
 
 import torch
 
-__all__ = ["bwd", "bwd_after_fwd", "fwd", "workspace_bytes", "workspace_offsets",
-           "library_path", "Desc", "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError"]
+__all__ = ["bwd", "bwd_after_fwd", "bwd_static", "fwd", "workspace_bytes", "workspace_offsets",
+           "library_path", "Desc", "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError", "STATIC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 _lib = None
 
 GATE_PER_CHANNEL, GATE_SCALAR = 0, 1
+STATIC_SCRATCH_BYTES = 64 << 20   # GDR_STATIC_SCRATCH_BYTES of include/gdr.h
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 WS_NAMES = ("ctab", "seq_off", "sAqkT", "A", "AT", "w", "wT", "kt", "ktT", "uT", "qsT",
             "glast", "h", "X", "dh", "T")
@@ -67,6 +68,8 @@ def _load():
         lib.gdr_fwd.argtypes = [D] + [P] * 9 + [P, ctypes.c_size_t, P]
         lib.gdr_bwd_after_fwd.restype = ctypes.c_int
         lib.gdr_bwd_after_fwd.argtypes = [D] + [P] * 14 + [P, ctypes.c_size_t, P]
+        lib.gdr_bwd_static.restype = ctypes.c_int
+        lib.gdr_bwd_static.argtypes = [D] + [P] * 15 + [P]
         lib.gdr_strerror.restype = ctypes.c_char_p
         lib.gdr_strerror.argtypes = [ctypes.c_int]
         lib.gdr_version.restype = ctypes.c_char_p
@@ -224,6 +227,26 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
             raise ValueError("stage_events: five created (recorded once) timing events")
         evs = (ctypes.c_void_p * 5)(*[e.cuda_event for e in stage_events])
         rc = lib.gdr_bwd_with_events(*args, evs)
+    if rc != 0:
+        raise _err(rc)
+    return dq, dk, dv, dg, db, dh0
+
+
+def bwd_static(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
+               chunk_size: int = 64, out=None):
+    """:func:`bwd` through gdr_bwd_static: no workspace argument, the library's
+    fixed per-GPU scratch (STATIC_SCRATCH_BYTES) instead. The C call allocates
+    nothing; pass ``out`` (dq, dk, dv, dg, db, dh0) to keep this binding from
+    allocating the outputs. Calls that may overlap on one GPU race on the
+    scratch (see gdr_bwd_static in include/gdr.h)."""
+    lib = _load()
+    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size)
+    dq, dk, dv, dg, db, dh0 = _grad_outputs(q, k, v, g, beta, N, H, K, V, out)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.gdr_bwd_static(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(h0), _ptr(do), _ptr(dht), _ptr(cu_seqlens),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0),
+                            ctypes.c_void_p(stream))
     if rc != 0:
         raise _err(rc)
     return dq, dk, dv, dg, db, dh0

@@ -65,6 +65,13 @@ bool token_buffers_ok(const gdr_bwd_desc_t* d, std::initializer_list<const void*
 
 }  // namespace
 
+namespace gdr {
+// Keeps the HIP error text of a failed call for gdr_strerror(GDR_EHIP).
+void set_hip_error(const char* what, hipError_t e) {
+    g_hip_msg = std::string("HIP error in ") + what + ": " + hipGetErrorString(e);
+}
+}  // namespace gdr
+
 extern "C" {
 
 int gdr_bwd_check(const gdr_bwd_desc_t* d) {
@@ -230,6 +237,9 @@ const char* gdr_strerror(int status) {
         case GDR_EUNSUPPORTED: return "unsupported configuration (K == V in {64,128}, K == 64 for fp32, chunk in {32,64}, sub_chunk 16)";
         case GDR_EWORKSPACE: return "workspace missing or smaller than gdr_bwd_workspace_bytes()";
         case GDR_EHIP: return g_hip_msg.empty() ? "HIP error" : g_hip_msg.c_str();
+        case GDR_ESCRATCH:
+            return "gdr_bwd_static: the problem needs more workspace than the library's fixed scratch "
+                   "(GDR_STATIC_SCRATCH_BYTES); use gdr_bwd with a caller workspace";
         default: return "unknown status";
     }
 }

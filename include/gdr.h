@@ -45,7 +45,9 @@ typedef enum {
     GDR_EINVAL = -1,        /* bad shape, null required pointer, misaligned buffer */
     GDR_EUNSUPPORTED = -2,  /* valid but not built: K, V not in {64,128}, K != V, fp32 with K != 64, chunk not in {32,64} */
     GDR_EWORKSPACE = -3,    /* workspace NULL or smaller than gdr_bwd_workspace_bytes() */
-    GDR_EHIP = -4           /* a HIP launch or query failed */
+    GDR_EHIP = -4,          /* a HIP launch or query failed */
+    GDR_ESCRATCH = -5       /* gdr_bwd_static: the problem needs more workspace than
+                               GDR_STATIC_SCRATCH_BYTES */
 } gdr_status_t;
 
 typedef enum {
@@ -202,6 +204,31 @@ int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d,
  * Returns GDR_OK, GDR_EINVAL or GDR_EUNSUPPORTED. Touches no GPU state.
  */
 int gdr_bwd_workspace_offsets(const gdr_bwd_desc_t* d, size_t* offsets, int n);
+
+/*
+ * gdr_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The same backward as gdr_bwd (same arguments,
+ * outputs, alignment and error codes, minus the workspace), with the
+ * workspace taken from a fixed device array inside this library:
+ * GDR_STATIC_SCRATCH_BYTES on each GPU the call runs on, held from the first
+ * such call on that GPU until the process ends. The call allocates and frees
+ * nothing. A descriptor whose gdr_bwd_workspace_bytes() exceeds
+ * GDR_STATIC_SCRATCH_BYTES is rejected with GDR_ESCRATCH before anything is
+ * enqueued. Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (no call reads them: every region is written before it
+ * is read). Calls that can overlap on one GPU (on different streams, or from
+ * host threads without an order between them) race on the array and give
+ * meaningless results; calls on one stream are ordered and safe. The current
+ * device must be the device of the buffers and of the stream.
+ */
+#define GDR_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdr_bwd_static(const gdr_bwd_desc_t* d,
+                   const void* q, const void* k, const void* v, const float* g,
+                   const void* beta, const float* h0, const void* do_, const float* dht,
+                   const int32_t* cu_seqlens,
+                   void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+                   void* stream);
 
 /* Static description of a status code (plus the HIP message for GDR_EHIP). */
 const char* gdr_strerror(int status);

@@ -149,3 +149,18 @@ def test_bwd_after_fwd_argument_errors(lib):
     assert call(wsp=P(0x1000010)) == -1            # workspace not 256-aligned
     assert call(cu=P(0x2000000)) == -1             # cu_seqlens without n_seqs
     assert call(dd=desc(K=96, V=96)) == -2         # unsupported
+
+
+def test_static_entry_rejects_problems_over_its_scratch(lib):
+    """gdr_bwd_static returns GDR_ESCRATCH for a descriptor whose workspace
+    exceeds GDR_STATIC_SCRATCH_BYTES, before touching the device (so NULL
+    buffers are fine here); invalid descriptors keep their own codes."""
+    P = [None] * 15
+    big = desc()   # the full-size headline workload: several hundred MB of workspace
+    assert gdr.workspace_bytes(big) > gdr.STATIC_SCRATCH_BYTES
+    assert lib.gdr_bwd_static(ctypes.byref(big), *P, None) == -5
+    assert b"scratch" in lib.gdr_strerror(-5)
+    assert lib.gdr_bwd_static(ctypes.byref(desc(K=96, V=96)), *P, None) == -2
+    assert lib.gdr_bwd_static(ctypes.byref(desc(H=16, Hg=5)), *P, None) == -1
+    with open(HEADER) as f:
+        assert f"((size_t){gdr.STATIC_SCRATCH_BYTES >> 20} << 20)" in f.read()
