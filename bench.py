@@ -9,8 +9,14 @@ events on the stream the kernels run on; the per-kernel times come from
 events recorded at the kernel boundaries inside the same timed steps.
 
 Prints one JSON line. `value` is tokens/s (B*T per second of the whole
-backward). `roofline` reports the dominant kernel against the HBM peak with
-its algorithmic bytes; `cpu_baseline` times the fp64 oracle on the host.
+backward). `roofline` is the whole backward against the HBM peak: the method's
+algorithmic bytes (inputs read once, outputs written once, one write and one
+read of the per-chunk state) over the time per step, with the summed counter
+traffic of the four kernels; `roofline.kernels` holds the same record for
+each kernel (its own algorithmic bytes in this four-kernel decomposition, its
+time from the stage events, its counter traffic, MFMA busy and LDS bank
+conflicts) and `roofline.dominant` names the longest one. `cpu_baseline`
+times the fp64 oracle on the host.
 """
 from __future__ import annotations
 
@@ -51,20 +57,26 @@ def per_token_head_costs(w, n_chunks: int, n_seqs: int, tokens: int) -> dict:
     f = (C + 1) / (2 * C)
     flops_chunk = 16 * C * K * V + 2 * C * C * f * (9 * K + 5 * V) + C ** 3
     flops = flops_chunk * n_chunks * H / th
-    # the chunk-gradient kernel alone: its inputs, outputs and the two states it reads
-    k_bytes = inp + out + state
-    return dict(method_bytes=inp + out + state + ends, io_bytes=inp + out + ends,
-                flops=flops, chunk_bwd_bytes=k_bytes)
+    return dict(method_bytes=inp + out + state + ends, io_bytes=inp + out + ends, flops=flops)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(inp, budget_s: float = 20.0, min_s: float = 10.0) -> dict:
     """Time the fp64 oracle on a bounded head sample of the same workload."""
-    import numpy as np  # noqa: F401
     import oracle
     from gdr_workloads import head_subset
     w = inp["workload"]
-    G = w.H // w.Hg
-    # probe: one q/k head group on the first sequence only gives the per-token cost
+    # probe: one q/k head group (all sequences) gives the cost per group
     sub, _ = head_subset(inp, [0])
     t0 = time.perf_counter()
     oracle.run(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"], sub["h0"],
@@ -92,112 +104,196 @@ def cpu_baseline(inp, budget_s: float = 20.0, min_s: float = 10.0) -> dict:
     frac = len(hv) / w.H
     tokens = inp["tokens"]
     return {"value": tokens * frac / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(hv)} of {w.H} value heads, all {tokens} tokens, {reps} run(s) "
                       f"({t:.2f} s each, fp64 on the host; value scaled to all heads)"}
 
 
 # ---------------------------------------------------------------------------
-# HBM traffic of the dominant kernel from rocprofv3 counters
+# Algorithmic bytes of each kernel in the four-kernel decomposition
 # ---------------------------------------------------------------------------
-# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the same counters
-# read for a plain elementwise copy of known size (`--copy-probe`), so the
-# result is in true bytes. The figures live in a text summary under profiles/
-# together with a hash of the kernel's sources; once the sources change the
-# stored figure no longer describes the kernel and `traffic` is reported null.
-KERNEL_SOURCES = ("chunked_gated_delta_gdr_amd/csrc/gdr_chunk_bwd.hpp",
-                  "chunked_gated_delta_gdr_amd/csrc/gdr_common.hpp")
+KERNELS = ("gdr_chunk_table", "gdr_prep", "gdr_sweep", "gdr_chunk_bwd")
+STAGE_OF = dict(zip(KERNELS, ("chunk_table", "prep", "sweep", "chunk_bwd")))
+
+
+def sweep_is_wide(w, n_seqs: int, cus: int = 256) -> bool:
+    """The launcher's V-tile choice for a backward (both sweep directions):
+    64-column tiles when 32-column tiles would fill the CUs twice over."""
+    return 2 * n_seqs * w.H * (w.K // 32) >= 2 * cus
+
+
+def kernel_bytes(w, n_chunks: int, n_seqs: int) -> dict:
+    """Bytes each kernel must move (read once, write once) in this
+    decomposition, per step: its inputs and outputs among the caller's tensors
+    and the workspace regions it writes or reads. q / k count once per q/k
+    head (a GQA group's value heads share them)."""
+    import torch
+    es = 4 if w.io_dtype == torch.float32 else 2
+    C, D, H, G = w.chunk, w.K, w.H, w.H // w.Hg
+    gb = D * 4 if w.gate == "kda" else 4
+    ch = n_chunks * H            # (chunk, value head) items
+    sh = n_seqs * H              # (sequence, value head) pairs
+    qk = 2 * C * D * es / G      # q, k rows of one chunk, per value head
+    tok_in = C * (D * es + gb + es)          # v, g, beta of one chunk-head
+    # the preparation also stores w^T and k~^T for a sweep that does not
+    # transpose w, k~ itself (fp32, K = 64, or 64-column tiles at C = 64)
+    wide = sweep_is_wide(w, n_seqs)
+    store_a2t = es == 4 or D != 128 or (C == 64 and wide)
+    factors = 2 * C * C * es + 4 * C * D * es + D * 4        # scale Aqk^T, A, w, k~, u^T, scale q~^T, 2^G_last
+    prep = ch * (qk + tok_in + factors + (2 * C * D * es if store_a2t else 0))
+    states = 2 * D * D * es                                   # h, dh of one chunk-head
+    xt = 2 * C * D * es                                       # X, T
+    sweep = ch * (3 * C * D * es + D * 4                      # forward: w, k~ (or k~^T), u^T, 2^G_last
+                  + 3 * C * D * es + D * 4 + C * D * es       # reverse: k~, w (or w^T), scale q~^T, 2^G_last, do
+                  + states + xt) + sh * 3 * D * D * 4         # h0, dht, dh0
+    grad_in = qk + C * D * es + tok_in + xt + states + 2 * C * C * es + D * 4   # + do, X, T, h, dh, A, Aqk^T
+    grad_out = qk + C * (D * es + gb + es)                    # dq, dk, dv, dg, db
+    chunk_bwd = ch * (grad_in + grad_out)
+    table = n_seqs * 8 + n_chunks * 16
+    return {"gdr_chunk_table": table, "gdr_prep": prep, "gdr_sweep": sweep, "gdr_chunk_bwd": chunk_bwd}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 counter summaries (profiles/gdr_counters_<workload>.md)
+# ---------------------------------------------------------------------------
+# Four passes over the same bench.py command, each a run of its own: FETCH_SIZE,
+# WRITE_SIZE (both with --copy-probe, whose plain copy of known size scales the
+# KiB they read into bytes), the derived MfmaUtil and LDSBankConflict, and raw
+# MFMA / LDS counts. Every kernel's row carries a hash of that kernel's own
+# sources; a row whose hash no longer matches the tree describes another build
+# of the kernel and its figures are reported as null.
+CSRC = "chunked_gated_delta_gdr_amd/csrc/"
+KERNEL_SOURCES = {
+    "gdr_chunk_table": ("gdr_prep.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
+    "gdr_prep": ("gdr_prep.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
+    "gdr_sweep": ("gdr_sweep.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
+    "gdr_chunk_bwd": ("gdr_chunk_bwd.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
+}
 COPY_KERNEL_KEY = "neg_kernel"   # torch.neg(out=...): reads N bytes, writes N bytes
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "util": ["MfmaUtil", "LDSBankConflict"],
+    "raw": ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+            "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, CSRC, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_summary_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"gdr_chunk_bwd_{workload}_traffic.md")
+def counters_summary_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gdr_counters_{workload}.md")
 
 
-def stored_traffic(workload: str):
-    """Bytes per launch from the committed counter summary, or None if there is
-    none or it was taken on other sources of the kernel."""
-    p = traffic_summary_path(workload)
+def stored_counters(workload: str) -> dict:
+    """{kernel: {field: value}} from the committed counter summary; a kernel
+    whose stored source hash differs from the tree's maps to None."""
+    p = counters_summary_path(workload)
+    out = {k: None for k in KERNELS}
     if not os.path.exists(p):
-        return None
+        return out
     kv = {}
     for line in open(p):
-        parts = line.strip().split("=")
-        if len(parts) == 2 and parts[0].strip().isidentifier():
+        parts = line.strip().split(" = ")
+        if len(parts) == 2 and "." in parts[0]:
             kv[parts[0].strip()] = parts[1].strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-def _read_counter_csv(path: str, counter: str) -> dict:
-    """{kernel name: [value per dispatch in KiB]} from a rocprofv3 counter_collection.csv."""
-    import csv
-    out = {}
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            if r["Counter_Name"] == counter:
-                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    for k in KERNELS:
+        if kv.get(f"{k}.source_sha256") != kernel_source_hash(k):
+            continue
+        rec = {}
+        for f in ("traffic_bytes", "read_bytes", "write_bytes", "mfma_util_pct", "lds_bank_conflict_pct",
+                  "mfma_flops", "lds_conflict_cycles_per_active"):
+            try:
+                rec[f] = float(kv[f"{k}.{f}"])
+            except (KeyError, ValueError):
+                rec[f] = None
+        out[k] = rec
     return out
 
 
-def _pick(d: dict, key: str):
-    names = [n for n in d if key in n]
-    if len(names) != 1:
-        raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
-    return d[names[0]]
+def _read_counter_csv(path: str) -> dict:
+    """{(kernel name, counter): [value per dispatch]} from a rocprofv3
+    counter_collection.csv, plus {kernel: resource row} under key None."""
+    import csv
+    vals, res = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+            res[r["Kernel_Name"]] = {c: r.get(c, "") for c in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count",
+                                                                "LDS_Block_Size", "Scratch_Size",
+                                                                "Workgroup_Size", "Grid_Size")}
+    return {"vals": vals, "res": res}
 
 
-def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: float, workload: str) -> str:
-    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
-    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+def _kernel_name(names, kernel: str):
+    m = [n for n in names if f"{kernel}<" in n or f"{kernel}I" in n]
+    if len(m) > 1:
+        raise SystemExit(f"several kernels match {kernel!r}: {m}")
+    return m[0] if m else None
+
+
+def summarize_counters(base: str, copy_mib: float, workload: str, command: str) -> str:
+    """Text summary of the four counter passes found under base/<pass>/."""
+    import glob
+    data = {}
+    for ps in COUNTER_PASSES:
+        files = glob.glob(os.path.join(base, ps, "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"pass {ps}: expected one counter_collection.csv under {base}/{ps}, found {files}")
+        data[ps] = _read_counter_csv(files[0])
+
+    def mean(ps, kname, counter):
+        v = data[ps]["vals"].get((kname, counter))
+        return sum(v) / len(v) if v else None
+
+    names = set(n for d in data.values() for (n, _c) in d["vals"])
+    copy_k = [n for n in names if COPY_KERNEL_KEY in n]
+    if len(copy_k) != 1:
+        raise SystemExit(f"expected one copy kernel, found {copy_k}")
     copy_bytes = copy_mib * 2 ** 20
-    cf, cw = _pick(fetch, COPY_KERNEL_KEY), _pick(write, COPY_KERNEL_KEY)
-    f_copy = copy_bytes / (sum(cf) / len(cf) * 1024)
-    w_copy = copy_bytes / (sum(cw) / len(cw) * 1024)
-    kf, kw = _pick(fetch, "gdr_chunk_bwd"), _pick(write, "gdr_chunk_bwd")
-    rd = sum(kf) / len(kf) * 1024 * f_copy
-    wr = sum(kw) / len(kw) * 1024 * w_copy
-    lines = [
-        f"# gdr_chunk_bwd HBM traffic, workload {workload}",
-        "",
-        "rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one pass each, scaled by the",
-        f"same counters on a plain copy of {copy_mib:g} MiB (torch.neg, reads and writes "
-        f"{copy_mib:g} MiB).",
-        "",
-        "```",
-        f"workload = {workload}",
-        f"kernel_source_sha256 = {kernel_source_hash()}",
-        f"copy_fetch_kib = {sum(cf) / len(cf):.1f}",
-        f"copy_write_kib = {sum(cw) / len(cw):.1f}",
-        f"fetch_scale = {f_copy:.4f}",
-        f"write_scale = {w_copy:.4f}",
-        f"kernel_fetch_kib = {sum(kf) / len(kf):.1f}",
-        f"kernel_write_kib = {sum(kw) / len(kw):.1f}",
-        f"read_bytes_per_launch = {rd:.0f}",
-        f"write_bytes_per_launch = {wr:.0f}",
-        f"traffic_bytes_per_launch = {rd + wr:.0f}",
-        "```",
-        "",
-        "Per dispatch (KiB, raw):",
-        "",
-        "| kernel | FETCH_SIZE | WRITE_SIZE |",
-        "|---|---|---|",
-    ]
-    for name in sorted(set(fetch) | set(write)):
-        fv, wv = fetch.get(name, [0.0]), write.get(name, [0.0])
-        lines.append(f"| `{name[:90]}` | {sum(fv) / len(fv):.1f} | {sum(wv) / len(wv):.1f} |")
+    fs = copy_bytes / (mean("fetch", copy_k[0], "FETCH_SIZE") * 1024)
+    ws = copy_bytes / (mean("write", copy_k[0], "WRITE_SIZE") * 1024)
+    lines = [f"# rocprofv3 counters per kernel, workload {workload}", "",
+             "Four passes of the same command, each a run of its own (FETCH_SIZE; WRITE_SIZE; the derived",
+             "MfmaUtil and LDSBankConflict; raw MFMA / LDS counts). FETCH_SIZE and WRITE_SIZE (KiB per",
+             f"dispatch) are scaled by what they read for a plain copy of {copy_mib:g} MiB run in the same",
+             "program (torch.neg: reads and writes that many bytes). Each kernel's `source_sha256` hashes",
+             "its own sources; bench.py reports a kernel's figures only while that hash matches the tree.",
+             "", "Command of every pass (`<counters>` per pass as above):", "", "```", command, "```", "",
+             "```", f"workload = {workload}", f"copy.fetch_scale = {fs:.4f}", f"copy.write_scale = {ws:.4f}"]
+    table = ["| kernel | read MB | write MB | traffic MB | MfmaUtil % | LDSBankConflict % | MFMA GFLOP "
+             "| LDS conflict / active | VGPR / AGPR | LDS bytes | scratch |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        kn = _kernel_name(names, k)
+        if kn is None:
+            continue
+        fk, wk = mean("fetch", kn, "FETCH_SIZE"), mean("write", kn, "WRITE_SIZE")
+        rd, wr = fk * 1024 * fs, wk * 1024 * ws
+        mu, lb = mean("util", kn, "MfmaUtil"), mean("util", kn, "LDSBankConflict")
+        mops = sum(mean("raw", kn, c) or 0.0 for c in COUNTER_PASSES["raw"][:3])
+        la, lc = mean("raw", kn, "SQ_LDS_IDX_ACTIVE"), mean("raw", kn, "SQ_LDS_BANK_CONFLICT")
+        ratio = lc / (la - lc) if la and la > lc else 0.0
+        res = data["raw"]["res"].get(kn, {})
+        lines += [f"{k}.source_sha256 = {kernel_source_hash(k)}", f"{k}.kernel_name = {kn[:120]}",
+                  f"{k}.fetch_kib = {fk:.1f}", f"{k}.write_kib = {wk:.1f}",
+                  f"{k}.read_bytes = {rd:.0f}", f"{k}.write_bytes = {wr:.0f}",
+                  f"{k}.traffic_bytes = {rd + wr:.0f}", f"{k}.mfma_util_pct = {mu:.3f}",
+                  f"{k}.lds_bank_conflict_pct = {lb:.3f}", f"{k}.mfma_flops = {mops * 512:.0f}",
+                  f"{k}.lds_conflict_cycles_per_active = {ratio:.4f}"]
+        table.append(f"| {k} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | {mu:.2f} | {lb:.2f} | "
+                     f"{mops * 512 / 1e9:.2f} | {ratio:.3f} | {res.get('VGPR_Count', '')} / "
+                     f"{res.get('Accum_VGPR_Count', '')} | {res.get('LDS_Block_Size', '')} | "
+                     f"{res.get('Scratch_Size', '')} |")
+    lines += ["```", "", "Per launch (one dispatch of each kernel; averages over the profiled dispatches):", ""]
+    lines += table
     return "\n".join(lines) + "\n"
 
 
@@ -322,14 +418,17 @@ def main() -> int:
                          "train (the forward pass, then the backward after it on its workspace)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after the timed steps, run a plain copy of MIB MiB (counter calibration)")
-    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the counter summary of the four rocprofv3 --pmc passes under "
+                         "DIR/{fetch,write,util,raw} and exit")
+    ap.add_argument("--pmc-command", default="",
+                    help="the profiled command, recorded in the counter summary")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
                     help="print a table of a rocprofv3 --stats kernel_stats.csv and exit")
     args = ap.parse_args()
-    if args.summarize_traffic:
-        print(summarize_traffic(*args.summarize_traffic, args.copy_probe or 1024.0, args.workload),
-              end="")
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.copy_probe or 1024.0, args.workload,
+                                 args.pmc_command), end="")
         return 0
     if args.summarize_stats:
         print(summarize_kernel_stats(args.summarize_stats), end="")
@@ -397,11 +496,28 @@ def main() -> int:
 
     costs = per_token_head_costs(w, n_chunks, n_seqs, tokens)
     th = tokens * w.H
-    k_ms = kernel_ms["chunk_bwd"]
-    k_bytes = costs["chunk_bwd_bytes"] * th
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
     fp32 = w.io_dtype == torch.float32
     step_s = ms * 1e-3
+    method_bytes = costs["method_bytes"] * th
+    achieved = method_bytes / step_s / 1e9
+    flops = costs["flops"] * th
+    mfma_peak = MFMA_FP32_PEAK_TFS if fp32 else MFMA_BF16_PEAK_TFS
+    kb = kernel_bytes(w, n_chunks, n_seqs)
+    stored = stored_counters(w.name)
+    kernels = {}
+    for k in KERNELS:
+        k_ms = kernel_ms[STAGE_OF[k]]
+        rec = stored[k]
+        traffic = rec["traffic_bytes"] if rec else None
+        kach = kb[k] / (k_ms * 1e-3) / 1e9 if k_ms > 0 else None
+        kernels[k] = {"ms": k_ms, "algorithmic_bytes": kb[k], "achieved": kach,
+                      "frac": kach / HBM_PEAK_GBS if kach is not None else None,
+                      "traffic": traffic,
+                      "traffic_over_algorithmic": traffic / kb[k] if traffic and kb[k] else None,
+                      "mfma_util_pct": rec["mfma_util_pct"] if rec else None,
+                      "lds_bank_conflict_pct": rec["lds_bank_conflict_pct"] if rec else None,
+                      "mfma_flops_counted": rec["mfma_flops"] if rec else None}
+    traffic_all = [kernels[k]["traffic"] for k in KERNELS]
     res = {
         "metric": METRIC,
         "value": tokens / step_s,
@@ -414,17 +530,17 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "T": w.T, "tokens": tokens, "H": w.H, "Hg": w.Hg,
                    "K": w.K, "V": w.V, "chunk": w.chunk, "sub_chunk": 16, "gate": w.gate,
                    "n_seqs": n_seqs, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "gdr_chunk_bwd", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic(w.name),
-                     "algorithmic_bytes": k_bytes, "ms": k_ms},
-        "step_roofline": {
-            "method_bytes": costs["method_bytes"] * th,
-            "hbm_frac": costs["method_bytes"] * th / step_s / 1e9 / HBM_PEAK_GBS,
-            "io_floor_frac": costs["io_bytes"] * th / step_s / 1e9 / HBM_PEAK_GBS,
-            "flops": costs["flops"] * th,
-            "mfma_frac": costs["flops"] * th / step_s / 1e12 /
-                         (MFMA_FP32_PEAK_TFS if fp32 else MFMA_BF16_PEAK_TFS)},
+        # the whole backward (all four kernels of one step) against the HBM peak
+        "roofline": {"bound": "hbm", "scope": "step", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": sum(traffic_all) if all(x is not None for x in traffic_all) else None,
+                     "algorithmic_bytes": method_bytes,
+                     "decomposition_bytes": sum(kb.values()),
+                     "io_floor_frac": costs["io_bytes"] * th / step_s / 1e9 / HBM_PEAK_GBS,
+                     "mfma": {"flops": flops, "achieved": flops / step_s / 1e12, "peak": mfma_peak,
+                              "unit": "TFLOP/s", "frac": flops / step_s / 1e12 / mfma_peak},
+                     "dominant": max(KERNELS, key=lambda k: kernels[k]["ms"]),
+                     "kernels": kernels},
         "kernels_ms": kernel_ms,
         "wall_ms_per_step": t_wall * 1e3 / args.steps,
     }
