@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["bwd", "bwd_after_fwd", "bwd_static", "fwd", "workspace_bytes", "workspace_offsets",
+__all__ = ["bwd", "bwd_after_fwd", "bwd_from_states", "bwd_static", "fwd", "workspace_bytes", "workspace_offsets",
            "library_path", "Desc", "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError", "STATIC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +38,8 @@ class Desc(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("sub_chunk", ctypes.c_int32),
                 ("n_seqs", ctypes.c_int32), ("gate", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("state_v_first", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -68,6 +69,8 @@ def _load():
         lib.gdr_fwd.argtypes = [D] + [P] * 9 + [P, ctypes.c_size_t, P]
         lib.gdr_bwd_after_fwd.restype = ctypes.c_int
         lib.gdr_bwd_after_fwd.argtypes = [D] + [P] * 14 + [P, ctypes.c_size_t, P]
+        lib.gdr_bwd_from_states.restype = ctypes.c_int
+        lib.gdr_bwd_from_states.argtypes = [D] + [P] * 9 + [ctypes.c_int64] + [P] * 6 + [P, ctypes.c_size_t, P]
         lib.gdr_bwd_static.restype = ctypes.c_int
         lib.gdr_bwd_static.argtypes = [D] + [P] * 15 + [P]
         lib.gdr_strerror.restype = ctypes.c_char_p
@@ -82,10 +85,11 @@ def _err(rc: int) -> GdrError:
 
 
 def make_desc(B, T, H, Hg, K, V, chunk=64, n_seqs=0, gate=GATE_PER_CHANNEL,
-              io_dtype=torch.bfloat16, scale=0.0, sub_chunk=16) -> Desc:
+              io_dtype=torch.bfloat16, scale=0.0, sub_chunk=16, state_v_first=False) -> Desc:
     return Desc(B=B, T=T, H=H, Hg=Hg, K=K, V=V, chunk=chunk, sub_chunk=sub_chunk,
                 n_seqs=n_seqs, gate=gate, io_dtype=_DTYPES.get(io_dtype, -1)
-                if isinstance(io_dtype, torch.dtype) else int(io_dtype), scale=scale)
+                if isinstance(io_dtype, torch.dtype) else int(io_dtype), scale=scale,
+                state_v_first=int(bool(state_v_first)))
 
 
 def check(desc: Desc) -> int:
@@ -158,7 +162,7 @@ def _grad_outputs(q, k, v, g, beta, N, H, K, V, out):
     return tuple(out)
 
 
-def _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size):
+def _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size, state_v_first=False):
     """Checks the backward's inputs; returns (descriptor, N, H, K, V)."""
     io = q.dtype
     if io not in _DTYPES:
@@ -184,7 +188,8 @@ def _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size):
     if dht is not None:
         _need(dht, "dht", torch.float32, (N, H, K, V), dev)
     desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
-                     io_dtype=io, scale=float(scale) if scale is not None else 0.0)
+                     io_dtype=io, scale=float(scale) if scale is not None else 0.0,
+                     state_v_first=state_v_first)
     rc = check(desc)
     if rc != 0:
         raise _err(rc)
@@ -193,7 +198,7 @@ def _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size):
 
 def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
         chunk_size: int = 64, workspace: Optional[torch.Tensor] = None, out=None,
-        stage_events=None, after_fwd: bool = False):
+        stage_events=None, after_fwd: bool = False, state_v_first: bool = False):
     """Backward of the gated delta rule (see include/gdr.h for the definition).
 
     q, k [B,T,Hg,K]; v, do [B,T,H,V]; beta [B,T,H] (all in one io dtype:
@@ -205,12 +210,14 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
     may hold preallocated outputs in the same order. ``stage_events``: five
     torch.cuda.Event(enable_timing=True), already recorded once, recorded at
     the kernel boundaries (see gdr_bwd_with_events). ``after_fwd``: see
-    :func:`bwd_after_fwd`.
+    :func:`bwd_after_fwd`. ``state_v_first``: h0, dht and dh0 hold each state
+    transposed, [N,H,V,K] (the same shape, since K == V).
     """
     lib = _load()
     if after_fwd and (h0 is not None or workspace is None or stage_events is not None):
         raise ValueError("after_fwd: pass the forward's workspace, and no h0 or stage_events")
-    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size)
+    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size,
+                                 state_v_first)
     workspace = _workspace(desc, workspace, q.device)
     dq, dk, dv, dg, db, dh0 = _grad_outputs(q, k, v, g, beta, N, H, K, V, out)
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -232,15 +239,49 @@ def bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
     return dq, dk, dv, dg, db, dh0
 
 
+def bwd_from_states(q, k, v, g, beta, do, h, dht=None, cu_seqlens=None, scale=None,
+                    chunk_size: int = 64, state_v_first: bool = False,
+                    workspace: Optional[torch.Tensor] = None, out=None):
+    """Backward from the per-chunk states the forward pass saved
+    (gdr_bwd_from_states): the forward state sweep is not run.
+
+    ``h`` holds the state before every chunk in the io dtype: [B, NT, H, K, V]
+    (fixed length, NT = ceil(T / chunk_size)) or [n_chunks, H, K, V] (chunks of
+    all sequences in order; varlen); with ``state_v_first`` the last two axes
+    are (V, K), as are dht's and dh0's. Returns what :func:`bwd` returns."""
+    lib = _load()
+    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, None, dht, cu_seqlens, scale, chunk_size,
+                                 state_v_first)
+    if not isinstance(h, torch.Tensor):
+        raise TypeError("h must be a torch tensor")
+    n_h = h.shape[0] * h.shape[1] if h.dim() == 5 else h.shape[0]
+    _need(h, "h", q.dtype, (h.shape[0], h.shape[1], H, K, V) if h.dim() == 5 else (n_h, H, K, V), q.device)
+    if cu_seqlens is None:
+        nt = (q.shape[1] + chunk_size - 1) // chunk_size
+        if n_h != q.shape[0] * nt or (h.dim() == 5 and h.shape[:2] != (q.shape[0], nt)):
+            raise ValueError(f"h: expected [{q.shape[0]}, {nt}, H, K, V] per-chunk states")
+    workspace = _workspace(desc, workspace, q.device)
+    dq, dk, dv, dg, db, dh0 = _grad_outputs(q, k, v, g, beta, N, H, K, V, out)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.gdr_bwd_from_states(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(do), _ptr(dht), _ptr(cu_seqlens), _ptr(h), ctypes.c_int64(n_h),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0),
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise _err(rc)
+    return dq, dk, dv, dg, db, dh0
+
+
 def bwd_static(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
-               chunk_size: int = 64, out=None):
+               chunk_size: int = 64, out=None, state_v_first: bool = False):
     """:func:`bwd` through gdr_bwd_static: no workspace argument, the library's
     fixed per-GPU scratch (STATIC_SCRATCH_BYTES) instead. The C call allocates
     nothing; pass ``out`` (dq, dk, dv, dg, db, dh0) to keep this binding from
     allocating the outputs. Calls that may overlap on one GPU race on the
     scratch (see gdr_bwd_static in include/gdr.h)."""
     lib = _load()
-    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size)
+    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size,
+                                 state_v_first)
     dq, dk, dv, dg, db, dh0 = _grad_outputs(q, k, v, g, beta, N, H, K, V, out)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib.gdr_bwd_static(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -253,7 +294,7 @@ def bwd_static(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=N
 
 
 def bwd_after_fwd(q, k, v, g, beta, do, workspace: torch.Tensor, dht=None, cu_seqlens=None,
-                  scale=None, chunk_size: int = 64, out=None):
+                  scale=None, chunk_size: int = 64, out=None, state_v_first: bool = False):
     """Backward after :func:`fwd`, from the per-chunk states it saved.
 
     ``workspace`` must be the one a :func:`fwd` call filled, with the same
@@ -262,11 +303,13 @@ def bwd_after_fwd(q, k, v, g, beta, do, workspace: torch.Tensor, dht=None, cu_se
     gradient kernel run. Returns what :func:`bwd` returns for those inputs.
     """
     return bwd(q, k, v, g, beta, do, dht=dht, cu_seqlens=cu_seqlens, scale=scale,
-               chunk_size=chunk_size, workspace=workspace, out=out, after_fwd=True)
+               chunk_size=chunk_size, workspace=workspace, out=out, after_fwd=True,
+               state_v_first=state_v_first)
 
 
 def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk_size: int = 64,
-        workspace: Optional[torch.Tensor] = None, out=None, final_state: bool = True):
+        workspace: Optional[torch.Tensor] = None, out=None, final_state: bool = True,
+        state_v_first: bool = False):
     """Forward of the gated delta rule: returns (o, ht).
 
     Same inputs as :func:`bwd` (without do, dht). o [B,T,H,V] in the io dtype;
@@ -292,7 +335,8 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk_size: int 
     if h0 is not None:
         _need(h0, "h0", torch.float32, (N, H, K, V), q.device)
     desc = make_desc(B, T, H, Hg, K, V, chunk=chunk_size, n_seqs=n_seqs, gate=gate,
-                     io_dtype=io, scale=float(scale) if scale is not None else 0.0)
+                     io_dtype=io, scale=float(scale) if scale is not None else 0.0,
+                     state_v_first=state_v_first)
     rc = check(desc)
     if rc != 0:
         raise _err(rc)

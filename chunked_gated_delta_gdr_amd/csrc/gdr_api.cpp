@@ -82,6 +82,7 @@ int gdr_bwd_check(const gdr_bwd_desc_t* d) {
     if (d->io_dtype < GDR_DTYPE_F32 || d->io_dtype > GDR_DTYPE_F16) return GDR_EINVAL;
     if (d->n_seqs < 0 || (d->n_seqs > 0 && d->B != 1)) return GDR_EINVAL;
     if (d->chunk < 1 || d->sub_chunk < 1) return GDR_EINVAL;
+    if (d->state_v_first != 0 && d->state_v_first != 1) return GDR_EINVAL;
     // flattened token indices are 32-bit on the device
     if (d->B * d->T > (int64_t)INT32_MAX / 2) return GDR_EUNSUPPORTED;
     if (d->K != d->V || (d->K != 64 && d->K != 128)) return GDR_EUNSUPPORTED;
@@ -131,6 +132,7 @@ static int fill_params(const gdr_bwd_desc_t* d, const int32_t* cu_seqlens, void*
     p.N = d->n_seqs > 0 ? d->n_seqs : (int)d->B;
     p.nc_max = (int)max_chunks(d);
     p.varlen = d->n_seqs > 0;
+    p.vfirst = d->state_v_first;
     p.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->K);
     p.cu = cu_seqlens;
     p.ctab = reinterpret_cast<gdr::ChunkEntry*>(ws + off[WS_CTAB]);
@@ -222,6 +224,31 @@ int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d, const void* q, const void* k, con
                   stream, nullptr);
 }
 
+int gdr_bwd_from_states(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v,
+                        const float* g, const void* beta, const void* do_, const float* dht,
+                        const int32_t* cu_seqlens, const void* h, int64_t n_h_chunks, void* dq, void* dk,
+                        void* dv, float* dg, void* db, float* dh0, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    int rc = gdr_bwd_check(d);
+    if (rc != GDR_OK) return rc;
+    if (!token_buffers_ok(d, {q, k, v, g, beta, do_, dq, dk, dv, dg, db, h})) return GDR_EINVAL;
+    if (!dh0 || !aligned16(dh0)) return GDR_EINVAL;
+    if (dht && !aligned16(dht)) return GDR_EINVAL;
+    if (n_h_chunks < 0 || n_h_chunks > max_chunks(d)) return GDR_EINVAL;
+    if (d->n_seqs == 0 && n_h_chunks != max_chunks(d)) return GDR_EINVAL;   // B ceil(T / C)
+    gdr::Params p;
+    rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
+    if (rc != GDR_OK) return rc;
+    p.dirs = 1;
+    p.dir0 = 1;   // reverse sweep only: the states kernel stands in for the forward sweep
+    p.hsrc = h;
+    p.nh_src = (int)n_h_chunks;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.dout = do_; p.dht = dht;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
+    return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 0), p,
+                  stream, nullptr);
+}
+
 int gdr_bwd(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v, const float* g,
             const void* beta, const float* h0, const void* do_, const float* dht,
             const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
@@ -244,6 +271,6 @@ const char* gdr_strerror(int status) {
     }
 }
 
-const char* gdr_version(void) { return "0.1.0"; }
+const char* gdr_version(void) { return "0.2.0"; }
 
 }  // extern "C"

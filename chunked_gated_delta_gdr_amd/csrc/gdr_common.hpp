@@ -417,8 +417,14 @@ struct Params {
     int dirs;            // state sweeps run: 1 = one direction, 2 = both
     int dir0;            // first direction: 0 = forward (forward pass, or both for the
                          // backward); 1 = reverse only (a backward after the forward
-                         // pass, whose table, factors, h and X are in the workspace)
+                         // pass, whose table, factors, h and X are in the workspace,
+                         // or a backward from caller-supplied per-chunk states)
+    int vfirst;          // h0, dht, dh0, ht (and hsrc) stored [V][K] instead of [K][V]
     float scale;
+    // per-chunk states supplied by the caller (backward from states), or NULL:
+    // [nh_src][H][K][V] ([..][V][K] with vfirst) in the io type
+    const void* hsrc;
+    int nh_src;          // chunk states the caller's buffer holds
     // inputs
     const void* q; const void* k; const void* v; const float* g; const void* beta;
     const float* h0; const void* dout; const float* dht; const int* cu;
@@ -445,6 +451,13 @@ struct Params {
     void* dhbuf;         // [nc][H][D/kTileV][D][kTileV]  dL/dS at the chunk end
     void* tbuf;          // [nc][H][D/kTileV][C][kTileV]  k~ dh
 };
+
+// Offset of state element (key row d, value column c) within one K x V state:
+// row-major [K][V], or [V][K] when the caller stores states value-first.
+template <int D>
+__device__ __forceinline__ size_t state_index(const Params& p, int d, int c) {
+    return p.vfirst ? (size_t)c * D + d : (size_t)d * D + c;
+}
 
 // First token (flattened b*T + t) and length of sequence n. Varlen offsets
 // are clamped to [0, T], each end to at least its start, so that no

@@ -3,6 +3,7 @@
 #include "gdr_chunk_bwd.hpp"
 #include "gdr_fwd_out.hpp"
 #include "gdr_prep.hpp"
+#include "gdr_states.hpp"
 #include "gdr_sweep.hpp"
 
 namespace gdr {
@@ -36,7 +37,10 @@ inline int compute_units() {
 // forward pass (p.dir0 == 1) finds the factors, h and X in the workspace and
 // runs the reverse sweep only; it rebuilds the chunk table all the same, so
 // that every index the kernels use comes from cu_seqlens and the shapes, not
-// from workspace contents. ev as above (entries 0..3).
+// from workspace contents. A backward from caller-supplied per-chunk states
+// (p.hsrc, p.dir0 == 1) runs the preparation, then the chunk-parallel states
+// kernel in place of the forward sweep, then the reverse sweep. ev as above
+// (entries 0..3).
 template <typename T, int C, int D, bool SCALAR>
 hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
@@ -55,7 +59,7 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     const bool store_a2t = wide ? !sweep_transposes_a2<T, C, D, kSweepBVW>() : !sweep_transposes_a2<T, C, D, kSweepBV>();
     static_assert(sweep_transposes_a2<T, C, D, kSweepBV>() == sweep_transposes_a2<T, C, D, kSweepBV1>(),
                   "16- and 32-column sweeps take the same operands");
-    if (p.dir0 == 0 && p.nc_max > 0) {
+    if ((p.dir0 == 0 || p.hsrc) && p.nc_max > 0) {
         // persistent: as many workgroups as the CUs hold at once
         const int items = p.nc_max * p.H, slots = compute_units() * resident_per_cu<T, C>();
         const dim3 grid(items < slots ? items : slots), block(128 * (C / 16));
@@ -63,6 +67,11 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
         else gdr_prep<T, C, D, SCALAR, false><<<grid, block, 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(2);
+    if (p.hsrc && p.nc_max > 0) {   // X and the tiled h from the caller's states
+        const dim3 grid(p.nc_max, p.H, D / kTileV);
+        if (p.vfirst) gdr_states_in<T, C, D, true><<<grid, dim3(256), 0, stream>>>(p);
+        else gdr_states_in<T, C, D, false><<<grid, dim3(256), 0, stream>>>(p);
+    }
     if (wide) {
         gdr_sweep<T, C, D, kSweepBVW><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
     } else {

@@ -195,7 +195,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int d = 16 * (w * S::SRW + i) + acc_row(e), c = v0 + 16 * ct + acc_col();
-                    st[i][ct][e] = init ? init[sh + (size_t)d * D + c] : 0.f;
+                    st[i][ct][e] = init ? init[sh + state_index<D>(p, d, c)] : 0.f;
                 }
     }
     // step k of this direction works on chunk `it` of the sequence
@@ -432,7 +432,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int d = 16 * (w * S::SRW + i) + acc_row(e), c = v0 + 16 * ct + acc_col();
-                    fin[sh + (size_t)d * D + c] = st[i][ct][e];
+                    fin[sh + state_index<D>(p, d, c)] = st[i][ct][e];
                 }
     }
 }

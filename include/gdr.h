@@ -73,6 +73,11 @@ typedef enum {
  *   gate      gdr_gate_t
  *   io_dtype  gdr_dtype_t of q, k, v, beta, do and of dq, dk, dv, db
  *   scale     readout scale; <= 0 means K^-0.5
+ *   state_v_first  0: every state buffer (h0, dht, dh0, ht, and the per-chunk
+ *             states of gdr_bwd_from_states) is [..][K][V], row k holding the
+ *             value columns; 1: [..][V][K] (the transposed layout the FlashQLA
+ *             page's state_v_first option selects). Shapes are unchanged
+ *             (K == V); only the order of the two state axes differs.
  */
 typedef struct {
     int64_t B, T;
@@ -82,6 +87,7 @@ typedef struct {
     int32_t gate;
     int32_t io_dtype;
     float scale;
+    int32_t state_v_first;
 } gdr_bwd_desc_t;
 
 /*
@@ -185,6 +191,34 @@ int gdr_bwd_after_fwd(const gdr_bwd_desc_t* d,
                       const int32_t* cu_seqlens,
                       void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward from per-chunk states the caller already holds: the interface
+ * of the FlashQLA issue #30 page's backward (fused_bwd.py's kernel signature
+ * and its fused_gdr_bwd wrapper take the forward's per-chunk states h as an
+ * input, with state_v_first choosing their layout). h_c is the state before
+ * chunk c (h_0 = h0 of each sequence):
+ *   h           io_dtype [n_h_chunks][H][K][V], or [n_h_chunks][H][V][K] when
+ *               d->state_v_first is 1; chunk c of sequence n is entry
+ *               sum_{m<n} ceil(len_m / chunk) + c (fixed length: n ceil(T /
+ *               chunk) + c, i.e. the [B][ceil(T/chunk)] order of a 5-d
+ *               [B, chunks, H, K, V] tensor).
+ *   n_h_chunks  entries in h: must be B ceil(T / chunk) for fixed length
+ *               (GDR_EINVAL otherwise); for varlen, the sum above (not
+ *               checkable without reading cu_seqlens: chunks at or past
+ *               n_h_chunks are never read, their gradients are then meaningless).
+ * The forward state sweep is not run: a chunk-parallel kernel forms X_c =
+ * u_c - w_c h_c from the given states, then the reverse sweep and the gradient
+ * kernel run as in gdr_bwd. h0 is not needed. Everything else (arguments,
+ * outputs, workspace size, alignment, error codes) as for gdr_bwd; dht and dh0
+ * follow d->state_v_first too.
+ */
+int gdr_bwd_from_states(const gdr_bwd_desc_t* d,
+                        const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const void* do_, const float* dht,
+                        const int32_t* cu_seqlens, const void* h, int64_t n_h_chunks,
+                        void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Byte offsets of the workspace regions for descriptor d, in this order:

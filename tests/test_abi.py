@@ -164,3 +164,22 @@ def test_static_entry_rejects_problems_over_its_scratch(lib):
     assert lib.gdr_bwd_static(ctypes.byref(desc(H=16, Hg=5)), *P, None) == -1
     with open(HEADER) as f:
         assert f"((size_t){gdr.STATIC_SCRATCH_BYTES >> 20} << 20)" in f.read()
+
+
+def test_from_states_argument_checks(lib):
+    """gdr_bwd_from_states validates on the host before touching the device:
+    the descriptor (state_v_first in {0, 1}), the per-chunk state count (fixed
+    length: exactly B ceil(T / chunk)) and the required pointers."""
+    P = ctypes.c_void_p
+    fake = P(0x10000)   # never dereferenced: every call below fails its host checks
+    bufs = [fake] * 8   # q, k, v, g, beta, do, dht, cu_seqlens
+    outs = [fake] * 6
+    d = desc(B=1, T=130, H=2, Hg=2)   # 3 chunks of 64
+    call = lambda dd, cu, h, n: lib.gdr_bwd_from_states(ctypes.byref(dd), *bufs[:7], cu, h, ctypes.c_int64(n),
+                                                        *outs, fake, ctypes.c_size_t(0), None)
+    assert gdr.check(desc(state_v_first=2)) == -1
+    assert call(d, None, fake, 2) == -1          # fixed length needs exactly 3 states
+    assert call(d, None, fake, 4) == -1
+    assert call(d, None, None, 3) == -1          # h required when there are tokens
+    assert call(d, None, fake, 3) == -3          # right count: then the (missing) workspace is the error
+    assert call(desc(state_v_first=3), None, fake, 3) == -1
