@@ -30,12 +30,14 @@
 //   2^(G_r - G_s) = Ein_r * phi_{b'+1} ... phi_{b-1} * Eout_s,
 // so the operands k Eout, q Ein, beta k Ein are scaled once per chunk and the
 // phi are applied to the accumulators between blocks (Horner); every exponent
-// is <= 0. Inside a diagonal block the source side needs 2^(G_16b - G_s) >= 1,
-// taken as the k Eout operand times 2^(G_16b - G_16(b+1)) on the accumulator
-// (the last block references its own last row); the MFMA form is used there
-// when the block's gate range, its next block's first row included, stays
-// within 2^64 (2^8 for fp16 operands) for every column of the wave, else an
-// exact VALU pass with one exp2 per (r, s, d). Finally
+// of these cross-block terms is <= 0. Inside a diagonal block the source side
+// needs 2^(G_16b - G_s) >= 1, taken as the k Eout operand times
+// 2^(G_16b - G_16(b+1)) on the accumulator (the last block references its own
+// last row): exp2 of a positive argument, up to the guard. The MFMA form is
+// used there when the block's gate range, its next block's first row
+// included, stays within 64 (8 for fp16 operands) for every column of the
+// wave, else an exact VALU pass with one exp2 per (r, s, d) of arguments <= 0
+// (the only form the bwd_intra page uses for diagonal blocks). Finally
 // dg = reverse cumsum of dG in the chunk (the page's fold_dg), dG_last collecting
 //   ln2 [2^G_last rowsum_v(h dh') + sum_r k_r dk~_r 2^(G_last - G_r)].
 #pragma once

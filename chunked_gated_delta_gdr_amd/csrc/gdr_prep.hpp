@@ -12,10 +12,13 @@
 //   k~    = k 2^(G_last - G),  q~ = q 2^G - Aqk w,  2^G_last.
 // Diagonal 16x16 blocks of Aqk/Akk use MFMA on operands scaled through the
 // block's first row b0: q_r 2^(G_r - G_b0) <= 1 against k_s 2^(G_b0 - G_s),
-// while the block's gate range |G_r - G_b0| stays within a bound that keeps
-// the second operand finite in the operand type (2^64 for bf16 / fp32, 2^8
-// for fp16); beyond it the block is formed per element, one decay per
-// (r, s, d), as a running product of per-token factors 2^g <= 1 along s.
+// whose exponent G_b0 - G_s is >= 0: a positive exponent, allowed only while
+// the block's gate range |G_r - G_b0| stays within a bound that keeps that
+// operand finite in the operand type (64, i.e. 2^64, for bf16 / fp32; 8 for
+// fp16). This departs from the bwd_intra page, which forms every diagonal
+// block per element with exponents <= 0 only; beyond the bound the block is
+// formed that way here too, one decay per (r, s, d), as a running product of
+// per-token factors 2^g <= 1 along s.
 // Off-diagonal blocks use MFMA on operands prescaled through the block
 // boundary rho = 16 i of the target row block: q 2^(G_r - G_rho) and
 // k 2^(G_rho - G_s), both exponents <= 0 (the per-block-boundary form of the

@@ -27,8 +27,14 @@
  *    for GDR_EHIP it also holds the HIP error text of the failing call
  *    (thread-local, until the next failing call on the same host thread).
  *  - Preconditions that are documented but not checked: g <= 0 elementwise
- *    (every exp2 argument the kernels form is then <= 0), finite inputs,
- *    non-overlapping output buffers, cu_seqlens non-decreasing on device.
+ *    (the gate decays; the off-diagonal exp2 arguments the kernels form are
+ *    then <= 0, the diagonal-block MFMA form uses arguments up to its guard,
+ *    see gdr_chunk_bwd.hpp), finite inputs, non-overlapping output buffers,
+ *    and on the device cu_seqlens[0] >= 0, cu_seqlens non-decreasing,
+ *    cu_seqlens[n_seqs] <= T. cu_seqlens values are clamped to [0, T] (each
+ *    end to at least its start) before any use, so a violation gives
+ *    meaningless results for the sequences concerned but never an access
+ *    outside the given buffers.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -105,12 +111,19 @@ int gdr_bwd_check(const gdr_bwd_desc_t* d);
 size_t gdr_bwd_workspace_bytes(const gdr_bwd_desc_t* d);
 
 /*
- * The backward pass. Inputs (device, read only):
+ * The backward pass: the argument list of the FlashQLA issue #30 page's
+ * fused_gdr_bwd wrapper (q, k, v, g, b, do, dht, scale, cu_seqlens,
+ * chunk_size) minus the forward-saved states it also takes (see
+ * gdr_bwd_from_states for that form), plus h0, which this call needs to
+ * recompute them; the outputs of the kernel_fun page's host wrapper
+ * chunk_kda_bwd_intra_cutedsl (dq, dk, db, dg, with the fold of dg into the
+ * raw-gate gradient) completed by dv and dh0. Inputs (device, read only):
  *   q, k        [B,T,Hg,K] io_dtype
  *   v, do_      [B,T,H,V]  io_dtype
  *   g           [B,T,H,K] (per channel) or [B,T,H] (scalar) fp32, raw log2 gate
  *   beta        [B,T,H]    io_dtype
  *   h0          [N,H,K,V]  fp32 initial states, N = n_seqs or B; NULL = zero
+ *               ([N,H,V,K] when d->state_v_first, as for dht and dh0)
  *   dht         [N,H,K,V]  fp32 gradient of the final states; NULL = zero
  *   cu_seqlens  int32 [n_seqs+1] (varlen) or NULL (fixed length)
  * Outputs (device, fully overwritten, never accumulated into):

@@ -4,6 +4,9 @@ max|gpu - ref| / max|ref| (the tolerance metric of the method's description:
 1e-4 for fp32 io, 2e-2 for bf16 / fp16 io)."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -89,3 +92,15 @@ def varlen_with_empty_sequences() -> dict:
     inp["h0"] = torch.randn(7, 2, 64, 64, generator=gen) * 0.1
     inp["dht"] = torch.randn(7, 2, 64, 64, generator=gen) * 0.1
     return inp
+
+
+def report(label: str, errs: dict, tol: float) -> None:
+    """Print the observed max relative error per output (and, when the
+    environment names a file in GDR_PARITY_LOG, append it there as a JSON line),
+    so that every parity margin against its bar is on record."""
+    line = f"parity {label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (bar {tol:g})"
+    print(line, flush=True)
+    path = os.environ.get("GDR_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": label, "tol": tol, "errs": errs}) + "\n")

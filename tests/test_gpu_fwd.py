@@ -58,6 +58,7 @@ def check(w, hks=None, with_h0=True):
         o, ht = o[:, :, hv], ht[:, hv]
     e = errs(o, ht, ro, rht, mask)
     tol = tu.tolerance(w)
+    tu.report(f"fwd {w.name} T={w.T} H={w.H}", e, tol)
     assert all(v <= tol for v in e.values()), f"{w.name}: {e} (tolerance {tol})"
 
 
@@ -96,6 +97,27 @@ def test_fwd_full_gdn_gqa_fp16():
 
 def test_fwd_full_kda_varlen():
     check(VARLEN, hks=[3])
+
+
+def test_fwd_full_kda_long():
+    check(WORKLOADS["kda_long"], hks=[7, 30])
+
+
+def test_fwd_varlen_more_sequences_than_one_table_pass():
+    """The forward pass over 300 packed sequences (the chunk table's multi-pass path)."""
+    gen = torch.Generator().manual_seed(62)
+    lens = torch.randint(1, 24, (300,), generator=gen)
+    cu = torch.zeros(301, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    w = scaled(VARLEN, T=int(cu[-1]), H=2, Hg=2, K=64, V=64, n_seqs=1, seed=62)
+    inp = make_inputs(w)
+    inp["cu_seqlens"] = cu
+    inp["h0"] = torch.randn(300, w.H, w.K, w.V, generator=gen) * 0.1
+    o, ht = run_fwd(inp)
+    ro, rht = ref_fwd(inp)
+    e = errs(o, ht, ro, rht, tu.real_token_mask(inp))
+    tu.report("fwd varlen 300 sequences", e, 2e-2)
+    assert all(v <= 2e-2 for v in e.values()), e
 
 
 def test_fwd_empty_input():

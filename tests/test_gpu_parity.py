@@ -18,6 +18,8 @@ tu = pytest.importorskip("gdr_testutil")
 
 
 def _check(errs, tol, label=""):
+    import os
+    tu.report(label or os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0], errs, tol)
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, f"{label} over tolerance {tol}: {bad} (all: {errs})"
 
@@ -259,3 +261,22 @@ def test_varlen_with_empty_sequences():
     got = tu.run_gpu(inp)
     for n in (0, 2, 3, 6):   # the empty sequences pass dht through
         assert torch.equal(got["dh0"][n], inp["dht"][n]), n
+
+
+def test_varlen_more_sequences_than_one_table_pass():
+    """300 packed sequences (lengths 1..23, K = V = 64): the chunk table takes
+    its sequences 256 at a time, so this runs its multi-pass path; every element
+    of every output compared."""
+    gen = torch.Generator().manual_seed(61)
+    lens = torch.randint(1, 24, (300,), generator=gen)
+    cu = torch.zeros(301, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    T = int(cu[-1])
+    w = scaled(VARLEN, T=T, H=2, Hg=2, K=64, V=64, n_seqs=1, seed=61)
+    inp = make_inputs(w)
+    inp["cu_seqlens"] = cu
+    inp["h0"] = torch.randn(300, w.H, w.K, w.V, generator=gen) * 0.1
+    inp["dht"] = torch.randn(300, w.H, w.K, w.V, generator=gen) * 0.1
+    gpu = tu.run_gpu(inp)
+    ref = tu.run_oracle(inp)
+    _check(tu.rel_errors(gpu, ref, tu.real_token_mask(inp)), tu.tolerance(w), "varlen 300 sequences")
