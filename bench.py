@@ -359,6 +359,57 @@ def bench_fwd(args, w, inp, t, tokens, n_chunks, n_seqs, ws) -> int:
     return 0
 
 
+def bench_fused(args, w, inp, t, tokens, n_chunks, n_seqs) -> int:
+    """The fused reverse backward (gdr_bwd_fused, chunk 32): the same backward
+    as the headline step with the reverse sweep and the chunk gradients in one
+    kernel per (sequence, value head); whole-call time with HIP events on the
+    launch stream, the method's bytes as for the step."""
+    import torch
+    import chunked_gated_delta_gdr_amd as gdr
+    dev = t["q"].device
+    out = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"]),
+           torch.empty_like(t["g"]), torch.empty_like(t["beta"]),
+           torch.empty((n_seqs, w.H, w.K, w.V), dtype=torch.float32, device=dev))
+    desc = gdr.make_desc(w.B, w.T, w.H, w.Hg, w.K, w.V, chunk=w.chunk, n_seqs=w.n_seqs,
+                         gate=0 if w.gate == "kda" else 1, io_dtype=w.io_dtype)
+    ws = torch.empty(int(gdr._load().gdr_bwd_fused_workspace_bytes(__import__("ctypes").byref(desc))),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        gdr.bwd_fused(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], h0=t["h0"], dht=t["dht"],
+                      cu_seqlens=t["cu_seqlens"], scale=inp["scale"], chunk_size=w.chunk, workspace=ws, out=out)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    costs = per_token_head_costs(w, n_chunks, n_seqs, tokens)
+    mb = costs["method_bytes"] * tokens * w.H
+    res = {
+        "metric": "gated-delta-rule bwd tokens/s (B*T), fused reverse kernel (chunk 32)",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[w.io_dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "fused", "tokens": tokens, "H": w.H, "Hg": w.Hg, "K": w.K,
+                   "V": w.V, "chunk": w.chunk, "gate": w.gate, "n_seqs": n_seqs,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "scope": "step", "achieved": mb / (ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": mb},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_train(args, w, inp, t, tokens, n_chunks, n_seqs, ws) -> int:
     """A training step's kernels: the forward pass, then the backward after it
     on the same workspace (gdr_bwd_after_fwd). Times each half and the pair
@@ -413,9 +464,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="kda_fixed_h16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("bwd", "fwd", "train"), default="bwd",
-                    help="bwd (the headline), fwd (the forward pass: o and final states) or "
-                         "train (the forward pass, then the backward after it on its workspace)")
+    ap.add_argument("--pass", dest="which", choices=("bwd", "fwd", "train", "fused"), default="bwd",
+                    help="bwd (the headline), fwd (the forward pass: o and final states), "
+                         "train (the forward pass, then the backward after it on its workspace) or "
+                         "fused (the backward through the fused reverse kernel, chunk 32 workloads)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after the timed steps, run a plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -465,6 +517,8 @@ def main() -> int:
         return bench_fwd(args, w, inp, t, tokens, n_chunks, n_seqs, ws)
     if args.which == "train":
         return bench_train(args, w, inp, t, tokens, n_chunks, n_seqs, ws)
+    if args.which == "fused":
+        return bench_fused(args, w, inp, t, tokens, n_chunks, n_seqs)
 
     def step(events=None):
         gdr.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], h0=t["h0"], dht=t["dht"],

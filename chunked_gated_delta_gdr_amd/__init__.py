@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["bwd", "bwd_after_fwd", "bwd_from_states", "bwd_static", "fwd", "workspace_bytes", "workspace_offsets",
+__all__ = ["bwd", "bwd_after_fwd", "bwd_from_states", "bwd_fused", "bwd_static", "fwd", "workspace_bytes", "workspace_offsets",
            "library_path", "Desc", "GATE_PER_CHANNEL", "GATE_SCALAR", "GdrError", "STATIC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,10 @@ def _load():
         lib.gdr_bwd_after_fwd.argtypes = [D] + [P] * 14 + [P, ctypes.c_size_t, P]
         lib.gdr_bwd_from_states.restype = ctypes.c_int
         lib.gdr_bwd_from_states.argtypes = [D] + [P] * 9 + [ctypes.c_int64] + [P] * 6 + [P, ctypes.c_size_t, P]
+        lib.gdr_bwd_fused.restype = ctypes.c_int
+        lib.gdr_bwd_fused.argtypes = [D] + [P] * 15 + [P, ctypes.c_size_t, P]
+        lib.gdr_bwd_fused_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdr_bwd_fused_workspace_bytes.argtypes = [D]
         lib.gdr_bwd_static.restype = ctypes.c_int
         lib.gdr_bwd_static.argtypes = [D] + [P] * 15 + [P]
         lib.gdr_strerror.restype = ctypes.c_char_p
@@ -267,6 +271,34 @@ def bwd_from_states(q, k, v, g, beta, do, h, dht=None, cu_seqlens=None, scale=No
                                  _ptr(do), _ptr(dht), _ptr(cu_seqlens), _ptr(h), ctypes.c_int64(n_h),
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0),
                                  _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise _err(rc)
+    return dq, dk, dv, dg, db, dh0
+
+
+def bwd_fused(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None,
+              chunk_size: int = 32, workspace: Optional[torch.Tensor] = None, out=None,
+              state_v_first: bool = False):
+    """:func:`bwd` through gdr_bwd_fused: one fused reverse kernel per
+    (sequence, value head) with the state gradient on chip (chunk 32 only).
+    ``workspace`` (uint8) needs gdr_bwd_fused_workspace_bytes bytes."""
+    lib = _load()
+    desc, N, H, K, V = _bwd_desc(q, k, v, g, beta, do, h0, dht, cu_seqlens, scale, chunk_size,
+                                 state_v_first)
+    nbytes = int(lib.gdr_bwd_fused_workspace_bytes(ctypes.byref(desc)))
+    if nbytes == 0:
+        raise GdrError(f"gdr_bwd_fused: unsupported descriptor (chunk {chunk_size}; built for 32)")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or
+          workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() < nbytes):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {q.device} with >= {nbytes} bytes")
+    dq, dk, dv, dg, db, dh0 = _grad_outputs(q, k, v, g, beta, N, H, K, V, out)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.gdr_bwd_fused(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(h0), _ptr(do), _ptr(dht), _ptr(cu_seqlens),
+                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0),
+                           _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
     if rc != 0:
         raise _err(rc)
     return dq, dk, dv, dg, db, dh0

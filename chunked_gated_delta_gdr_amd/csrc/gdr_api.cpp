@@ -100,6 +100,19 @@ size_t gdr_bwd_workspace_bytes(const gdr_bwd_desc_t* d) {
     return off[WS_COUNT];
 }
 
+// The fused reverse backward's workspace: the standard regions, then (GQA
+// only) fp32 dq and dk partials per value head, [B*T][H][K] each.
+static size_t fused_partial_bytes(const gdr_bwd_desc_t* d) {
+    return d->H > d->Hg ? align256((size_t)(d->B * d->T) * d->H * d->K * 4) : 0;
+}
+
+size_t gdr_bwd_fused_workspace_bytes(const gdr_bwd_desc_t* d) {
+    if (gdr_bwd_check(d) != GDR_OK || d->chunk != 32) return 0;
+    size_t off[WS_COUNT + 1];
+    layout(d, off);
+    return off[WS_COUNT] + 2 * fused_partial_bytes(d);
+}
+
 int gdr_bwd_workspace_offsets(const gdr_bwd_desc_t* d, size_t* offsets, int n) {
     const int rc = gdr_bwd_check(d);
     if (rc != GDR_OK) return rc;
@@ -246,6 +259,34 @@ int gdr_bwd_from_states(const gdr_bwd_desc_t* d, const void* q, const void* k, c
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.dout = do_; p.dht = dht;
     p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
     return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 0), p,
+                  stream, nullptr);
+}
+
+int gdr_bwd_fused(const gdr_bwd_desc_t* d, const void* q, const void* k, const void* v, const float* g,
+                  const void* beta, const float* h0, const void* do_, const float* dht,
+                  const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = gdr_bwd_check(d);
+    if (rc != GDR_OK) return rc;
+    if (d->chunk != 32) return GDR_EUNSUPPORTED;
+    if (!token_buffers_ok(d, {q, k, v, g, beta, do_, dq, dk, dv, dg, db})) return GDR_EINVAL;
+    if (!dh0 || !aligned16(dh0)) return GDR_EINVAL;
+    if ((h0 && !aligned16(h0)) || (dht && !aligned16(dht))) return GDR_EINVAL;
+    const size_t need = gdr_bwd_fused_workspace_bytes(d);
+    if (!workspace || workspace_bytes < need) return GDR_EWORKSPACE;
+    gdr::Params p;
+    rc = fill_params(d, cu_seqlens, workspace, workspace_bytes, p);
+    if (rc != GDR_OK) return rc;
+    size_t off[WS_COUNT + 1];
+    layout(d, off);
+    char* ws = static_cast<char*>(workspace);
+    p.dqp = reinterpret_cast<float*>(ws + off[WS_COUNT]);
+    p.dkp = reinterpret_cast<float*>(ws + off[WS_COUNT] + fused_partial_bytes(d));
+    p.dirs = 1;
+    p.dir0 = 0;   // the forward sweep alone: the reverse one runs inside the fused kernel
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = do_; p.dht = dht;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.db = db; p.dh0 = dh0;
+    return launch(gdr::find_launcher(d->io_dtype, d->chunk, d->K, d->gate == GDR_GATE_SCALAR, 2), p,
                   stream, nullptr);
 }
 

@@ -111,6 +111,13 @@ struct BwdLds {
     static constexpr size_t DVS_END = DVS + sz(C, LT, sizeof(T));
     static constexpr size_t U_BYTES = cmax(cmax(cmax(P1_END, P2_B_END), cmax(P2_X_END, E_END)), DVS_END);
     static constexpr size_t TOTAL = U_OFF + U_BYTES;
+    // the fused reverse kernel (state gradient on chip) adds: w rows [C][LT]
+    // (read as w^T through transposed loads), -T^T of the slice [BVS][LC],
+    // 2^G_last f32 [D]
+    static constexpr size_t F_W = TOTAL;
+    static constexpr size_t F_TT = F_W + sz(C, LT, sizeof(T));
+    static constexpr size_t F_GAM = F_TT + sz(BVS, LC, sizeof(T));
+    static constexpr size_t F_TOTAL = F_GAM + size_t(D) * 4;
     static_assert(P2_DA_END <= P2_T1T, "dAqk/dAkk operands must not overlap T1T");
     static_assert(size_t(4) * C * 16 <= sz(D, LC, sizeof(T)), "cumsum segment totals fit the dw region");
     static_assert(TOTAL <= 163840, "LDS budget of gdr_chunk_bwd");
@@ -175,18 +182,34 @@ template <typename T, int C>
 constexpr int resident_per_cu() { return C == 32 && sizeof(T) == 2 ? 2 : 1; }
 
 // Waves per SIMD of the gradient kernel (caps its registers): its C / 8 waves
-// times the workgroups a CU holds, over 4 SIMDs.
-template <typename T, int C, int D, bool SCALAR, bool GROUPED>
+// times the workgroups a CU holds, over 4 SIMDs (the fused reverse kernel: one
+// workgroup per CU).
+//
+// FUSED: the reverse state sweep runs inside the gradient kernel. One
+// workgroup per (sequence, value head) walks the sequence's chunks from the
+// last to the first, holding the state gradient dh (fp32, K x V) in the
+// accumulators of its waves: each chunk's body takes dh' = dh_{c+1} from them
+// (a bf16 copy per V slice in LDS), forms T = k~ dh' itself, and ends each
+// slice with the sweep's update dh_c = Diag(2^G_last) dh' - w^T T +
+// (scale q~)^T do on those accumulators, so neither dh nor T goes through
+// memory (the FlashQLA issue #30 page's fused design: the CONSUMER_S state
+// stays resident for the whole loop). The next chunk's inputs are requested in
+// the current chunk's epilogue. With GQA the value heads of a group are in
+// different workgroups: dq, dk go out as fp32 partials per value head and
+// gdr_group_sum adds them in group order.
+template <typename T, int C, int D, bool SCALAR, bool GROUPED, bool FUSED = false>
 __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
-    C / 32 * resident_per_cu<T, C>(), C / 32 * resident_per_cu<T, C>()))) void gdr_chunk_bwd(Params p) {
+    C / 32 * (FUSED ? 1 : resident_per_cu<T, C>()), C / 32 * (FUSED ? 1 : resident_per_cu<T, C>())))) void
+gdr_chunk_bwd(Params p) {
     using L = BwdLds<T, C, D>;
+    static_assert(!FUSED || (!GROUPED && L::F_TOTAL <= 163840), "fused reverse kernel: per value head, LDS budget");
     constexpr int NB = L::NB, NW = 2 * NB, NT = 64 * NW, BVS = L::BVS;
     constexpr int LT = L::LT, LC = L::LC, LB = L::LB, LF = L::LF;
     constexpr int DH2 = D / 2, CH2 = C / 2, VH2 = BVS / 2;    // column halves
     constexpr int NTD = DH2 / 16, NTC = CH2 / 16, NTV = VH2 / 16;
     constexpr int V8 = 16 / sizeof(T);
     static_assert(NTD >= 1 && NTC >= 1 && NTV >= 1 && D <= NT, "tiling");
-    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    __shared__ __attribute__((aligned(16))) char smem[FUSED ? L::F_TOTAL : L::TOTAL];
     T* const qL0 = reinterpret_cast<T*>(smem + L::Q_OFF);
     T* const kL0 = reinterpret_cast<T*>(smem + L::K_OFF);
     float* bs = reinterpret_cast<float*>(smem + L::BETA_OFF);
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             pv[i] = ld16(v + row);
             const int col = v0 + c;   // V-tiled: tile col / kTileV, column col % kTileV
             px[i] = ld16(xb + (size_t)(col / kTileV) * kTileV * C + r * kTileV + col % kTileV);
-            pt[i] = ld16(tb + (size_t)(col / kTileV) * kTileV * C + r * kTileV + col % kTileV);
+            if constexpr (!FUSED) pt[i] = ld16(tb + (size_t)(col / kTileV) * kTileV * C + r * kTileV + col % kTileV);
         }
 #pragma unroll
         for (int i = 0; i < NPD; ++i) {
@@ -260,7 +283,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             const int d = e / PR, c = (e % PR) * V8;
             const int col = v0 + c;   // V-tiled, as above
             ph[i] = ld16(hb + (size_t)(col / kTileV) * kTileV * D + d * kTileV + col % kTileV);
-            pdh[i] = ld16(dhb + (size_t)(col / kTileV) * kTileV * D + d * kTileV + col % kTileV);
+            if constexpr (!FUSED) pdh[i] = ld16(dhb + (size_t)(col / kTileV) * kTileV * D + d * kTileV + col % kTileV);
         }
     };
     // (tid, l, rows: the caller's thread, lane and first row of the wave; the
@@ -281,6 +304,34 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         request_slice(e2, jh2, h2, 0, tid);
 #pragma unroll
         for (int i = 0; i < NPD; ++i) pgl[i] = p.glast[jh2 * D + min((tid + NT * i) / PR, D - 1)];
+    };
+
+    // FUSED: the chunk operands of the state update and of T, requested with
+    // the rest of a head's inputs: rows r0.. of k~ and the wave's state rows of
+    // scale q~^T as MFMA fragments, and w (for w^T) as 16-byte pieces; the
+    // state gradient itself, the wave's RW row tiles x all column tiles
+    constexpr int NKD = D / KS;
+    constexpr int RW = FUSED ? (D / 16) / NW : 1, CWT = FUSED ? D / 16 : 1;
+    static_assert(!FUSED || RW * NW == D / 16, "state row tiles per wave");
+    Frag fKt[FUSED ? NKD : 1];
+    Frag fQs[RW][FUSED ? NKC : 1];
+    Vec16 pw[FUSED ? NQP : 1];
+    f32x4 dst[RW][CWT];
+    auto request_fused = [&](const size_t jh2, const int tid, const int l, const int rows,
+                             const int srows) __attribute__((always_inline)) {
+        if constexpr (FUSED) {
+            const T* ktp = static_cast<const T*>(p.kt) + jh2 * C * D;
+            const T* qsp = static_cast<const T*>(p.qsT) + jh2 * D * C;
+            const T* wp = static_cast<const T*>(p.w) + jh2 * C * D;
+#pragma unroll
+            for (int k2 = 0; k2 < NKD; ++k2) fKt[k2] = frag_fo<T, D>(ktp, rows, k2 * KS, l);
+#pragma unroll
+            for (int i = 0; i < RW; ++i)
+#pragma unroll
+                for (int k2 = 0; k2 < NKC; ++k2) fQs[i][k2] = frag_fo<T, C>(qsp, srows + 16 * i, k2 * KS, l);
+#pragma unroll
+            for (int i = 0; i < NQP; ++i) pw[i] = ld16(wp + (size_t)(tid + i * NT) * V8);   // fragment order
+        }
     };
 
     // GROUPED: fp32 group sums of dq, dk in this wave's accumulator tiles
@@ -381,6 +432,21 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                     fo_piece<T, C>(e, ar, ac);
                     st16(AmW + ar * LC + ac, pam[i]);
                 }
+                if constexpr (FUSED) {   // w rows (stored in fragment order) and 2^G_last
+                    T* wW = reinterpret_cast<T*>(smem + L::F_W);
+                    float* gam = reinterpret_cast<float*>(smem + L::F_GAM);
+#pragma unroll
+                    for (int i = 0; i < NQP; ++i) {
+                        int wr, wc;
+                        fo_piece<T, D>(tid + i * NT, wr, wc);
+                        st16(wW + wr * LT + wc, pw[i]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < NPD; ++i) {
+                        const int e = tid + NT * i;
+                        if (e < D * PR && e % PR == 0) gam[e / PR] = pgl[i];
+                    }
+                }
             }
 #pragma unroll
             for (int i = 0; i < NPC; ++i) {
@@ -392,7 +458,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                     st16(doL + r * LB + c, dv);
                     st16(vL + r * LB + c, vv);
                     st16(XL + r * LB + c, px[i]);
-                    st16(TL + r * LB + c, pt[i]);
+                    if constexpr (!FUSED) st16(TL + r * LB + c, pt[i]);
                 }
             }
 #pragma unroll
@@ -401,14 +467,26 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 if (e < D * PR) {
                     const int d = e / PR, c = (e % PR) * V8;
                     st16(hL + d * LB + c, ph[i]);
-                    st16(dhL + d * LB + c, pdh[i]);
-                    const T* ha = reinterpret_cast<const T*>(&ph[i]);
-                    const T* hb2 = reinterpret_cast<const T*>(&pdh[i]);
-                    float s2 = 0.f;
+                    if constexpr (!FUSED) {
+                        st16(dhL + d * LB + c, pdh[i]);
+                        const T* ha = reinterpret_cast<const T*>(&ph[i]);
+                        const T* hb2 = reinterpret_cast<const T*>(&pdh[i]);
+                        float s2 = 0.f;
 #pragma unroll
-                    for (int q2 = 0; q2 < V8; ++q2) s2 += to_f32(ha[q2]) * to_f32(hb2[q2]);
-                    hdh[i] += s2;
+                        for (int q2 = 0; q2 < V8; ++q2) s2 += to_f32(ha[q2]) * to_f32(hb2[q2]);
+                        hdh[i] += s2;
+                    }
                 }
+            }
+            if constexpr (FUSED) {   // dh' of the slice: the bf16 copy of the wave's state tiles
+#pragma unroll
+                for (int rt = 0; rt < RW; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < BVS / 16; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            dhL[(16 * (RW * w + rt) + acc_row(e, l)) * LB + 16 * ct + acc_col(l)] =
+                                from_f32<T>(dst[rt][v0 / 16 + ct][e]);
             }
             if (v0 + BVS < D) {
                 request_slice(ce, jh, h, v0 + BVS, tid);   // next slice
@@ -423,11 +501,40 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
             // dX = T + scale Aqk^T do  (own rows, own half of the slice)
             f32x4 dX[NTV];
+            if constexpr (FUSED) {
+                // T = k~ dh' on chip (dh' rows as B through transposed loads),
+                // kept as -T^T for the state update; rowsum(h dh') from LDS
+                T* TTw = reinterpret_cast<T*>(smem + L::F_TT);
 #pragma unroll
-            for (int t = 0; t < NTV; ++t) {
+                for (int t = 0; t < NTV; ++t) dX[t] = zero4();
+                panel_mma_ra<T, NTV, NKD, true>(dX, fKt, dhL, LB, cv0, l);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dX[t][i] = to_f32(TL[(r0 + acc_row(i, l)) * LB + cv0 + 16 * t + acc_col(l)]);
+                for (int t = 0; t < NTV; ++t) {
+                    const int c = cv0 + 16 * t + acc_col(l), rr = r0 + acc_row(0, l);
+                    store4<T>(TTw + c * LC + rr, -dX[t][0], -dX[t][1], -dX[t][2], -dX[t][3]);
+                }
+#pragma unroll
+                for (int i = 0; i < NPD; ++i) {
+                    const int e = tid + NT * i;
+                    if (e < D * PR) {
+                        const int d = e / PR, c = (e % PR) * V8;
+                        // both from LDS: the registers of h already hold the next slice
+                        const Vec16 hv = ld16(hL + d * LB + c), dhv = ld16(dhL + d * LB + c);
+                        const T* ha = reinterpret_cast<const T*>(&hv);
+                        const T* hb2 = reinterpret_cast<const T*>(&dhv);
+                        float s2 = 0.f;
+#pragma unroll
+                        for (int q2 = 0; q2 < V8; ++q2) s2 += to_f32(ha[q2]) * to_f32(hb2[q2]);
+                        hdh[i] += s2;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < NTV; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dX[t][i] = to_f32(TL[(r0 + acc_row(i, l)) * LB + cv0 + 16 * t + acc_col(l)]);
+                }
             }
             panel_mma_ra<T, NTV, NKC, true>(dX, fAq, doL, LB, cv0, l);   // do rows as B (transposed loads)
 #pragma unroll
@@ -467,6 +574,31 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                     const int r = r0 + acc_row(i, l);
                     dbp[i] += dvh[t][i] * to_f32(vL[r * LB + c]);
                     dvS[r * LT + v0 + c] = from_f32<T>(bs[r] * dvh[t][i]);
+                }
+            }
+            if constexpr (FUSED) {
+                // the reverse sweep's update of the slice's state columns:
+                // dh = Diag(2^G_last) dh' + (scale q~)^T do + w^T (-T)
+                const T* wL = reinterpret_cast<const T*>(smem + L::F_W);
+                const T* TTr = reinterpret_cast<const T*>(smem + L::F_TT);
+                const float* gam = reinterpret_cast<const float*>(smem + L::F_GAM);
+#pragma unroll
+                for (int rt = 0; rt < RW; ++rt) {
+                    const int d0 = 16 * (RW * w + rt);
+                    float gm[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gm[e] = gam[d0 + acc_row(e, l)];
+#pragma unroll
+                    for (int ct = 0; ct < BVS / 16; ++ct) {
+                        f32x4& sv = dst[rt][v0 / 16 + ct];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sv[e] *= gm[e];
+#pragma unroll
+                        for (int k2 = 0; k2 < NKC; ++k2) {
+                            sv = Mfma<T>::mma(fQs[rt][k2], frag_ks(doL, LB, 16 * ct, k2 * KS, l), sv);
+                            sv = Mfma<T>::mma(frag_ks(wL, LT, d0, k2 * KS, l), frag_kc(TTr, LC, 16 * ct, k2 * KS, l), sv);
+                        }
+                    }
                 }
             }
         }
@@ -1009,6 +1141,12 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                     if constexpr (GROUPED) {
                         dq_tot[t][i] += Pq[t][i];
                         dk_tot[t][i] += Pk[t][i];
+                    } else if (FUSED && p.G > 1) {   // fp32 partials of this value head
+                        if (r < len) {
+                            const size_t o = ((size_t)(tok0 + r) * p.H + h) * D + c;
+                            p.dqp[o] = Pq[t][i];
+                            p.dkp[o] = Pk[t][i];
+                        }
                     } else {
                         dqS[r * LT + c] = from_f32<T>(Pq[t][i]);
                         dkS[r * LT + c] = from_f32<T>(Pk[t][i]);
@@ -1026,7 +1164,9 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 }
             }
             __syncthreads();
-            if constexpr (!GROUPED) store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
+            if constexpr (!GROUPED) {
+                if (!FUSED || p.G == 1) store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
+            }
             if constexpr (!SCALAR) {
                 constexpr int NS = C * (D / 4) / NT;   // pieces per thread, read first
                 static_assert(NS * NT == C * (D / 4), "row piece split");
@@ -1079,6 +1219,48 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();
         store_rows<T, C, D, NT>(p, dqS, dkS, tok0, len, hk, tid);
+    } else if constexpr (FUSED) {
+        // one workgroup per (sequence n, value head h), chunks from the last to
+        // the first; dh starts as dht and ends as dh0
+        const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, hk = h / p.G, gi = h % p.G;
+        const int c0 = p.seq_off[n], c1 = p.seq_off[n + 1];
+        const size_t sh = ((size_t)n * p.H + h) * D * D;
+        const int l = lane_id();
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CWT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int d = 16 * (RW * w + rt) + acc_row(e, l), c = 16 * ct + acc_col(l);
+                    dst[rt][ct][e] = p.dht ? p.dht[sh + state_index<D>(p, d, c)] : 0.f;
+                }
+        if (c1 > c0) {
+            ChunkEntry ce = p.ctab[c1 - 1];
+            request_qk(ce, hk, threadIdx.x);
+            request_head(ce, c1 - 1, h, threadIdx.x, l, r0);
+            request_fused((size_t)(c1 - 1) * p.H + h, threadIdx.x, l, r0, 16 * RW * w);
+#pragma unroll 1
+            for (int j = c1 - 1; j >= c0; --j) {
+                const int jn = j > c0 ? j - 1 : j;   // past the first chunk: a redundant valid request
+                const ChunkEntry ce_n = p.ctab[jn];
+                head(j, hk, gi, ce, true, [&](const int tid, const int l2, const int rows) __attribute__((always_inline)) {
+                    request_qk(ce_n, hk, tid);
+                    request_head(ce_n, jn, h, tid, l2, rows);
+                    request_fused((size_t)jn * p.H + h, tid, l2, rows, 16 * RW * (tid >> 6));
+                });
+                ce = ce_n;
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CWT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int d = 16 * (RW * w + rt) + acc_row(e, l), c = 16 * ct + acc_col(l);
+                    p.dh0[sh + state_index<D>(p, d, c)] = dst[rt][ct][e];
+                }
     } else {
         // persistent: at most one workgroup per CU walks the (chunk, head)
         // items blockIdx.x, + gridDim.x, ...; the next item's first requests go
@@ -1100,6 +1282,33 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             ce = ce_n;
         }
     }
+}
+
+// dq, dk of the fused reverse kernel with GQA: the fp32 partials of the value
+// heads of each group added in group order (deterministic), rounded once to
+// the io type. One thread per 4 consecutive columns of a (token, q/k head);
+// varlen tokens outside [cu_seqlens[0], cu_seqlens[n]) are not written.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gdr_group_sum(Params p) {
+    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (size_t)(p.B * p.T) * p.Hg * (D / 4)) return;
+    const int c = (int)(e % (D / 4)) * 4;
+    const size_t th = e / (D / 4);
+    const int hk = (int)(th % p.Hg);
+    const int tok = (int)(th / p.Hg);
+    if (p.varlen) {
+        const int nt = (int)p.T, a = min(max(p.cu[0], 0), nt), b = min(max(p.cu[p.N], a), nt);
+        if (tok < a || tok >= b) return;
+    }
+    f32x4 sq = zero4(), sk = zero4();
+    for (int gi = 0; gi < p.G; ++gi) {
+        const size_t o = ((size_t)tok * p.H + hk * p.G + gi) * D + c;
+        sq += *reinterpret_cast<const f32x4*>(p.dqp + o);
+        sk += *reinterpret_cast<const f32x4*>(p.dkp + o);
+    }
+    const size_t oo = ((size_t)tok * p.Hg + hk) * D + c;
+    store4<T>(static_cast<T*>(p.dq) + oo, sq[0], sq[1], sq[2], sq[3]);
+    store4<T>(static_cast<T*>(p.dk) + oo, sk[0], sk[1], sk[2], sk[3]);
 }
 
 }  // namespace gdr

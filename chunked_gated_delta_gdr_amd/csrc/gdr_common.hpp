@@ -425,6 +425,8 @@ struct Params {
     // [nh_src][H][K][V] ([..][V][K] with vfirst) in the io type
     const void* hsrc;
     int nh_src;          // chunk states the caller's buffer holds
+    // fused reverse backward with GQA: fp32 dq, dk per value head [B*T][H][K]
+    float* dqp; float* dkp;
     // inputs
     const void* q; const void* k; const void* v; const float* g; const void* beta;
     const float* h0; const void* dout; const float* dht; const int* cu;

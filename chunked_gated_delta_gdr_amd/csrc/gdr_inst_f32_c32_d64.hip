@@ -1,8 +1,10 @@
-// Explicit instantiation: io dtype float, chunk 32, K = V = 64, both gate forms, both passes.
+// Explicit instantiation: io dtype float, chunk 32, K = V = 64, both gate forms, both passes and the fused reverse backward.
 #include "gdr_launch.hpp"
 namespace gdr {
 template hipError_t launch_bwd<float, 32, 64, false>(const Params&, hipStream_t, hipEvent_t const*);
 template hipError_t launch_fwd<float, 32, 64, false>(const Params&, hipStream_t, hipEvent_t const*);
 template hipError_t launch_bwd<float, 32, 64, true>(const Params&, hipStream_t, hipEvent_t const*);
 template hipError_t launch_fwd<float, 32, 64, true>(const Params&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_fused<float, 32, 64, false>(const Params&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_fused<float, 32, 64, true>(const Params&, hipStream_t, hipEvent_t const*);
 }  // namespace gdr

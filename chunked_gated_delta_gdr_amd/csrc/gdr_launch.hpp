@@ -105,6 +105,28 @@ hipError_t launch_bwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
     return le != hipSuccess ? le : e;
 }
 
+// The fused reverse backward (chunk 32): chunk table, preparation and the
+// forward sweep alone (p.dirs == 1, p.dir0 == 0: h and X), then one gradient
+// workgroup per (sequence, value head) that runs the reverse sweep itself with
+// the state gradient on chip, then, with GQA, the fp32 group sums of dq, dk.
+template <typename T, int C, int D, bool SCALAR>
+hipError_t launch_fused(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
+    hipError_t e = launch_front<T, C, D, SCALAR>(p, stream, ev);
+    if constexpr (C == 32) {
+        // always launched: with no chunks it still writes dh0 = dht
+        gdr_chunk_bwd<T, C, D, SCALAR, false, true><<<dim3(p.N * p.H), dim3(128 * (C / 16)), 0, stream>>>(p);
+        if (p.G > 1 && p.B * p.T > 0) {
+            const size_t n = (size_t)(p.B * p.T) * p.Hg * (D / 4);
+            gdr_group_sum<T, D><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(p);
+        }
+    } else {
+        return hipErrorInvalidValue;   // not built: its LDS plan needs chunk 32
+    }
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[4], stream);
+    const hipError_t le = hipGetLastError();
+    return le != hipSuccess ? le : e;
+}
+
 // The forward pass (p.dirs == 1): the same front, then the output kernel.
 template <typename T, int C, int D, bool SCALAR>
 hipError_t launch_fwd(const Params& p, hipStream_t stream, hipEvent_t const* ev) {
@@ -116,7 +138,7 @@ hipError_t launch_fwd(const Params& p, hipStream_t stream, hipEvent_t const* ev)
 }
 
 // Instantiated in gdr_inst_*.hip; looked up by the C ABI.
-// pass: 0 = backward, 1 = forward.
+// pass: 0 = backward, 1 = forward, 2 = fused reverse backward (chunk 32 only).
 LaunchFn find_launcher(int io_dtype, int chunk, int dim, int scalar, int pass);
 
 }  // namespace gdr

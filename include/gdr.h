@@ -234,6 +234,30 @@ int gdr_bwd_from_states(const gdr_bwd_desc_t* d,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The backward as one fused reverse kernel per (sequence, value head) with the
+ * state gradient resident on chip (the FlashQLA issue #30 page's single fused
+ * backward kernel, whose state-gradient role keeps dh in registers for the
+ * whole loop over chunks): the chunk table, the preparation and the forward
+ * state sweep run as in gdr_bwd, then each workgroup walks its sequence's
+ * chunks from the last to the first, computing that chunk's gradients and the
+ * reverse sweep's update of dh without writing dh (or T = k~ dh) to memory.
+ * With GQA, dq and dk of the value heads of a group are added in fp32 by a
+ * second small kernel, in group order. Built for chunk == 32 only (its LDS
+ * plan): other chunks return GDR_EUNSUPPORTED. Same arguments, outputs and
+ * error codes as gdr_bwd; the workspace must hold
+ * gdr_bwd_fused_workspace_bytes(d) bytes (gdr_bwd's regions plus, with GQA,
+ * the fp32 partials of dq and dk). The results match gdr_bwd's within the
+ * rounding of the io type (the reductions are ordered differently).
+ */
+size_t gdr_bwd_fused_workspace_bytes(const gdr_bwd_desc_t* d);
+int gdr_bwd_fused(const gdr_bwd_desc_t* d,
+                  const void* q, const void* k, const void* v, const float* g,
+                  const void* beta, const float* h0, const void* do_, const float* dht,
+                  const int32_t* cu_seqlens,
+                  void* dq, void* dk, void* dv, float* dg, void* db, float* dh0,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Byte offsets of the workspace regions for descriptor d, in this order:
  *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A,
  *   4 (empty: A^T is taken from A; kept so that the numbering holds),
