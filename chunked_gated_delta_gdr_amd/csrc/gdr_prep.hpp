@@ -23,6 +23,12 @@
 // boundary rho = 16 i of the target row block: q 2^(G_r - G_rho) and
 // k 2^(G_rho - G_s), both exponents <= 0 (the per-block-boundary form of the
 // bwd_intra page).
+// At C = 64 a chunk whose every |G_r - G_last / 2| is within that same bound
+// takes a shorter route instead: all of Aqk and Akk as two masked C x C
+// products over D, on operands scaled once through the one reference
+// G_last / 2 per column (exponents of either sign, bounded as above). The
+// bound is checked per chunk from its cumsum; a chunk beyond it takes the
+// per-boundary route.
 #pragma once
 #include "gdr_common.hpp"
 
@@ -96,17 +102,22 @@ struct PrepLds {
     static constexpr int LCF = C + 4;         // f32 [*][C]
     static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
     static constexpr size_t G_OFF = 0;
-    static constexpr size_t X_OFF = G_OFF + size_t(C) * LF * 4;
+    static constexpr size_t Q_OFF = G_OFF + size_t(C) * LF * 4;
+    static constexpr size_t K_OFF = Q_OFF + size_t(C) * LT * sizeof(T);
+    static constexpr size_t X_OFF = K_OFF + size_t(C) * LT * sizeof(T);
     static constexpr size_t X_BYTES = cmax(cmax(size_t(C) * LF * 4, size_t(C + 16) * LT * sizeof(T)),
                                            size_t(D) * LC * sizeof(T));
-    static constexpr size_t Q_OFF = X_OFF + X_BYTES;
-    static constexpr size_t K_OFF = Q_OFF + size_t(C) * LT * sizeof(T);
-    static constexpr size_t AQK_OFF = K_OFF + size_t(C) * LT * sizeof(T);
+    static constexpr size_t AQK_OFF = X_OFF + X_BYTES;
     static constexpr size_t AKK_OFF = AQK_OFF + size_t(C) * LCF * 4;
     static constexpr size_t AF_OFF = AKK_OFF + size_t(C) * LCF * 4;
     static constexpr size_t SCR_OFF = AF_OFF + size_t(C) * LCF * 4;
-    static constexpr size_t BETA_OFF = SCR_OFF + size_t(NB) * 16 * 20 * 4;
+    static constexpr size_t FLAG_OFF = SCR_OFF + size_t(NB) * 16 * 20 * 4;     // f32 [NW]: per wave, max |G_r - G_last / 2|
+    static constexpr size_t BETA_OFF = FLAG_OFF + size_t(NW) * 4;
     static constexpr size_t TOTAL = BETA_OFF + size_t(C) * 4;
+    // the one-reference form of Aqk / Akk (phases 2-3) keeps its three [C][LT]
+    // operands in the X region and the Aqk / Akk regions that follow it (the
+    // products land there after a barrier); A's region stays untouched
+    static constexpr bool FAST = C == 64 && 3 * size_t(C) * LT * sizeof(T) <= AF_OFF - X_OFF;
     // after the inverse, A and Aqk are converted in place to MFMA operands
     static_assert(size_t(C) * LC * sizeof(T) <= size_t(C) * LCF * 4, "A/Aqk in place");
     static_assert(size_t(NB) * 16 * 20 >= size_t(NT > D ? NT : D) * 1, "cumsum scratch");
@@ -147,8 +158,27 @@ __device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
 }
 
 // STORE_A2T: also store w^T and k~^T (for a sweep that does not form them).
+// Diagonal block m of A = (I + Akk)^-1 by forward substitution: column jj
+// (one per lane) from the strictly lower part of Akk's block m (row pitch LCF).
+template <int LCF>
+__device__ __forceinline__ void diag_block_inverse(const float* akk, float* a, const int m, const int jj) {
+    const int b0 = 16 * m;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float acc = (r == jj) ? 1.f : 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < r; ++s2) acc -= akk[(b0 + r) * LCF + b0 + s2] * x[s2];
+        x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[(b0 + r) * LCF + b0 + jj] = x[r];
+}
+
+// Two waves per SIMD: at C = 64 the one 8-wave workgroup a CU holds; at
+// C = 32 two 4-wave workgroups per CU, which needs VGPRs + AGPRs <= 256.
 template <typename T, int C, int D, bool SCALAR, bool STORE_A2T>
-__global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
+__global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdr_prep(Params p) {
     using L = PrepLds<T, C, D>;
     constexpr int NB = L::NB, NT = L::NT, LT = L::LT, LC = L::LC, LF = L::LF, LCF = L::LCF;
     constexpr int NTD = D / 16;  // column tiles of a [C][D] product
@@ -163,6 +193,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     float* AkkF = reinterpret_cast<float*>(smem + L::AKK_OFF);
     float* AF = reinterpret_cast<float*>(smem + L::AF_OFF);
     float* scr = reinterpret_cast<float*>(smem + L::SCR_OFF);
+    float* flags = reinterpret_cast<float*>(smem + L::FLAG_OFF);
     float* bs = reinterpret_cast<float*>(smem + L::BETA_OFF);
 
     // Persistent: at most one workgroup per CU walks the (chunk, value head)
@@ -214,7 +245,12 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             vpre[i] = ld16(v + ((size_t)(e2.tok0 + rt) * p.H + hh) * D + d0);
         }
     };
+    // The chunk entries are requested an item ahead of their use: a vector
+    // load of the next item's entry at the top of an item would make its wait
+    // (memory counters retire in order) also wait for all of the previous
+    // item's output stores.
     ChunkEntry ce = p.ctab[item / p.H];
+    ChunkEntry ce_n = p.ctab[min(item + (int)gridDim.x, nit - 1) / p.H];
     load_in(item, ce);
     load_v(item, ce);
 
@@ -223,7 +259,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     const int tok0 = ce.tok0, len = ce.len;
     const size_t jh = size_t(j) * p.H + h;
     const int nxt = min(item + (int)gridDim.x, nit - 1);   // past the end: a redundant valid load
-    const ChunkEntry ce_n = p.ctab[nxt / p.H];
+    const ChunkEntry ce_nn = p.ctab[min(item + 2 * (int)gridDim.x, nit - 1) / p.H];
     // a fresh opaque thread index per item: thread-dependent address arithmetic
     // is recomputed in every item instead of being kept live across items
     const int tid = [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }();
@@ -231,10 +267,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     __syncthreads();  // the previous item's LDS use is over
 
     // ---- phase 1: this item's inputs (already in registers) to LDS ----
+    // A above its diagonal blocks stays zero; so does Aqk above its diagonal,
+    // which the one-reference form writes itself (its operands overlay Aqk)
     for (int e = tid; e < C * LCF / 4; e += NT) {
-        reinterpret_cast<f32x4*>(AqkF)[e] = zero4();
-        reinterpret_cast<f32x4*>(AkkF)[e] = zero4();
         reinterpret_cast<f32x4*>(AF)[e] = zero4();
+        if constexpr (!L::FAST) reinterpret_cast<f32x4*>(AqkF)[e] = zero4();
     }
 #pragma unroll
     for (int i = 0; i < NGP; ++i) {
@@ -251,7 +288,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         st16(kL + r * LT + d0, r < len ? kpre[i] : Vec16{});
     }
     if (tid < C) bs[tid] = tid < len ? bpre : 0.f;
-    load_in(nxt, ce_n);  // the next item's g, q, k, beta
+    if constexpr (!L::FAST) load_in(nxt, ce_n);  // the next item's g, q, k, beta
     __syncthreads();
     {   // column cumsum in NSEG segments of SR rows: local scans, then segment offsets
         constexpr int NSEG = NT / D > 0 ? NT / D : 1, SR = C / NSEG;
@@ -269,19 +306,172 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             segtot[sg * D + d] = gv[SR - 1];
         }
         __syncthreads();
+        float dev = 0.f;   // the largest |G_r - G_last / 2| of the thread's rows
         if (sg < NSEG) {
-            float off = 0.f;   // all segment totals read (one wait), the earlier ones summed
+            float off = 0.f, tot = 0.f;   // all segment totals read (one wait), the earlier ones summed
 #pragma unroll
-            for (int s2 = 0; s2 < NSEG - 1; ++s2) {
+            for (int s2 = 0; s2 < NSEG; ++s2) {
                 const float x = segtot[s2 * D + d];
                 off += s2 < sg ? x : 0.f;
+                tot += x;
             }
 #pragma unroll
-            for (int i = 0; i < SR; ++i) Gs[(sg * SR + i) * LF + d] = gv[i] + off;
+            for (int i = 0; i < SR; ++i) {
+                const float G = gv[i] + off;
+                Gs[(sg * SR + i) * LF + d] = G;
+                if constexpr (L::FAST) dev = fmaxf(dev, fabsf(G - 0.5f * tot));
+            }
+        }
+        if constexpr (L::FAST) {
+            dev = wave_max(dev);
+            if ((tid & 63) == 0) flags[w] = dev;
         }
         __syncthreads();
     }
+    // Whether every |G_r - G_last / 2| of the chunk is within the guard of the
+    // MFMA form (a decaying column qualifies when its range -G_last is at most
+    // twice the guard): then all of Aqk and Akk are formed through that one
+    // reference per column; else through the block boundaries and the
+    // diagonal blocks' own rows, as below.
+    bool fast = false;
+    if constexpr (L::FAST) {
+        constexpr float guard = __is_same(T, _Float16) ? 8.f : 64.f;
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < L::NW; ++i) m = fmaxf(m, flags[i]);
+        fast = m <= guard;
+    }
 
+    // 4a (of the inverse below): the diagonal blocks of A = (I + Akk)^-1. The
+    // per-boundary path runs them for all blocks in the last wave (lanes
+    // 0..C-1) during its first product round, where that wave has no tile;
+    // the one-reference path in the waves that form Akk's diagonal blocks.
+    // (written out here rather than through diag_block_inverse: at C = 32 the
+    // call form raised the kernel's registers past two waves per SIMD)
+    auto diag_inverse = [&](const int lane) __attribute__((always_inline)) {
+        if (lane < C) {
+            const int m = lane >> 4, jj = lane & 15, b0 = 16 * m;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == jj) ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc -= AkkF[(b0 + r) * LCF + b0 + s2] * x[s2];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) AF[(b0 + r) * LCF + b0 + jj] = x[r];
+        }
+    };
+
+    if (fast) {
+        // ---- phases 2-3, one reference per column: every element of Aqk and
+        //      Akk on MFMA from q 2^(G - G_m), k 2^(G - G_m) and k 2^(G_m - G)
+        //      with G_m = G_last / 2 (the reference cancels in each channel's
+        //      term q_r,d k_s,d 2^(G_r,d - G_s,d)). The exponents G_r - G_m
+        //      take either sign; the check above bounds them by the guard, so
+        //      the scaled operands stay finite and normal in T, as in the
+        //      diagonal-block form below, here for the whole chunk at once.
+        //      Each term is still one product of two rounded operands. ----
+        T* xq = reinterpret_cast<T*>(smem + L::X_OFF);   // [C][LT] each
+        T* xkq = xq + C * LT;
+        T* xk = xkq + C * LT;
+        {   // all LDS reads of the thread's pieces first (one wait), then the writes
+            constexpr int NP = C * (D / 8) / NT;
+            static_assert(NP * NT == C * (D / 8), "piece split");
+            static_assert(NT % (D / 8) == 0, "a thread's pieces share their columns");
+            struct Raw8 { T v[8]; };   // 8 elements as stored
+            float gv[NP][8], gl[8];
+            Raw8 qr[NP], kr[NP];
+            load8f(Gs + (C - 1) * LF + (tid % (D / 8)) * 8, gl);
+#pragma unroll
+            for (int it = 0; it < NP; ++it) {
+                const int e = tid + it * NT, r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+                load8f(Gs + r * LF + d0, gv[it]);
+                qr[it] = *reinterpret_cast<const Raw8*>(qL + r * LT + d0);
+                kr[it] = *reinterpret_cast<const Raw8*>(kL + r * LT + d0);
+            }
+#pragma unroll
+            for (int it = 0; it < NP; ++it) {
+                const int e = tid + it * NT, r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+                float a[8], b[8], c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float x = gv[it][i] - 0.5f * gl[i];
+                    const float ex = fast_exp2(x), exi = fast_exp2(-x);
+                    const float qv = to_f32(qr[it].v[i]), kv = to_f32(kr[it].v[i]);
+                    a[i] = qv * ex;
+                    b[i] = kv * ex;
+                    c[i] = kv * exi;
+                }
+                store8<T>(xq + r * LT + d0, a);
+                store8<T>(xkq + r * LT + d0, b);
+                store8<T>(xk + r * LT + d0, c);
+            }
+        }
+        __syncthreads();
+        // the lower 16 x 16 tiles of Aqk (which 0) and Akk (which 1), spread over the waves
+        constexpr int NLT = NB * (NB + 1) / 2, NTI = 2 * NLT, TPW = (NTI + L::NW - 1) / L::NW;
+        auto tile_ij = [](int tt, int& bi, int& bj) {   // row-major order of the lower triangle
+            bi = 0;
+            while ((bi + 1) * (bi + 2) / 2 <= tt) ++bi;
+            bj = tt - bi * (bi + 1) / 2;
+        };
+        f32x4 accT[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = w + L::NW * i;
+            accT[i] = zero4();
+            if (t < NTI) {
+                int bi, bj;
+                tile_ij(t % NLT, bi, bj);
+                f32x4 a1[1] = {zero4()};
+                panel_mma<T, 1, D>(a1, t >= NLT ? xkq : xq, LT, 16 * bi, xk, LT, 16 * bj, l);
+                accT[i] = a1[0];
+            }
+        }
+        __syncthreads();   // the operand reads are done: Aqk and Akk overlay them
+        int mydiag = -1;   // the Akk diagonal block this wave formed, if any
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = w + L::NW * i;
+            if (t < NTI) {
+                const bool kk = t >= NLT;
+                int bi, bj;
+                tile_ij(t % NLT, bi, bj);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * bi + acc_row(e, l), s2 = 16 * bj + acc_col(l);
+                    if (kk) AkkF[r * LCF + s2] = s2 < r ? bs[r] * accT[i][e] : 0.f;
+                    else AqkF[r * LCF + s2] = s2 <= r ? accT[i][e] : 0.f;
+                }
+                if (kk && bi == bj) mydiag = bi;
+            }
+        }
+        if (mydiag >= 0) {   // its inverse, from the wave's own writes
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (l < 16) diag_block_inverse<LCF>(AkkF, AF, mydiag, l);
+        }
+        // the tiles of Aqk above the diagonal are zero
+        for (int t = w; t < NB * (NB - 1) / 2; t += L::NW) {
+            int bi, bj;
+            tile_ij(t, bi, bj);   // (bi, bj) of the strict lower triangle, shifted: (bj, bi + 1)
+            const int ti = bj, tj = bi + 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) AqkF[(16 * ti + acc_row(e, l)) * LCF + 16 * tj + acc_col(l)] = 0.f;
+        }
+        __syncthreads();
+    } else {
+    // Aqk above its diagonal is zero (no thread of phases 2-3 writes there;
+    // below it and on it they write every element, as they do in Akk's
+    // strictly lower part, the only part of Akk that is read)
+    if constexpr (L::FAST) {
+        for (int e = tid; e < C * C; e += NT) {
+            const int r = e / C, s2 = e % C;
+            if (s2 > r) AqkF[r * LCF + s2] = 0.f;
+        }
+    }
     // ---- phase 2: diagonal 16x16 blocks; wave w -> block w % NB, Aqk (w < NB) or Akk ----
     const bool is_kk = w >= NB;
     bool diag_mfma;
@@ -395,26 +585,6 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     }
     __syncthreads();
 
-    // 4a (of the inverse below): the diagonal blocks of A = (I + Akk)^-1 by
-    // forward substitution, one column per lane (lanes 0..C-1 of the wave that
-    // calls it). It needs only the diagonal blocks of Akk, so the last wave runs
-    // it during the first product round of phase 3, where it has no tile.
-    auto diag_inverse = [&](const int lane) __attribute__((always_inline)) {
-        if (lane < C) {
-            const int m = lane >> 4, jj = lane & 15, b0 = 16 * m;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == jj) ? 1.f : 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < r; ++s2) acc -= AkkF[(b0 + r) * LCF + b0 + s2] * x[s2];
-                x[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) AF[(b0 + r) * LCF + b0 + jj] = x[r];
-        }
-    };
-
     // ---- phase 3: off-diagonal blocks through the boundary rho = 16 i (MFMA) ----
     // For boundary i: q_r 2^(G_r - G_rho) and k_r 2^(G_r - G_rho) of block i,
     // k_s 2^(G_rho - G_s) of the rows s < rho, then the block products. Two
@@ -489,6 +659,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
             for (int ib = 1; ib < NB; ++ib) pass(std::integral_constant<int, 1>{}, ib, ib == 1);
         }
     }
+    }   // per-boundary path
 
     // ---- phase 4: A = (I + Akk)^-1 (4a, the diagonal blocks, ran in phase 3) ----
     // 4b: block rows: A_ij = -A_ii * sum_{kb=j}^{i-1} L_i,kb A_kb,j  (fp32 MFMA).
@@ -518,6 +689,11 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
     }
     __syncthreads();
 
+    // the next item's g, q, k, beta: with the one-reference form compiled in,
+    // requested here rather than in phase 1 (their registers are then free
+    // during phases 1-4, which that form needs; the loads still have most of
+    // an item to arrive)
+    if constexpr (L::FAST) load_in(nxt, ce_n);
     // ---- phase 5: A and scale Aqk^T to the workspace in 8-element row
     //      pieces (the gradient kernel takes A^T from its LDS copy of A through
     //      transposed loads); A and Aqk in place as MFMA operands in LDS ----
@@ -733,6 +909,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void gdr_prep(Params p) {
         for (int d = tid; d < D; d += NT) p.glast[jh * D + d] = fast_exp2(Gs[(C - 1) * LF + d]);
     }
     ce = ce_n;
+    ce_n = ce_nn;
     }
 }
 

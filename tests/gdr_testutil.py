@@ -104,3 +104,21 @@ def report(label: str, errs: dict, tol: float) -> None:
     if path:
         with open(path, "a") as f:
             f.write(json.dumps({"case": label, "tol": tol, "errs": errs}) + "\n")
+
+
+def one_reference_split(w: Workload, guard: float) -> tuple[int, int]:
+    """(chunk, head) items on each side of the preparation kernel's
+    one-reference bound: max over rows r and channels of |G_r - G_last / 2|,
+    with G the chunk-local cumsum of the raw gate, at most `guard` or not.
+    Computed from the seeded inputs on the host (fixed-length workloads)."""
+    g = make_inputs(w)["g"].double()
+    if g.dim() == 3:
+        g = g.unsqueeze(-1)
+    fast = slow = 0
+    for b in range(g.shape[0]):
+        for c0 in range(0, g.shape[1], w.chunk):
+            G = g[b, c0:c0 + w.chunk].cumsum(0)
+            dev = (G - 0.5 * G[-1:]).abs().amax(dim=(0, 2))
+            fast += int((dev <= guard).sum())
+            slow += int((dev > guard).sum())
+    return fast, slow

@@ -121,6 +121,22 @@ def test_f16_diagonal_guard_mixed():
     _check(tu.parity(w), tu.tolerance(w))
 
 
+@pytest.mark.parametrize("dtype,gate_mult,guard", [(torch.bfloat16, 2.0, 64.0), (torch.float16, 0.25, 8.0),
+                                                     (torch.float32, 2.4, 64.0)])
+def test_prep_one_reference_bound_mixed(dtype, gate_mult, guard):
+    """Chunk 64: the preparation kernel forms Aqk / Akk through one reference
+    G_last / 2 per column when every |G_r - G_last / 2| is within the operand
+    guard, else through the block boundaries. Gates chosen so that one launch
+    holds (chunk, head) items of both kinds."""
+    if dtype == torch.float32:
+        w = scaled(TINY, T=130, gate_mult=gate_mult, h0_std=0.1, dht_std=0.1, seed=57)
+    else:
+        w = scaled(KDA16, B=1, T=200, H=3, Hg=3, io_dtype=dtype, gate_mult=gate_mult, dht_std=0.1, seed=53)
+    fast, slow = tu.one_reference_split(w, guard)
+    assert fast > 0 and slow > 0, (fast, slow)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
 def test_gdn_gqa_huge_gates():
     """Scalar gate, GQA, C = 32, gates large enough for the exact diagonal path."""
     w = scaled(GDN, B=1, T=150, H=4, Hg=2, gate_mult=8.0, seed=43)
