@@ -165,6 +165,28 @@ constexpr int do_pitch() { return BV + (sizeof(T) == 2 ? 16 : 4); }
 template <typename T, int C>
 constexpr bool do_rows() { return sizeof(T) == 2 && C == 32; }
 
+// 64-column tiles with 16-bit operands copy the state and X / T out with
+// 16-bit reads, 8 rows per thread piece, rows 8 apart: at the padded row
+// pitches those rows share one LDS bank (and the C = 64 reverse direction
+// writes do^T the same way). So at C = 64 these buffers hold element
+// (row c, index k) at c * pitch + (k ^ swz(c)), an XOR of k's 8-element
+// groups by c / 8 (limited to the K / 8 groups of the index range K): the
+// 8-element MFMA fragment reads and 4-element writes stay contiguous, and the
+// eight rows of a copy-out read fall in distinct banks (varlen workload sweep
+// 675 -> 600 us). At C = 32 the same layout measured slower (1176 -> 1211 us),
+// so it is not used there.
+template <typename T, int C, int BV, int K>
+__device__ __forceinline__ int sweep_swz(int c) {
+    if constexpr (sizeof(T) == 2 && BV == 64 && C == 64) return 8 * ((c >> 3) & ((K / 8 < 8 ? K / 8 : 8) - 1));
+    else return 0;
+}
+// frag_kc on a buffer laid out as above
+template <typename T, int C, int BV, int K>
+__device__ __forceinline__ typename Mfma<T>::frag frag_kc_swz(const T* p, int ld, int i0, int k0, int l = lane_id()) {
+    const int i = i0 + (l & 15), k = k0 + (l >> 4) * Mfma<T>::KL;
+    return *reinterpret_cast<const typename Mfma<T>::frag*>(p + (long)i * ld + (k ^ sweep_swz<T, C, BV, K>(i)));
+}
+
 // One direction of the sweep for (sequence n, value head h, V tile at v0).
 template <typename T, int C, int D, int BV, int DIR, int NPF>
 __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS0, T* sS1, T* sX0, T* sX1, T* sDo0,
@@ -218,7 +240,8 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
             for (int ct = 0; ct < SCT; ++ct) {
                 const int d = 16 * (w * S::SRW + i) + acc_row(0), c = 16 * ct + acc_col();
-                store4<T>(sS + c * LS + d, st[i][ct][0], st[i][ct][1], st[i][ct][2], st[i][ct][3]);
+                store4<T>(sS + c * LS + (d ^ sweep_swz<T, C, BV, D>(c)), st[i][ct][0], st[i][ct][1], st[i][ct][2],
+                          st[i][ct][3]);
             }
         if constexpr (DIR == 1) {
             const int len = min(C, slen - it * C);
@@ -237,7 +260,8 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                         asm volatile("" : "+v"(dv.w[0]), "+v"(dv.w[1]), "+v"(dv.w[2]), "+v"(dv.w[3]));
                         const T* xp = reinterpret_cast<const T*>(&dv);
 #pragma unroll
-                        for (int q = 0; q < V8; ++q) sDo[(cc + q) * LX + r] = r < len ? xp[q] : T(0.f);
+                        for (int q = 0; q < V8; ++q)
+                            sDo[(cc + q) * LX + (r ^ sweep_swz<T, C, BV, C>(cc + q))] = r < len ? xp[q] : T(0.f);
                     }
                 }
             }
@@ -262,7 +286,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
 #pragma unroll
             for (int jj = 0; jj < S::XCT; ++jj)
 #pragma unroll
-                for (int k2 = 0; k2 < D / KS; ++k2) bx[jj][k2] = frag_kc(sS, LS, 16 * S::xcol(w, jj), k2 * KS);
+                for (int k2 = 0; k2 < D / KS; ++k2) bx[jj][k2] = frag_kc_swz<T, C, BV, D>(sS, LS, 16 * S::xcol(w, jj), k2 * KS);
             if constexpr (Ops::TRA2) {
                 const int l = lane_id();
 #pragma unroll
@@ -287,7 +311,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                     float o[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = DIR == 0 ? to_f32(cur.u[i][jj][e]) - acc[jj][e] : -acc[jj][e];
-                    store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
+                    store4<T>(sX + c * LX + (r ^ sweep_swz<T, C, BV, C>(c)), o[0], o[1], o[2], o[3]);
                 }
             }
         }
@@ -304,10 +328,10 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
             for (int ct = 0; ct < SCT; ++ct)
 #pragma unroll
                 for (int k2 = 0; k2 < C / KS; ++k2) {
-                    bxs[ct][k2] = frag_kc(sX, LX, 16 * ct, k2 * KS);
+                    bxs[ct][k2] = frag_kc_swz<T, C, BV, C>(sX, LX, 16 * ct, k2 * KS);
                     if constexpr (DIR == 1)
                         bdo[ct][k2] = do_rows<T, C>() ? frag_ks(sDo, LDO, 16 * ct, k2 * KS)    // do^T from do rows
-                                                      : frag_kc(sDo, LX, 16 * ct, k2 * KS);
+                                                      : frag_kc_swz<T, C, BV, C>(sDo, LX, 16 * ct, k2 * KS);
                 }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -364,7 +388,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                     Vec16 v;
                     T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
-                    for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + d];
+                    for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + (d ^ sweep_swz<T, C, BV, D>(c + q))];
                     st16(gS + tiled_index<D, BV>(d, v0, c), v);
                 }
             }
@@ -395,7 +419,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                     T* vp = reinterpret_cast<T*>(&v);
 #pragma unroll
                     for (int q = 0; q < V8; ++q) {
-                        const T x = sX[(c + q) * LX + r];
+                        const T x = sX[(c + q) * LX + (r ^ sweep_swz<T, C, BV, C>(c + q))];
                         vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
                     }
                     st16(gX + tiled_index<C, BV>(r, v0, c), v);
