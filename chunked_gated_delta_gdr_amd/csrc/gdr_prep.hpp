@@ -410,7 +410,9 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             }
         }
         __syncthreads();
-        // the lower 16 x 16 tiles of Aqk (which 0) and Akk (which 1), spread over the waves
+        // the lower 16 x 16 tiles of Aqk (t < NLT) and Akk (t >= NLT), tile t
+        // on wave t % NW; the tile loops are unrolled, so that each copy's
+        // block indices and masks are constants and only the wave's own copies run
         constexpr int NLT = NB * (NB + 1) / 2, NTI = 2 * NLT, TPW = (NTI + L::NW - 1) / L::NW;
         auto tile_ij = [](int tt, int& bi, int& bj) {   // row-major order of the lower triangle
             bi = 0;
@@ -419,34 +421,35 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         };
         f32x4 accT[TPW];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int t = w + L::NW * i;
-            accT[i] = zero4();
-            if (t < NTI) {
-                int bi, bj;
-                tile_ij(t % NLT, bi, bj);
-                f32x4 a1[1] = {zero4()};
-                panel_mma<T, 1, D>(a1, t >= NLT ? xkq : xq, LT, 16 * bi, xk, LT, 16 * bj, l);
-                accT[i] = a1[0];
-            }
+        for (int i = 0; i < TPW; ++i) accT[i] = zero4();
+#pragma unroll
+        for (int t = 0; t < NTI; ++t) {
+            if (t % L::NW != w) continue;
+            int bi, bj;
+            tile_ij(t % NLT, bi, bj);
+            f32x4 a1[1] = {zero4()};
+            panel_mma<T, 1, D>(a1, t >= NLT ? xkq : xq, LT, 16 * bi, xk, LT, 16 * bj, l);
+            accT[t / L::NW] = a1[0];
         }
         __syncthreads();   // the operand reads are done: Aqk and Akk overlay them
         int mydiag = -1;   // the Akk diagonal block this wave formed, if any
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int t = w + L::NW * i;
-            if (t < NTI) {
-                const bool kk = t >= NLT;
-                int bi, bj;
-                tile_ij(t % NLT, bi, bj);
+        for (int t = 0; t < NTI; ++t) {
+            if (t % L::NW != w) continue;
+            const bool kk = t >= NLT;
+            int bi, bj;
+            tile_ij(t % NLT, bi, bj);
+            float bsv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * bi + acc_row(e, l), s2 = 16 * bj + acc_col(l);
-                    if (kk) AkkF[r * LCF + s2] = s2 < r ? bs[r] * accT[i][e] : 0.f;
-                    else AqkF[r * LCF + s2] = s2 <= r ? accT[i][e] : 0.f;
-                }
-                if (kk && bi == bj) mydiag = bi;
+            for (int e = 0; e < 4; ++e) bsv[e] = kk ? bs[16 * bi + acc_row(e, l)] : 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * bi + acc_row(e, l), s2 = 16 * bj + acc_col(l);
+                const float v = accT[t / L::NW][e];
+                if (kk) AkkF[r * LCF + s2] = s2 < r ? bsv[e] * v : 0.f;
+                else AqkF[r * LCF + s2] = s2 <= r ? v : 0.f;
             }
+            if (kk && bi == bj) mydiag = bi;
         }
         if (mydiag >= 0) {   // its inverse, from the wave's own writes
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
