@@ -220,7 +220,8 @@ gdr_chunk_bwd(Params p) {
     float* btot = reinterpret_cast<float*>(smem + L::BT_OFF);
     char* const U0 = smem + L::U_OFF;
 
-    const int w = wave_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());   // uniform: a scalar register
+    const int wave_k = w;
     const int rb = w % NB, ch = w / NB;
     const int r0 = 16 * rb;                   // this wave's rows
     const int cd0 = ch * DH2, cc0 = ch * CH2, cv0 = ch * VH2;  // its column halves
@@ -349,12 +350,12 @@ gdr_chunk_bwd(Params p) {
     auto head = [&](const int j, const int hk, const int gi, const ChunkEntry ce, const bool first,
                     auto&& at_epilogue) __attribute__((always_inline)) {
         const int l = opaque_lane_id();  // fresh per head: see above
-        const int tid = [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }();
+        const int tid = fresh_tid(w);
         // the wave's rows and column halves, also fresh per head (shadowing the
         // kernel-scope ones), so that no address derived from them is kept
         // live across the items of the persistent kernel
-        const int w = [] {
-            int t = __builtin_amdgcn_readfirstlane(wave_id());
+        const int w = [wk = wave_k] {
+            int t = wk;
             asm volatile("" : "+s"(t));
             return t;
         }();
@@ -418,7 +419,7 @@ gdr_chunk_bwd(Params p) {
             // head's start (29 -> 3 spilled registers at C = 32). Without GQA
             // the kept addresses measured faster.
             const int tid_h = tid, l_h = l;
-            const int tid = GROUPED ? [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }()
+            const int tid = GROUPED ? fresh_tid(w)
                                     : tid_h;
             const int l = GROUPED ? opaque_lane_id() : l_h;
             __syncthreads();  // the previous slice's LDS reads are over
@@ -1076,7 +1077,7 @@ gdr_chunk_bwd(Params p) {
         {   // the next item's first requests (persistent kernel), addressed from
             // fresh opaque thread and lane indices, so that no address part is
             // shared with this item's own requests and kept live until here
-            const int t2 = [] { int t = static_cast<int>(threadIdx.x); asm volatile("" : "+v"(t)); return t; }();
+            const int t2 = fresh_tid(w);
             at_epilogue(t2, opaque_lane_id(), r0);
         }
         {

@@ -366,13 +366,32 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ int acc_row(int i, int l = lane_id()) { return 4 * (l >> 4) + i; }
 __device__ __forceinline__ int acc_col(int l = lane_id()) { return l & 15; }
 
+// The lane id from the count of lower lanes in the full mask (v_mbcnt), which
+// needs no register kept from the kernel's start. The mask goes through an
+// empty asm: with a visible all-ones mask the compiler folds the count back
+// into the thread id register.
+__device__ __forceinline__ int mbcnt_lane() {
+    unsigned m = ~0u;
+    asm volatile("" : "+s"(m));
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u)));
+}
+
 // The hardware lane id behind an empty asm: each call yields a value the
 // compiler cannot prove equal to any other, so lane-dependent arithmetic
 // derived from it is neither hoisted out of loops nor merged across copies.
 __device__ __forceinline__ int opaque_lane_id() {
-    int l = static_cast<int>(threadIdx.x & 63);
+    int l = mbcnt_lane();
     asm volatile("" : "+v"(l));
     return l;
+}
+// The thread index as wave * 64 + lane, behind an empty asm like the lane id
+// above; wv is the wave index held in a scalar register. Neither part reads
+// the thread id register, so a persistent kernel need not keep that register
+// (or a spilled copy of it) alive across its items.
+__device__ __forceinline__ int fresh_tid(int wv) {
+    int t = wv * 64 + mbcnt_lane();
+    asm volatile("" : "+v"(t));
+    return t;
 }
 
 // Store 4 consecutive values (accumulator rows r..r+3 of one column) to
