@@ -670,13 +670,59 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     // in order; besides Akk and the diagonal blocks of A it reads only blocks
     // of its own column, so only the wave's own LDS writes must be ordered (a
     // wave-level fence) until the workgroup barrier at the end.
+    auto wave_fence = [] {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    };
+    if constexpr (NB == 4) {
+        // Two levels instead of one walk per block column (whose first column
+        // chains three dependent steps): with P = L A (a 16 x 16 block product
+        // through the scratch tile) and A_ij = -A_ii P,
+        //   level 1: A10 = -A11 L10 A00 (wave 0), A32 = -A33 L32 A22 (wave 1);
+        //   level 2: the lower left 32 x 32 block, -A_bot (L_bl A_top):
+        //     A20 = -A22 (L20 A00 + L21 A10), A21 = -A22 L21 A11,
+        //     A30 = -(A32 (L20 A00 + L21 A10) + A33 (L30 A00 + L31 A10)),
+        //     A31 = -(A32 L21 A11 + A33 L31 A11), waves 0..3, each forming
+        //     the products it needs itself (waves 2, 3 keep their second
+        //     tile in Akk's diagonal blocks 0, 1, which 4a has finished with).
+        auto prod = [&](const int ai, const int aj, const int kd, const float* B, const int ldb, const int bk0,
+                        const int bj0) __attribute__((always_inline)) {
+            f32x4 acc = zero4();
+            return tile_f32(acc, AkkF, LCF, ai, aj, B, ldb, bk0, bj0, kd, l);
+        };
+        auto put = [&](float* dst, const int ld, const f32x4 acc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[acc_row(i, l) * ld + acc_col(l)] = acc[i];
+        };
+        float* sc = scr + w * 16 * 20;
+        if (w < 2) {   // level 1
+            const int b = 2 * w;   // A_{b+1,b}
+            put(sc, 20, prod(16 * (b + 1), 16 * b, 16, AF, LCF, 16 * b, 16 * b));
+            wave_fence();
+            f32x4 acc = zero4();
+            acc = tile_f32(acc, AF, LCF, 16 * (b + 1), 16 * (b + 1), sc, 20, 0, 0, 16, l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) AF[(16 * (b + 1) + acc_row(i, l)) * LCF + 16 * b + acc_col(l)] = -acc[i];
+        }
+        __syncthreads();
+        if (w < 4) {   // level 2: wave w forms A_{2 + w / 2, w % 2}
+            const int jc = w & 1, ir = 2 + (w >> 1);
+            // Y_{2, jc} = L_{2, jc..1} A_{jc..1, jc} (K = 32 - 16 jc)
+            put(sc, 20, prod(32, 16 * jc, 32 - 16 * jc, AF, LCF, 16 * jc, 16 * jc));
+            float* sc2 = AkkF + (16 * jc) * LCF + 16 * jc;   // Akk's diagonal block jc
+            if (ir == 3) put(sc2, LCF, prod(48, 16 * jc, 32 - 16 * jc, AF, LCF, 16 * jc, 16 * jc));   // Y_{3, jc}
+            wave_fence();
+            f32x4 acc = zero4();
+            // A_{2, jc} = -A22 Y_2jc; A_{3, jc} = -(A32 Y_2jc + A33 Y_3jc)
+            acc = tile_f32(acc, AF, LCF, 16 * ir, 32, sc, 20, 0, 0, 16, l);
+            if (ir == 3) acc = tile_f32(acc, AF, LCF, 48, 48, sc2, LCF, 0, 0, 16, l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) AF[(16 * ir + acc_row(i, l)) * LCF + 16 * jc + acc_col(l)] = -acc[i];
+        }
+    } else {
     if (w < NB - 1) {
         const int bj = w;
         float* sc = scr + w * 16 * 20;
-        auto wave_fence = [] {
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-        };
         for (int bi = bj + 1; bi < NB; ++bi) {
             f32x4 acc = zero4();
             acc = tile_f32(acc, AkkF, LCF, 16 * bi, 16 * bj, AF, LCF, 16 * bj, 16 * bj, 16 * (bi - bj), l);
@@ -689,6 +735,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             for (int i = 0; i < 4; ++i) AF[(16 * bi + acc_row(i, l)) * LCF + 16 * bj + acc_col(l)] = -acc[i];
             wave_fence();   // A_ij and the sc reads done before the next row reuses them
         }
+    }
     }
     __syncthreads();
 
