@@ -664,12 +664,11 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     }
     }   // per-boundary path
 
-    // ---- phase 4: A = (I + Akk)^-1 (4a, the diagonal blocks, ran in phase 3) ----
-    // 4b: block rows: A_ij = -A_ii * sum_{kb=j}^{i-1} L_i,kb A_kb,j  (fp32 MFMA).
-    // Wave w < NB - 1 owns block column j = w and walks its rows i = j+1, ...
-    // in order; besides Akk and the diagonal blocks of A it reads only blocks
-    // of its own column, so only the wave's own LDS writes must be ordered (a
-    // wave-level fence) until the workgroup barrier at the end.
+    // ---- phase 4: A = (I + Akk)^-1 (4a, the diagonal blocks, ran in phases 2-3) ----
+    // 4b: the blocks below the diagonal (fp32 MFMA), A_ij = -A_ii P_ij with
+    // P_ij = sum_{kb=j}^{i-1} L_i,kb A_kb,j. At C = 64 in two levels (below);
+    // at C = 32 one block, by wave 0. Each wave orders only its own LDS writes
+    // (a wave-level fence) until a workgroup barrier.
     auto wave_fence = [] {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
