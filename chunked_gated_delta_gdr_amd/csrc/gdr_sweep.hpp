@@ -66,7 +66,11 @@ struct SweepOps {
 };
 
 // Loads the operands of global chunk j (first token tok0, len real rows).
-template <typename T, int C, int D, int BV, int DIR>
+// PART selects which operands: 0 all; 1 those the step has used by its first
+// barrier (the staged k~ / w tiles, do); 2 those of the chunk-row product
+// (w / k~ fragments, u); 3 those of the state update (k~^T / w^T fragments,
+// (scale q~)^T, 2^G_last).
+template <typename T, int C, int D, int BV, int DIR, int PART = 0>
 __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const Params& p, int j, int tok0,
                                            int len, int h, int v0, int w) {
     using S = SweepTiles<T, C, D, BV>;
@@ -74,25 +78,33 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
     const size_t jh = (size_t)j * p.H + h;
     const T* A1 = static_cast<const T*>(DIR == 0 ? p.w : p.kt) + jh * C * D;
     const T* A2 = static_cast<const T*>(DIR == 0 ? p.ktT : p.wT) + jh * D * C;
+    constexpr bool P1 = PART == 0 || PART == 1, P2 = PART == 0 || PART == 2, P3 = PART == 0 || PART == 3;
+    if constexpr (P2) {
 #pragma unroll
-    for (int i = 0; i < S::XRT; ++i)
+        for (int i = 0; i < S::XRT; ++i)
 #pragma unroll
-        for (int k = 0; k < D / S::KS; ++k) o.a1[i][k] = frag_fo<T, D>(A1, 16 * S::xrow(w, i), k * S::KS);
+            for (int k = 0; k < D / S::KS; ++k) o.a1[i][k] = frag_fo<T, D>(A1, 16 * S::xrow(w, i), k * S::KS);
+    }
     if constexpr (SweepOps<T, C, D, BV, DIR>::TRA2) {
-        const T* A2r = static_cast<const T*>(DIR == 0 ? p.kt : p.w) + jh * C * D;
-        const int l = lane_id();
+        if constexpr (P1) {
+            const T* A2r = static_cast<const T*>(DIR == 0 ? p.kt : p.w) + jh * C * D;
+            const int l = lane_id();
 #pragma unroll
-        for (int ct = 0; ct < C / 16; ++ct) o.a2r[ct] = ld16(A2r + fo_index<T, D>(16 * ct + (l & 15), 32 * w + 8 * (l >> 4)));
-    } else {
+            for (int ct = 0; ct < C / 16; ++ct)
+                o.a2r[ct] = ld16(A2r + fo_index<T, D>(16 * ct + (l & 15), 32 * w + 8 * (l >> 4)));
+        }
+    } else if constexpr (P3) {
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
             for (int k = 0; k < C / S::KS; ++k) o.a2[i][k] = frag_fo<T, C>(A2, 16 * (w * S::SRW + i), k * S::KS);
     }
-    const float* gl = p.glast + jh * D;
+    if constexpr (P3) {
+        const float* gl = p.glast + jh * D;
 #pragma unroll
-    for (int i = 0; i < S::SRW; ++i) o.gl[i] = *reinterpret_cast<const f32x4*>(gl + 16 * (w * S::SRW + i) + acc_row(0));
-    if constexpr (DIR == 0) {
+        for (int i = 0; i < S::SRW; ++i) o.gl[i] = *reinterpret_cast<const f32x4*>(gl + 16 * (w * S::SRW + i) + acc_row(0));
+    }
+    if constexpr (DIR == 0 && P2) {
         const T* uT = static_cast<const T*>(p.uT) + jh * D * C;
 #pragma unroll
         for (int i = 0; i < S::XRT; ++i)
@@ -102,12 +114,15 @@ __device__ __forceinline__ void sweep_load(SweepOps<T, C, D, BV, DIR>& o, const 
                 const int c = v0 + 16 * S::xcol(w, jj) + acc_col();
                 o.u[i][jj] = *reinterpret_cast<const Q*>(uT + ao_index<C>(c, r));   // accumulator order
             }
-    } else {
+    }
+    if constexpr (DIR == 1 && P3) {
         const T* qsT = static_cast<const T*>(p.qsT) + jh * D * C;
 #pragma unroll
         for (int i = 0; i < S::SRW; ++i)
 #pragma unroll
             for (int k = 0; k < C / S::KS; ++k) o.a3[i][k] = frag_fo<T, C>(qsT, 16 * (w * S::SRW + i), k * S::KS);
+    }
+    if constexpr (DIR == 1 && P1) {
         // do rows of the chunk, this thread's 16-byte piece; rows past the
         // sequence end read its last row (always valid) and are zeroed at use
         constexpr int V8 = 16 / sizeof(T);
@@ -188,7 +203,7 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_kc_swz(const T* p, int ld
 }
 
 // One direction of the sweep for (sequence n, value head h, V tile at v0).
-template <typename T, int C, int D, int BV, int DIR, int NPF>
+template <typename T, int C, int D, int BV, int DIR, int NPF, bool SPREAD>
 __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0, T* sS0, T* sS1, T* sX0, T* sX1, T* sDo0,
                                           T* sDo1, T* sA2) {
     using S = SweepTiles<T, C, D, BV>;
@@ -222,11 +237,17 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
     }
     // step k of this direction works on chunk `it` of the sequence
     auto chunk_it = [&](int k) { return DIR == 0 ? k : nch - 1 - k; };
-    auto load = [&](Ops& o, int k) __attribute__((always_inline)) {
+    // part 0: all operands; 1-3: the groups a step has finished with at its
+    // three refill points (see sweep_load)
+    auto load = [&](auto part_c, Ops& o, int k) __attribute__((always_inline)) {
         const int it = chunk_it(k < nch ? k : nch - 1);   // past the end: a redundant valid load
-        sweep_load<T, C, D, BV, DIR>(o, p, c0 + it, stok0 + it * C, min(C, slen - it * C), h, v0, w);
+        sweep_load<T, C, D, BV, DIR, decltype(part_c)::value>(o, p, c0 + it, stok0 + it * C, min(C, slen - it * C), h,
+                                                             v0, w);
     };
-    auto step = [&](const Ops& cur, const int k) __attribute__((always_inline)) {
+    // refill(part): request the next use of this register set, part by part,
+    // as soon as the step no longer reads that part (spreading the requests
+    // over the step instead of issuing them all behind its stores)
+    auto step = [&](const Ops& cur, const int k, auto&& refill) __attribute__((always_inline)) {
         const int it = chunk_it(k);
         const size_t jh = (size_t)(c0 + it) * p.H + h;
         T* sS = (k & 1) ? sS1 : sS0;
@@ -272,6 +293,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
             for (int ct = 0; ct < C / 16; ++ct) st16(sA2 + (w * (C / 16) + ct) * 512 + 8 * l, cur.a2r[ct]);
         }
         __syncthreads();
+        refill(std::integral_constant<int, 1>{});
 
         // 2. chunk-row product: X = u - w h (fwd) or T = k~ dh (rev); forward
         //    keeps +X, reverse keeps -T so the state update is a pure sum. All
@@ -315,6 +337,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 }
             }
         }
+        refill(std::integral_constant<int, 2>{});
         __syncthreads();
 
         // 3. state update: st = Diag(2^G_last) st + A2 X (+ (scale q~)^T do for reverse).
@@ -357,6 +380,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                             st[i][ct] = Mfma<T>::mma(cur.a3[i][k2], bdo[ct][k2], st[i][ct]);
             }
         }
+        refill(std::integral_constant<int, 3>{});
         {   // the incoming state to the workspace, row-major: 8 columns per piece,
             // read back from its LDS buffer while the update's MFMAs run.
             // Stores are never behind a branch (spare threads repeat a piece with
@@ -433,18 +457,24 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
         // loop is unrolled NPF times so that the sets never move
         Ops ops[NPF];
 #pragma unroll
-        for (int s2 = 0; s2 < NPF; ++s2) load(ops[s2], s2);
+        for (int s2 = 0; s2 < NPF; ++s2) load(std::integral_constant<int, 0>{}, ops[s2], s2);
         int k0 = 0;
         for (; k0 + NPF <= nch; k0 += NPF) {
 #pragma unroll
             for (int s2 = 0; s2 < NPF; ++s2) {
-                step(ops[s2], k0 + s2);
-                load(ops[s2], k0 + s2 + NPF);
+                if constexpr (SPREAD) {
+                    step(ops[s2], k0 + s2, [&](auto part_c) __attribute__((always_inline)) {
+                        load(part_c, ops[s2], k0 + s2 + NPF);
+                    });
+                } else {
+                    step(ops[s2], k0 + s2, [](auto) {});
+                    load(std::integral_constant<int, 0>{}, ops[s2], k0 + s2 + NPF);
+                }
             }
         }
 #pragma unroll
         for (int s2 = 0; s2 < NPF - 1; ++s2)
-            if (k0 + s2 < nch) step(ops[s2], k0 + s2);
+            if (k0 + s2 < nch) step(ops[s2], k0 + s2, [](auto) {});
     }
     // the final state: dh0 (reverse), or ht for the forward pass when asked
     float* fin = DIR == 1 ? p.dh0 : p.ht;
@@ -461,7 +491,10 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
     }
 }
 
-template <typename T, int C, int D, int BV>
+// SPREAD: the next use of a register set is requested part by part, as the
+// step finishes with each part (see sweep_load), instead of all at once after
+// the step.
+template <typename T, int C, int D, int BV, bool SPREAD = false>
 __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     constexpr int LS = D + pad<T>();
     constexpr int LX = C + pad<T>();
@@ -484,8 +517,8 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     const int h = bid % p.H; bid /= p.H;
     const int n = bid % p.N;
     const int dir = p.dir0 + bid / p.N;
-    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
-    else sweep_run<T, C, D, BV, 1, NPF>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
+    if (dir == 0) sweep_run<T, C, D, BV, 0, NPF, SPREAD>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
+    else sweep_run<T, C, D, BV, 1, NPF, SPREAD>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
 }
 
 }  // namespace gdr
