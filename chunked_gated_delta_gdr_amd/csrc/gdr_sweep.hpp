@@ -507,16 +507,29 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     // per wave: its 32-column block of k~ / w (C / 16 fragment-order tiles)
     __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, C, D, BV>() ? 4 * (C / 16) * 512 : 8];
 
-    // Block order: the V tile varies slowest. Workgroups are dispatched to the
-    // 8 XCDs round-robin by block id, so with 2 N H a multiple of 8 the D/BV
-    // tiles of one (direction, sequence, head) land on the same XCD and share
-    // the chunk operands (w, k~, q~, do) through its L2.
-    const int ngroups = p.dirs * p.N * p.H;   // dirs = 1: the direction dir0 only
-    const int vt = blockIdx.x / ngroups;
-    int bid = blockIdx.x % ngroups;
-    const int h = bid % p.H; bid /= p.H;
-    const int n = bid % p.N;
-    const int dir = p.dir0 + bid / p.N;
+    // Block order. All reverse workgroups come first (with both directions in
+    // the grid): a reverse step costs more than a forward one, so when the grid
+    // takes several rounds of the CUs the longer jobs start first and the
+    // forward ones fill in behind them. Within a direction, workgroups are
+    // dispatched to the 8 XCDs round-robin by block id: with N H a multiple of
+    // 8, the D/BV tiles of one (sequence, head) get block ids 8 apart (same
+    // XCD, dispatched together), so they share the chunk operands (w, k~, q~,
+    // do) through that XCD's L2 while they run; otherwise the V tile varies
+    // slowest.
+    constexpr int NV = D / BV;
+    const int nh = p.N * p.H, per_dir = NV * nh;
+    const int rd = blockIdx.x / per_dir;      // dirs = 1: the direction dir0 only
+    const int dir = p.dirs == 2 ? 1 - rd : p.dir0;
+    const int i = blockIdx.x % per_dir;
+    int vt, hh;
+    if (nh % 8 == 0) {
+        vt = (i / 8) % NV;
+        hh = (i / (8 * NV)) * 8 + i % 8;
+    } else {
+        vt = i / nh;
+        hh = i % nh;
+    }
+    const int h = hh % p.H, n = hh / p.H;
     if (dir == 0) sweep_run<T, C, D, BV, 0, NPF, SPREAD>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
     else sweep_run<T, C, D, BV, 1, NPF, SPREAD>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
 }
