@@ -38,7 +38,7 @@ void layout(const gdr_bwd_desc_t* d, size_t off[WS_COUNT + 1]) {
     const size_t N = d->n_seqs > 0 ? d->n_seqs : d->B;
     size_t sz[WS_COUNT];
     sz[WS_CTAB] = nc * sizeof(gdr::ChunkEntry);
-    sz[WS_SEQOFF] = (N + 1) * sizeof(int);
+    sz[WS_SEQOFF] = (2 * N + 1) * sizeof(int);   // chunk offsets, then the longest-first order
     sz[WS_SAQKT] = sz[WS_AM] = nc * H * C * C * es;
     sz[WS_AT] = 0;   // kept in the order, empty: A^T is read from the staged A
     sz[WS_W] = sz[WS_WT] = sz[WS_KT] = sz[WS_KTT] = sz[WS_UT] = sz[WS_QST] = nc * H * C * D * es;
@@ -150,6 +150,7 @@ static int fill_params(const gdr_bwd_desc_t* d, const int32_t* cu_seqlens, void*
     p.cu = cu_seqlens;
     p.ctab = reinterpret_cast<gdr::ChunkEntry*>(ws + off[WS_CTAB]);
     p.seq_off = reinterpret_cast<int*>(ws + off[WS_SEQOFF]);
+    p.seq_ord = p.seq_off + p.N + 1;
     p.sAqkT = ws + off[WS_SAQKT];
     p.Am = ws + off[WS_AM];
     p.w = ws + off[WS_W];

@@ -455,6 +455,7 @@ struct Params {
     // workspace
     ChunkEntry* ctab;    // [nc_max]
     int* seq_off;        // [N+1] first chunk of each sequence; seq_off[N] = chunk count
+    int* seq_ord;        // [N] varlen: sequences by chunk count, longest first (ties in any order)
     void* sAqkT;         // [nc][H][C][C]  scale * Aqk^T
     void* Am;            // [nc][H][C][C]  A = (I + Akk)^-1
     // scale Aqk^T, A, w, w^T, k~, k~^T and scale q~^T in MFMA fragment order (fo_index)

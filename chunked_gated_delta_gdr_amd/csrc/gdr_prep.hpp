@@ -37,6 +37,7 @@ namespace gdr {
 // ---------------------------------------------------------------------------
 // Chunk table: one workgroup. seq_off[n] = first global chunk of sequence n,
 // ctab[j] = {first token, length, sequence, chunk index in the sequence}.
+// Varlen: seq_ord = the sequences by chunk count, longest first.
 // Fixed length: B sequences of T. Sequences are taken 256 at a time: a scan
 // of their chunk counts gives their first chunks, then every thread writes
 // entries of the block's chunks, finding each chunk's sequence by binary
@@ -86,6 +87,43 @@ __global__ __launch_bounds__(256) void gdr_chunk_table(Params p) {
         __syncthreads();
     }
     if (tid == 0) p.seq_off[p.N] = min(s_base, p.nc_max);
+    if (!p.varlen) return;
+    // Varlen: the sequences ordered by chunk count, longest first, for the
+    // state sweeps' block order (the longest jobs start first). A counting
+    // sort over kBuckets counts (longer sequences share the top bucket):
+    // histogram, exclusive scan from the top bucket down, then each sequence
+    // takes the next slot of its bucket (ties land in any order; only the
+    // order of the workgroups depends on it, not any result).
+    constexpr int kBuckets = 1024, BPT = kBuckets / 256;
+    __shared__ int s_hist[kBuckets];
+    auto bucket = [&](int n) {
+        int len, tok0;
+        seq_span(p, n, tok0, len);
+        return kBuckets - 1 - min((len + C - 1) / C, kBuckets - 1);   // 0 = longest
+    };
+    for (int b = tid; b < kBuckets; b += 256) s_hist[b] = 0;
+    __syncthreads();
+    for (int n = tid; n < p.N; n += 256) atomicAdd(&s_hist[bucket(n)], 1);
+    __syncthreads();
+    int cnt[BPT], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) sum += (cnt[i] = s_hist[BPT * tid + i]);
+    s_scan[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the per-thread sums
+        int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    int start = s_scan[tid] - sum;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        s_hist[BPT * tid + i] = start;
+        start += cnt[i];
+    }
+    __syncthreads();
+    for (int n = tid; n < p.N; n += 256) p.seq_ord[atomicAdd(&s_hist[bucket(n)], 1)] = n;
 }
 
 // ---------------------------------------------------------------------------

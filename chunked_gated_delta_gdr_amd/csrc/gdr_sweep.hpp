@@ -507,10 +507,11 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     // per wave: its 32-column block of k~ / w (C / 16 fragment-order tiles)
     __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, C, D, BV>() ? 4 * (C / 16) * 512 : 8];
 
-    // Block order. All reverse workgroups come first (with both directions in
-    // the grid): a reverse step costs more than a forward one, so when the grid
-    // takes several rounds of the CUs the longer jobs start first and the
-    // forward ones fill in behind them. Within a direction, workgroups are
+    // Block order: the longer jobs start first, which matters when the grid
+    // takes several rounds of the CUs. All reverse workgroups come first (with
+    // both directions in the grid: a reverse step costs more than a forward
+    // one), and varlen sequences are taken longest first (the chunk table's
+    // order), so shorter jobs fill in behind. Within a direction, workgroups are
     // dispatched to the 8 XCDs round-robin by block id: with N H a multiple of
     // 8, the D/BV tiles of one (sequence, head) get block ids 8 apart (same
     // XCD, dispatched together), so they share the chunk operands (w, k~, q~,
@@ -529,7 +530,8 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
         vt = i / nh;
         hh = i % nh;
     }
-    const int h = hh % p.H, n = hh / p.H;
+    // varlen: sequences longest first (the chunk table's order)
+    const int h = hh % p.H, n = p.varlen ? p.seq_ord[hh / p.H] : hh / p.H;
     if (dir == 0) sweep_run<T, C, D, BV, 0, NPF, SPREAD>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
     else sweep_run<T, C, D, BV, 1, NPF, SPREAD>(p, n, h, vt * BV, sS[0], sS[1], sX[0], sX[1], sDo[0], sDo[1], sA2);
 }

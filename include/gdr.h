@@ -259,7 +259,8 @@ int gdr_bwd_fused(const gdr_bwd_desc_t* d,
 
 /*
  * Byte offsets of the workspace regions for descriptor d, in this order:
- *   0 chunk table, 1 per-sequence chunk offsets, 2 scale*Aqk^T, 3 A,
+ *   0 chunk table, 1 per-sequence chunk offsets (n + 1 int32, then, for
+ *   varlen, the n sequences by chunk count, longest first), 2 scale*Aqk^T, 3 A,
  *   4 (empty: A^T is taken from A; kept so that the numbering holds),
  *   5 w, 6 w^T, 7 k~, 8 k~^T (6 and 8 are written only where the state
  *   sweep does not form them from w and k~ itself: fp32 io, K = 64, or its

@@ -296,3 +296,39 @@ def test_varlen_more_sequences_than_one_table_pass():
     gpu = tu.run_gpu(inp)
     ref = tu.run_oracle(inp)
     _check(tu.rel_errors(gpu, ref, tu.real_token_mask(inp)), tu.tolerance(w), "varlen 300 sequences")
+
+
+def test_varlen_longest_first_order():
+    """The chunk table's longest-first sequence order, which sets the state
+    sweeps' block order: a permutation of the sequences with non-increasing
+    chunk counts (counts of 1023 chunks or more share its top bucket), next to
+    the chunk offsets; empty sequences and one sequence past the top bucket
+    included, every output compared with the oracle."""
+    import chunked_gated_delta_gdr_amd as gdr
+    gen = torch.Generator().manual_seed(67)
+    lens = torch.randint(0, 300, (40,), generator=gen)
+    lens[3] = 0
+    lens[17] = 1025 * 64 - 5          # 1025 chunks
+    lens[29] = 1023 * 64              # 1023 chunks
+    cu = torch.zeros(41, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    T = int(cu[-1])
+    w = scaled(VARLEN, T=T, H=1, Hg=1, K=64, V=64, n_seqs=0, seed=67)   # lengths set below
+    inp = make_inputs(w)
+    inp["cu_seqlens"] = cu
+    inp["h0"] = torch.randn(40, w.H, w.K, w.V, generator=gen) * 0.1
+    inp["dht"] = torch.randn(40, w.H, w.K, w.V, generator=gen) * 0.1
+    desc = gdr.make_desc(1, T, w.H, w.Hg, w.K, w.V, chunk=w.chunk, n_seqs=40, io_dtype=w.io_dtype)
+    offs = gdr.workspace_offsets(desc)
+    ws = torch.zeros(offs["total"], dtype=torch.uint8, device="cuda")
+    gpu = tu.run_gpu(inp, workspace=ws)
+    words = ws[offs["seq_off"]: offs["seq_off"] + 4 * 81].cpu().view(torch.int32).numpy()
+    nch = (lens.numpy() + 63) // 64
+    assert list(words[:41]) == [0] + list(np.cumsum(nch))
+    order = words[41:81]
+    assert sorted(order.tolist()) == list(range(40))
+    capped = np.minimum(nch[order], 1023)
+    assert np.all(np.diff(capped) <= 0), capped
+    assert set(order[:2].tolist()) == {17, 29}
+    ref = tu.run_oracle(inp)
+    _check(tu.rel_errors(gpu, ref, tu.real_token_mask(inp)), tu.tolerance(w), "varlen longest first")
