@@ -116,11 +116,10 @@ __device__ __forceinline__ void fo_piece(int e, int& r, int& c) {
 }
 // Whether the sweep with V tiles of BV columns forms its k~^T and w^T
 // fragments from k~ and w itself (staged in LDS, read through transposed
-// loads): 16-bit operands at K = 128, except 64-column tiles at C = 64, whose
-// registers are at the limit already. The preparation stores k~^T and w^T
+// loads): 16-bit operands at K = 128. The preparation stores k~^T and w^T
 // only for a sweep that does not.
 template <typename T, int C, int D, int BV>
-constexpr bool sweep_transposes_a2() { return sizeof(T) == 2 && D == 128 && !(C == 64 && BV == 64); }
+constexpr bool sweep_transposes_a2() { return sizeof(T) == 2 && D == 128; }
 // The A fragment (rows i0 .. +15, k0 .. +KS) of such a matrix.
 template <typename T, int K>
 __device__ __forceinline__ typename Mfma<T>::frag frag_fo(const T* p, int i0, int k0, int l = lane_id()) {

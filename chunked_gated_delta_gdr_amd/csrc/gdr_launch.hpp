@@ -52,19 +52,20 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     // more rounds of the CUs (each workgroup then loads the chunk operands once
     // for twice the columns); else 16 for a single direction at C = 64 (one
     // round either way, fewer bytes per workgroup); else 32. The preparation
-    // stores k~^T and w^T when that sweep does not form them itself (the same
-    // rule decides for the backward after a forward pass: both take dirs = 1).
+    // stores k~^T and w^T when the sweeps do not form them themselves (which
+    // depends on the operand type and K only, so a backward after a forward
+    // pass finds what its sweep needs).
     const int tiles32 = p.dirs * p.N * p.H * (D / kSweepBV);
     const bool wide = tiles32 >= 2 * compute_units();
-    const bool store_a2t = wide ? !sweep_transposes_a2<T, C, D, kSweepBVW>() : !sweep_transposes_a2<T, C, D, kSweepBV>();
-    static_assert(sweep_transposes_a2<T, C, D, kSweepBV>() == sweep_transposes_a2<T, C, D, kSweepBV1>(),
-                  "16- and 32-column sweeps take the same operands");
+    constexpr bool store_a2t = !sweep_transposes_a2<T, C, D, kSweepBV>();
+    static_assert(sweep_transposes_a2<T, C, D, kSweepBV>() == sweep_transposes_a2<T, C, D, kSweepBV1>() &&
+                      sweep_transposes_a2<T, C, D, kSweepBV>() == sweep_transposes_a2<T, C, D, kSweepBVW>(),
+                  "sweeps of every tile width take the same operands");
     if ((p.dir0 == 0 || p.hsrc) && p.nc_max > 0) {
         // persistent: as many workgroups as the CUs hold at once
         const int items = p.nc_max * p.H, slots = compute_units() * resident_per_cu<T, C>();
         const dim3 grid(items < slots ? items : slots), block(128 * (C / 16));
-        if (store_a2t) gdr_prep<T, C, D, SCALAR, true><<<grid, block, 0, stream>>>(p);
-        else gdr_prep<T, C, D, SCALAR, false><<<grid, block, 0, stream>>>(p);
+        gdr_prep<T, C, D, SCALAR, store_a2t><<<grid, block, 0, stream>>>(p);
     }
     if (e == hipSuccess) e = mark(2);
     if (p.hsrc && p.nc_max > 0) {   // X and the tiled h from the caller's states
@@ -73,7 +74,8 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
         else gdr_states_in<T, C, D, false><<<grid, dim3(256), 0, stream>>>(p);
     }
     if (wide) {
-        gdr_sweep<T, C, D, kSweepBVW><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
+        // C = 64: refills spread over the step (one set of operands in flight)
+        gdr_sweep<T, C, D, kSweepBVW, C == 64><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
     } else {
         bool narrow = false;
         if constexpr (C == 64) {

@@ -263,8 +263,8 @@ int gdr_bwd_fused(const gdr_bwd_desc_t* d,
  *   varlen, the n sequences by chunk count, longest first), 2 scale*Aqk^T, 3 A,
  *   4 (empty: A^T is taken from A; kept so that the numbering holds),
  *   5 w, 6 w^T, 7 k~, 8 k~^T (6 and 8 are written only where the state
- *   sweep does not form them from w and k~ itself: fp32 io, K = 64, or its
- *   64-column tiles at chunk 64), 9 u^T, 10 scale*q~^T, 11 2^G_last,
+ *   sweep does not form them from w and k~ itself: fp32 io or K = 64),
+ *   9 u^T, 10 scale*q~^T, 11 2^G_last,
  *   12 h (state before each chunk), 13 X, 14 dh (state gradient at each
  *   chunk end), 15 T = k~ dh, 16 = total bytes.
  * Per-chunk regions are [chunks][H][..] in io_dtype (2^G_last in fp32);
