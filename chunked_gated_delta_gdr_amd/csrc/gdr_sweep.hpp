@@ -183,16 +183,16 @@ constexpr bool do_rows() { return sizeof(T) == 2 && C == 32; }
 // 64-column tiles with 16-bit operands copy the state and X / T out with
 // 16-bit reads, 8 rows per thread piece, rows 8 apart: at the padded row
 // pitches those rows share one LDS bank (and the C = 64 reverse direction
-// writes do^T the same way). So at C = 64 these buffers hold element
-// (row c, index k) at c * pitch + (k ^ swz(c)), an XOR of k's 8-element
-// groups by c / 8 (limited to the K / 8 groups of the index range K): the
-// 8-element MFMA fragment reads and 4-element writes stay contiguous, and the
-// eight rows of a copy-out read fall in distinct banks (varlen workload sweep
-// 675 -> 600 us). At C = 32 the same layout measured slower (1176 -> 1211 us),
-// so it is not used there.
+// writes do^T the same way). So these buffers hold element (row c, index k)
+// at c * pitch + (k ^ swz(c)), an XOR of k's 8-element groups by c / 8
+// (limited to the K / 8 groups of the index range K): the 8-element MFMA
+// fragment reads and 4-element writes stay contiguous, and the eight rows of
+// a copy-out read fall in distinct banks (at most two share one for X / T at
+// C = 32, whose 32-element rows have four groups). Measured: varlen workload
+// sweep (C = 64) 675 -> 600 us, GDN GQA sweep (C = 32) 1102 -> 879 us.
 template <typename T, int C, int BV, int K>
 __device__ __forceinline__ int sweep_swz(int c) {
-    if constexpr (sizeof(T) == 2 && BV == 64 && C == 64) return 8 * ((c >> 3) & ((K / 8 < 8 ? K / 8 : 8) - 1));
+    if constexpr (sizeof(T) == 2 && BV == 64) return 8 * ((c >> 3) & ((K / 8 < 8 ? K / 8 : 8) - 1));
     else return 0;
 }
 // frag_kc on a buffer laid out as above
