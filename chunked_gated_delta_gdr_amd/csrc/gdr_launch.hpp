@@ -74,8 +74,9 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
         else gdr_states_in<T, C, D, false><<<grid, dim3(256), 0, stream>>>(p);
     }
     if (wide) {
-        // C = 64: refills spread over the step (one set of operands in flight)
-        gdr_sweep<T, C, D, kSweepBVW, C == 64><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
+        // refills spread over the step (measured: C = 64 with one set of
+        // operands in flight 400 -> 363 us varlen; C = 32 878 -> 866 us GDN GQA)
+        gdr_sweep<T, C, D, kSweepBVW, true><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);
     } else {
         bool narrow = false;
         if constexpr (C == 64) {
