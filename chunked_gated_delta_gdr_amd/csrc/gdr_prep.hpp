@@ -702,6 +702,32 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     }
     }   // per-boundary path
 
+    // k~ = k 2^(G_last - G) in fragment order, by NTK threads from t0 (16-bit:
+    // row fastest, so the fragment-order stores are contiguous); ktS: also the
+    // k~ rows staged in LDS (for k~^T), or null
+    auto kt_out = [&](auto ntk_c, const int t0, T* ktS) __attribute__((always_inline)) {
+        constexpr int NTK = decltype(ntk_c)::value;
+        T* gkt = static_cast<T*>(p.kt) + jh * C * D;
+        static_assert(C * (D / 8) % NTK == 0, "piece split");
+#pragma unroll
+        for (int it = 0; it < C * (D / 8) / NTK; ++it) {
+            const int e = t0 + it * NTK;
+            const int r = sizeof(T) == 2 ? e % C : e / (D / 8);
+            const int d0 = sizeof(T) == 2 ? (e / C) * 8 : (e % (D / 8)) * 8;
+            float x[8], gl[8], g[8];
+            load8<T>(kL + r * LT + d0, x);
+            load8f(Gs + (C - 1) * LF + d0, gl);
+            load8f(Gs + r * LF + d0, g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
+            store8<T>(gkt + fo_index<T, D>(r, d0), x);
+            if (ktS) store8<T>(ktS + r * LT + d0, x);
+        }
+    };
+    // At C = 64 without the k~^T store, waves 4..7 write k~ while waves 0..3
+    // form the lower-left blocks of the inverse (phase 4b, level 2)
+    constexpr bool EARLY_KT = NB == 4 && !STORE_A2T;
+
     // ---- phase 4: A = (I + Akk)^-1 (4a, the diagonal blocks, ran in phases 2-3) ----
     // 4b: the blocks below the diagonal (fp32 MFMA), A_ij = -A_ii P_ij with
     // P_ij = sum_{kb=j}^{i-1} L_i,kb A_kb,j. At C = 64 in two levels (below);
@@ -755,6 +781,8 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             if (ir == 3) acc = tile_f32(acc, AF, LCF, 48, 48, sc2, LCF, 0, 0, 16, l);
 #pragma unroll
             for (int i = 0; i < 4; ++i) AF[(16 * ir + acc_row(i, l)) * LCF + 16 * jc + acc_col(l)] = -acc[i];
+        } else if constexpr (EARLY_KT) {
+            kt_out(std::integral_constant<int, NT / 2>{}, tid - NT / 2, nullptr);
         }
     } else {
     if (w < NB - 1) {
@@ -943,28 +971,15 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     }
 
     // ---- phase 9: k~ = k 2^(G_last - G) (fragment order, and transposed where
-    //      the sweep does not transpose it itself), 2^G_last ----
+    //      the sweep does not transpose it itself; written in phase 4b instead
+    //      where EARLY_KT), 2^G_last ----
     {
-        T* gkt = static_cast<T*>(p.kt) + jh * C * D;
         T* gktT = static_cast<T*>(p.ktT) + jh * D * C;
         // 16-bit: k~ rows also staged over the dead Aqk / Akk (for k~^T below)
         T* ktS = reinterpret_cast<T*>(smem + L::AQK_OFF);
         static_assert(size_t(C) * LT * sizeof(T) <= 2 * size_t(C) * LCF * 4, "k~ staging fits over Aqk, Akk");
-#pragma unroll
-        for (int it = 0; it < C * (D / 8) / NT; ++it) {
-            const int e = tid + it * NT;
-            // 16-bit: row fastest, so the fragment-order stores are contiguous
-            const int r = sizeof(T) == 2 ? e % C : e / (D / 8);
-            const int d0 = sizeof(T) == 2 ? (e / C) * 8 : (e % (D / 8)) * 8;
-            float x[8], gl[8], g[8];
-            load8<T>(kL + r * LT + d0, x);
-            load8f(Gs + (C - 1) * LF + d0, gl);
-            load8f(Gs + r * LF + d0, g);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= fast_exp2(gl[i] - g[i]);
-            store8<T>(gkt + fo_index<T, D>(r, d0), x);
-            if constexpr (sizeof(T) == 2 && STORE_A2T) store8<T>(ktS + r * LT + d0, x);
-        }
+        if constexpr (!EARLY_KT)
+            kt_out(std::integral_constant<int, NT>{}, tid, sizeof(T) == 2 && STORE_A2T ? ktS : nullptr);
         if constexpr (!STORE_A2T) {
             // k~^T is formed by the sweep
         } else if constexpr (sizeof(T) == 2) {
