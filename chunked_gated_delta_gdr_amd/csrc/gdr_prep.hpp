@@ -23,7 +23,7 @@
 // boundary rho = 16 i of the target row block: q 2^(G_r - G_rho) and
 // k 2^(G_rho - G_s), both exponents <= 0 (the per-block-boundary form of the
 // bwd_intra page).
-// At C = 64 a chunk whose every |G_r - G_last / 2| is within that same bound
+// A chunk (C = 64 or 32) whose every |G_r - G_last / 2| is within that same bound
 // takes a shorter route instead: all of Aqk and Akk as two masked C x C
 // products over D, on operands scaled once through the one reference
 // G_last / 2 per column (exponents of either sign, bounded as above). The
@@ -155,7 +155,8 @@ struct PrepLds {
     // the one-reference form of Aqk / Akk (phases 2-3) keeps its three [C][LT]
     // operands in the X region and the Aqk / Akk regions that follow it (the
     // products land there after a barrier); A's region stays untouched
-    static constexpr bool FAST = C == 64 && 3 * size_t(C) * LT * sizeof(T) <= AF_OFF - X_OFF;
+    // (both chunk sizes: at C = 32 the three operands fill that span exactly)
+    static constexpr bool FAST = (C == 64 || C == 32) && 3 * size_t(C) * LT * sizeof(T) <= AF_OFF - X_OFF;
     // after the inverse, A and Aqk are converted in place to MFMA operands
     static_assert(size_t(C) * LC * sizeof(T) <= size_t(C) * LCF * 4, "A/Aqk in place");
     static_assert(size_t(NB) * 16 * 20 >= size_t(NT > D ? NT : D) * 1, "cumsum scratch");

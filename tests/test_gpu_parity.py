@@ -121,17 +121,26 @@ def test_f16_diagonal_guard_mixed():
     _check(tu.parity(w), tu.tolerance(w))
 
 
-@pytest.mark.parametrize("dtype,gate_mult,guard", [(torch.bfloat16, 2.0, 64.0), (torch.float16, 0.25, 8.0),
-                                                     (torch.float32, 2.4, 64.0)])
-def test_prep_one_reference_bound_mixed(dtype, gate_mult, guard):
-    """Chunk 64: the preparation kernel forms Aqk / Akk through one reference
-    G_last / 2 per column when every |G_r - G_last / 2| is within the operand
-    guard, else through the block boundaries. Gates chosen so that one launch
-    holds (chunk, head) items of both kinds."""
-    if dtype == torch.float32:
-        w = scaled(TINY, T=130, gate_mult=gate_mult, h0_std=0.1, dht_std=0.1, seed=57)
-    else:
-        w = scaled(KDA16, B=1, T=200, H=3, Hg=3, io_dtype=dtype, gate_mult=gate_mult, dht_std=0.1, seed=53)
+ONE_REF_MIXED = {
+    "bf16_c64": (scaled(KDA16, B=1, T=200, H=3, Hg=3, gate_mult=2.0, dht_std=0.1, seed=53), 64.0),
+    "f16_c64": (scaled(KDA16, B=1, T=200, H=3, Hg=3, io_dtype=torch.float16, gate_mult=0.25, dht_std=0.1,
+                       seed=53), 8.0),
+    "f32_c64": (scaled(TINY, T=130, gate_mult=2.4, h0_std=0.1, dht_std=0.1, seed=57), 64.0),
+    "bf16_c32": (scaled(KDA16, B=1, T=200, H=3, Hg=3, chunk=32, gate_mult=4.0, dht_std=0.1, seed=53), 64.0),
+    "f16_c32": (scaled(KDA16, B=1, T=200, H=3, Hg=3, chunk=32, io_dtype=torch.float16, gate_mult=0.5,
+                       dht_std=0.1, seed=53), 8.0),
+    "f16_c32_gdn_gqa": (scaled(GDN, B=1, T=200, H=4, Hg=2, gate_mult=1.0, seed=59), 8.0),
+    "f32_c32": (scaled(TINY, T=130, chunk=32, gate_mult=4.0, h0_std=0.1, dht_std=0.1, seed=57), 64.0),
+}
+
+
+@pytest.mark.parametrize("name", list(ONE_REF_MIXED))
+def test_prep_one_reference_bound_mixed(name):
+    """The preparation kernel forms Aqk / Akk through one reference G_last / 2
+    per column when every |G_r - G_last / 2| is within the operand guard, else
+    through the block boundaries. Gates chosen so that one launch holds
+    (chunk, head) items of both kinds, at both chunk sizes."""
+    w, guard = ONE_REF_MIXED[name]
     fast, slow = tu.one_reference_split(w, guard)
     assert fast > 0 and slow > 0, (fast, slow)
     _check(tu.parity(w), tu.tolerance(w))
