@@ -495,6 +495,12 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             __builtin_amdgcn_wave_barrier();
             if (l < 16) diag_block_inverse<LCF>(AkkF, AF, mydiag, l);
         }
+        // the next item's g, q, k, beta: with the one-reference form compiled
+        // in, requested here (after its operand and product registers are
+        // free, before the inverse, while the memory pipeline is idle) rather
+        // than in phase 1, where they would spill at C = 64; or at the
+        // matching point of the per-boundary path
+        if constexpr (L::FAST) load_in(nxt, ce_n);
         // the tiles of Aqk above the diagonal are zero
         for (int t = w; t < NB * (NB - 1) / 2; t += L::NW) {
             int bi, bj;
@@ -701,6 +707,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             for (int ib = 1; ib < NB; ++ib) pass(std::integral_constant<int, 1>{}, ib, ib == 1);
         }
     }
+    if constexpr (L::FAST) load_in(nxt, ce_n);
     }   // per-boundary path
 
     // k~ = k 2^(G_last - G) in fragment order, by NTK threads from t0 (16-bit:
@@ -805,11 +812,6 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
 
-    // the next item's g, q, k, beta: with the one-reference form compiled in,
-    // requested here rather than in phase 1 (their registers are then free
-    // during phases 1-4, which that form needs; the loads still have most of
-    // an item to arrive)
-    if constexpr (L::FAST) load_in(nxt, ce_n);
     // ---- phase 5: A and scale Aqk^T to the workspace in 8-element row
     //      pieces (the gradient kernel takes A^T from its LDS copy of A through
     //      transposed loads); A and Aqk in place as MFMA operands in LDS ----
