@@ -251,19 +251,19 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     constexpr int NGP = C * (D / 4) / NT;    // 4-float gate pieces per thread
     constexpr int NQP = C * (D / V8) / NT;   // 16-byte q / k / v pieces per thread
     static_assert(NGP * NT == C * (D / 4) && NQP * NT == C * (D / V8), "piece split");
-    f32x4 gpre[NGP];
+    f32x4 gpre[SCALAR ? 1 : NGP];   // per-channel gate pieces
+    float gsc;                       // scalar gate: the gate of row (lane id)
     Vec16 qpre[NQP], kpre[NQP], vpre[NQP];
     float bpre;
     // rows past the sequence end read the last row (zeroed at use)
     auto load_in = [&](const int it, const ChunkEntry& e2) __attribute__((always_inline)) {
         const int hh = it % p.H, hkk = hh / p.G;
+        if constexpr (SCALAR) {
+            gsc = p.g[(size_t)(e2.tok0 + min(tid & 63, e2.len - 1)) * p.H + hh];
+        } else {
 #pragma unroll
-        for (int i = 0; i < NGP; ++i) {
-            const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4, rt = min(r, e2.len - 1);
-            if constexpr (SCALAR) {
-                const float sg = p.g[(size_t)(e2.tok0 + rt) * p.H + hh];
-                gpre[i] = f32x4{sg, sg, sg, sg};
-            } else {
+            for (int i = 0; i < NGP; ++i) {
+                const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4, rt = min(r, e2.len - 1);
                 gpre[i] = *reinterpret_cast<const f32x4*>(p.g + ((size_t)(e2.tok0 + rt) * p.H + hh) * D + d0);
             }
         }
@@ -312,13 +312,41 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         reinterpret_cast<f32x4*>(AF)[e] = zero4();
         if constexpr (!L::FAST) reinterpret_cast<f32x4*>(AqkF)[e] = zero4();
     }
+    if constexpr (SCALAR) {
+        // one gate per row: every wave scans the chunk's C gates across its
+        // lanes (lane = row; rows past the end add 0, so they take G_last) and
+        // writes its pieces of the cumsum G and of 2^g broadcast over the
+        // columns; the chunk's range check comes from the same scan
+        static_assert(C <= 64, "one row per lane");
+        const int ll = tid & 63;
+        const float gr = ll < len ? gsc : 0.f;
+        float G = gr;
 #pragma unroll
-    for (int i = 0; i < NGP; ++i) {
-        const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4;
-        const f32x4 gv = r < len ? gpre[i] : zero4();
-        *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = gv;
-        *reinterpret_cast<f32x4*>(At + r * LF + d0) =
-            f32x4{fast_exp2(gv[0]), fast_exp2(gv[1]), fast_exp2(gv[2]), fast_exp2(gv[3])};
+        for (int off = 1; off < C; off <<= 1) {
+            const float y = __shfl_up(G, off);
+            G += ll >= off ? y : 0.f;
+        }
+        if constexpr (L::FAST) {
+            const float tot = __shfl(G, C - 1);
+            const float dev = wave_max(ll < C ? fabsf(G - 0.5f * tot) : 0.f);
+            if (ll == 0) flags[w] = dev;
+        }
+#pragma unroll
+        for (int i = 0; i < NGP; ++i) {
+            const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4;
+            const float Gv = __shfl(G, r), ex = fast_exp2(__shfl(gr, r));
+            *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = f32x4{Gv, Gv, Gv, Gv};
+            *reinterpret_cast<f32x4*>(At + r * LF + d0) = f32x4{ex, ex, ex, ex};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NGP; ++i) {
+            const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4;
+            const f32x4 gv = r < len ? gpre[i] : zero4();
+            *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = gv;
+            *reinterpret_cast<f32x4*>(At + r * LF + d0) =
+                f32x4{fast_exp2(gv[0]), fast_exp2(gv[1]), fast_exp2(gv[2]), fast_exp2(gv[3])};
+        }
     }
 #pragma unroll
     for (int i = 0; i < NQP; ++i) {
@@ -329,7 +357,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     if (tid < C) bs[tid] = tid < len ? bpre : 0.f;
     if constexpr (!L::FAST) load_in(nxt, ce_n);  // the next item's g, q, k, beta
     __syncthreads();
-    {   // column cumsum in NSEG segments of SR rows: local scans, then segment offsets
+    if constexpr (!SCALAR) {   // column cumsum in NSEG segments of SR rows: local scans, then segment offsets
         constexpr int NSEG = NT / D > 0 ? NT / D : 1, SR = C / NSEG;
         static_assert(NT % D == 0 || NT < D, "cumsum split");
         float* segtot = scr;  // [NSEG][D]
