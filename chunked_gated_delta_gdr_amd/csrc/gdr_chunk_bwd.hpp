@@ -1223,7 +1223,10 @@ gdr_chunk_bwd(Params p) {
     } else if constexpr (FUSED) {
         // one workgroup per (sequence n, value head h), chunks from the last to
         // the first; dh starts as dht and ends as dh0
-        const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, hk = h / p.G, gi = h % p.G;
+        // varlen: sequences longest first (the chunk table's order), so the
+        // longest walks start first
+        const int ns = blockIdx.x / p.H, h = blockIdx.x % p.H, hk = h / p.G, gi = h % p.G;
+        const int n = p.varlen ? p.seq_ord[ns] : ns;
         const int c0 = p.seq_off[n], c1 = p.seq_off[n + 1];
         const size_t sh = ((size_t)n * p.H + h) * D * D;
         const int l = lane_id();
