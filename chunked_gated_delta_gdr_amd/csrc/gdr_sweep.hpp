@@ -500,8 +500,9 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     constexpr int LX = C + pad<T>();
     // chunks of operands in flight: at C = 64 with 64-column tiles one, its
     // refills spread over the step (two sets measured slower there: their
-    // registers spilled)
-    constexpr int NPF = C == 32 ? 2 : BV == 64 ? 1 : 3;
+    // registers spilled); else two (three measured slower at 32-column tiles:
+    // headline sweep 128 vs 120 us)
+    constexpr int NPF = C == 64 && BV == 64 ? 1 : 2;
     static_assert(kTileV % BV == 0 || BV % kTileV == 0, "sweep V tiles and stored tiles nest");
     static_assert(kTileV % (16 / sizeof(T)) == 0, "a 16-byte piece lies within one stored tile");
     __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];
