@@ -176,9 +176,10 @@ constexpr int do_pitch() { return BV + (sizeof(T) == 2 ? 16 : 4); }
 // Whether the reverse direction keeps do rows as loaded (one 16-byte LDS write
 // per piece, do^T fragments through transposed loads) instead of writing do^T
 // element by element: measured faster at C = 32 (GDN GQA sweep 1.20 -> 1.17
-// ms), slower at C = 64 (125.8 -> 128.3 us).
-template <typename T, int C>
-constexpr bool do_rows() { return sizeof(T) == 2 && C == 32; }
+// ms) and for 32-column tiles at C = 64 (headline sweep 121.9 -> 120.9 us),
+// slower for 64-column tiles at C = 64 (varlen sweep 364 -> 368 us).
+template <typename T, int C, int BV>
+constexpr bool do_rows() { return sizeof(T) == 2 && (C == 32 || BV <= 32); }
 
 // 64-column tiles with 16-bit operands copy the state and X / T out with
 // 16-bit reads, 8 rows per thread piece, rows 8 apart: at the padded row
@@ -271,7 +272,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 const int e = threadIdx.x + 256 * pi;
                 if (e < C * (BV / V8)) {
                     const int r = e / (BV / V8), cc = (e % (BV / V8)) * V8;
-                    if constexpr (do_rows<T, C>()) {
+                    if constexpr (do_rows<T, C, BV>()) {
                         // rows as loaded (the product reads them through transposed loads)
                         st16(sDo + r * LDO + cc, r < len ? cur.dov[pi] : Vec16{});
                     } else {
@@ -353,7 +354,7 @@ __device__ __forceinline__ void sweep_run(const Params& p, int n, int h, int v0,
                 for (int k2 = 0; k2 < C / KS; ++k2) {
                     bxs[ct][k2] = frag_kc_swz<T, C, BV, C>(sX, LX, 16 * ct, k2 * KS);
                     if constexpr (DIR == 1)
-                        bdo[ct][k2] = do_rows<T, C>() ? frag_ks(sDo, LDO, 16 * ct, k2 * KS)    // do^T from do rows
+                        bdo[ct][k2] = do_rows<T, C, BV>() ? frag_ks(sDo, LDO, 16 * ct, k2 * KS)    // do^T from do rows
                                                       : frag_kc_swz<T, C, BV, C>(sDo, LX, 16 * ct, k2 * KS);
                 }
             __builtin_amdgcn_sched_barrier(0);
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256) void gdr_sweep(Params p) {
     static_assert(kTileV % (16 / sizeof(T)) == 0, "a 16-byte piece lies within one stored tile");
     __shared__ __attribute__((aligned(16))) T sS[2][BV * LS];
     __shared__ __attribute__((aligned(16))) T sX[2][BV * LX];
-    __shared__ __attribute__((aligned(16))) T sDo[2][do_rows<T, C>() ? C * do_pitch<T, BV>() : BV * LX];
+    __shared__ __attribute__((aligned(16))) T sDo[2][do_rows<T, C, BV>() ? C * do_pitch<T, BV>() : BV * LX];
     // per wave: its 32-column block of k~ / w (C / 16 fragment-order tiles)
     __shared__ __attribute__((aligned(16))) T sA2[sweep_transposes_a2<T, C, D, BV>() ? 4 * (C / 16) * 512 : 8];
 
