@@ -222,15 +222,15 @@ WIDE = {
 }
 
 
-# Sequences of more than 64 chunks on 32-column sweep tiles at chunk 64: the
+# Sequences of more than 128 chunks on 32-column sweep tiles at chunk 64: the
 # sweep refills its operand registers part by part within each step there;
 # every element compared, at every (io, K) form of that sweep.
 SPREAD = {
-    "bf16_d128": scaled(KDA16, B=1, T=64 * 70 + 9, H=2, Hg=2, h0_std=0.1, dht_std=0.1, seed=71),
-    "f16_d128": scaled(KDA16, B=1, T=64 * 66, H=2, Hg=1, io_dtype=torch.float16, gate_mult=0.25, dht_std=0.1,
+    "bf16_d128": scaled(KDA16, B=1, T=64 * 134 + 9, H=2, Hg=2, h0_std=0.1, dht_std=0.1, seed=71),
+    "f16_d128": scaled(KDA16, B=1, T=64 * 130, H=2, Hg=1, io_dtype=torch.float16, gate_mult=0.25, dht_std=0.1,
                        seed=72),
-    "bf16_d64": scaled(KDA16, B=2, T=64 * 65 + 1, H=2, Hg=2, K=64, V=64, dht_std=0.1, seed=73),
-    "fp32_d64": scaled(TINY, B=1, T=64 * 67 + 30, H=2, Hg=2, h0_std=0.1, dht_std=0.1, seed=74),
+    "bf16_d64": scaled(KDA16, B=2, T=64 * 129 + 1, H=2, Hg=2, K=64, V=64, dht_std=0.1, seed=73),
+    "fp32_d64": scaled(TINY, B=1, T=64 * 131 + 30, H=2, Hg=2, h0_std=0.1, dht_std=0.1, seed=74),
 }
 
 
@@ -238,7 +238,7 @@ SPREAD = {
 def test_long_sequence_spread_refills(name):
     w = SPREAD[name]
     nch = (w.T + w.chunk - 1) // w.chunk
-    assert w.chunk == 64 and nch > 64 and 2 * w.B * w.H * (w.V // 32) < 512
+    assert w.chunk == 64 and nch > 128 and 2 * w.B * w.H * (w.V // 32) < 512
     _check(tu.parity(w), tu.tolerance(w), name)
 
 
