@@ -166,7 +166,7 @@ CSRC = "chunked_gated_delta_gdr_amd/csrc/"
 KERNEL_SOURCES = {
     "gdr_chunk_table": ("gdr_prep.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
     "gdr_prep": ("gdr_prep.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
-    "gdr_sweep": ("gdr_sweep.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
+    "gdr_sweep": ("gdr_sweep.hpp", "gdr_sweep_ws.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
     "gdr_chunk_bwd": ("gdr_chunk_bwd.hpp", "gdr_common.hpp", "gdr_launch.hpp"),
 }
 COPY_KERNEL_KEY = "neg_kernel"   # torch.neg(out=...): reads N bytes, writes N bytes

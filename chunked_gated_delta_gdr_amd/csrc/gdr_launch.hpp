@@ -5,6 +5,7 @@
 #include "gdr_prep.hpp"
 #include "gdr_states.hpp"
 #include "gdr_sweep.hpp"
+#include "gdr_sweep_ws.hpp"
 
 namespace gdr {
 
@@ -85,13 +86,19 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
             if (narrow) gdr_sweep<T, C, D, kSweepBV1, true><<<dim3(p.N * p.H * (D / kSweepBV1)), dim3(256), 0, stream>>>(p);
         }
         if (!narrow) {
-            // C = 64, 32-column tiles: more than 128 chunks per sequence (on
-            // average; nc_max bounds the total) take the refills spread over
-            // the step (measured with two sets in flight: 1.74 vs 1.80 ms at
-            // 1024 chunks; 190.1 vs 189.0 us at 128 chunks; at 64 chunks
-            // 127 vs 121 us)
-            if (C == 64 && p.nc_max > 128 * p.N) gdr_sweep<T, C, D, kSweepBV, C == 64><<<dim3(tiles32), dim3(256), 0, stream>>>(p);
-            else gdr_sweep<T, C, D, kSweepBV><<<dim3(tiles32), dim3(256), 0, stream>>>(p);
+            if constexpr (sizeof(T) == 2 && C == 64 && D == 128) {
+                // loader waves (headline sweep 121.1 -> 117.7 us, 1024 chunks
+                // per sequence 1739 -> 1704 us)
+                gdr_sweep_ws<T, C, D, kSweepBV><<<dim3(tiles32), dim3(512), 0, stream>>>(p);
+            } else {
+                // C = 64, 32-column tiles: more than 128 chunks per sequence (on
+                // average; nc_max bounds the total) take the refills spread over
+                // the step (measured with two sets in flight: 1.74 vs 1.80 ms at
+                // 1024 chunks; 190.1 vs 189.0 us at 128 chunks; at 64 chunks
+                // 127 vs 121 us)
+                if (C == 64 && p.nc_max > 128 * p.N) gdr_sweep<T, C, D, kSweepBV, C == 64><<<dim3(tiles32), dim3(256), 0, stream>>>(p);
+                else gdr_sweep<T, C, D, kSweepBV><<<dim3(tiles32), dim3(256), 0, stream>>>(p);
+            }
         }
     }
     if (e == hipSuccess) e = mark(3);
