@@ -233,7 +233,9 @@ def _read_counter_csv(path: str) -> dict:
 
 
 def _kernel_name(names, kernel: str):
-    m = [n for n in names if f"{kernel}<" in n or f"{kernel}I" in n]
+    # the sweep has two kernels: gdr_sweep, and gdr_sweep_ws (loader waves)
+    keys = (f"{kernel}<", f"{kernel}I") + ((f"{kernel}_wsI",) if kernel == "gdr_sweep" else ())
+    m = [n for n in names if any(k in n for k in keys)]
     if len(m) > 1:
         raise SystemExit(f"several kernels match {kernel!r}: {m}")
     return m[0] if m else None
