@@ -29,6 +29,11 @@
 // G_last / 2 per column (exponents of either sign, bounded as above). The
 // bound is checked per chunk from its cumsum; a chunk beyond it takes the
 // per-boundary route.
+// With a scalar gate (one G per row) the decay 2^(G_r - G_s) is the same for
+// every channel, so Aqk and Akk are the plain products q k^T and k k^T over D
+// (operands as loaded), each element then times its decay (exponent <= 0
+// below the diagonal) in fp32: one route for every chunk at C = 64 or 32, no
+// operand scaling and no bound (GDN GQA workload prep 475 -> 418 us).
 #pragma once
 #include "gdr_common.hpp"
 
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         // one gate per row: every wave scans the chunk's C gates across its
         // lanes (lane = row; rows past the end add 0, so they take G_last) and
         // writes its pieces of the cumsum G and of 2^g broadcast over the
-        // columns; the chunk's range check comes from the same scan
+        // columns
         static_assert(C <= 64, "one row per lane");
         const int ll = tid & 63;
         const float gr = ll < len ? gsc : 0.f;
@@ -325,11 +330,6 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         for (int off = 1; off < C; off <<= 1) {
             const float y = __shfl_up(G, off);
             G += ll >= off ? y : 0.f;
-        }
-        if constexpr (L::FAST) {
-            const float tot = __shfl(G, C - 1);
-            const float dev = wave_max(ll < C ? fabsf(G - 0.5f * tot) : 0.f);
-            if (ll == 0) flags[w] = dev;
         }
 #pragma unroll
         for (int i = 0; i < NGP; ++i) {
@@ -401,7 +401,9 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     // reference per column; else through the block boundaries and the
     // diagonal blocks' own rows, as below.
     bool fast = false;
-    if constexpr (L::FAST) {
+    if constexpr (L::FAST && SCALAR) {
+        fast = true;   // plain q k^T and k k^T times the decay: no operand scaling, no guard
+    } else if constexpr (L::FAST) {
         constexpr float guard = __is_same(T, _Float16) ? 8.f : 64.f;
         float m = 0.f;
 #pragma unroll
@@ -439,11 +441,13 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
         //      take either sign; the check above bounds them by the guard, so
         //      the scaled operands stay finite and normal in T, as in the
         //      diagonal-block form below, here for the whole chunk at once.
-        //      Each term is still one product of two rounded operands. ----
+        //      Each term is still one product of two rounded operands.
+        //      Scalar gate: the products take q and k as loaded, and the
+        //      decay multiplies each element as it is written. ----
         T* xq = reinterpret_cast<T*>(smem + L::X_OFF);   // [C][LT] each
         T* xkq = xq + C * LT;
         T* xk = xkq + C * LT;
-        {   // all LDS reads of the thread's pieces first (one wait), then the writes
+        if constexpr (!SCALAR) {   // all LDS reads of the thread's pieces first (one wait), then the writes
             constexpr int NP = C * (D / 8) / NT;
             static_assert(NP * NT == C * (D / 8), "piece split");
             static_assert(NT % (D / 8) == 0, "a thread's pieces share their columns");
@@ -475,8 +479,8 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
                 store8<T>(xkq + r * LT + d0, b);
                 store8<T>(xk + r * LT + d0, c);
             }
+            __syncthreads();
         }
-        __syncthreads();
         // the lower 16 x 16 tiles of Aqk (t < NLT) and Akk (t >= NLT), tile t
         // on wave t % NW; the tile loops are unrolled, so that each copy's
         // block indices and masks are constants and only the wave's own copies run
@@ -495,7 +499,8 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             int bi, bj;
             tile_ij(t % NLT, bi, bj);
             f32x4 a1[1] = {zero4()};
-            panel_mma<T, 1, D>(a1, t >= NLT ? xkq : xq, LT, 16 * bi, xk, LT, 16 * bj, l);
+            if constexpr (SCALAR) panel_mma<T, 1, D>(a1, t >= NLT ? kL : qL, LT, 16 * bi, kL, LT, 16 * bj, l);
+            else panel_mma<T, 1, D>(a1, t >= NLT ? xkq : xq, LT, 16 * bi, xk, LT, 16 * bj, l);
             accT[t / L::NW] = a1[0];
         }
         __syncthreads();   // the operand reads are done: Aqk and Akk overlay them
@@ -509,10 +514,19 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
             float bsv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) bsv[e] = kk ? bs[16 * bi + acc_row(e, l)] : 1.f;
+            float dec[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (SCALAR) {   // G is stored broadcast over the columns
+                const float gs = Gs[(16 * bj + acc_col(l)) * LF];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * bi + acc_row(e, l), s2 = 16 * bj + acc_col(l);
+                    dec[e] = s2 <= r ? fast_exp2(Gs[r * LF] - gs) : 0.f;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * bi + acc_row(e, l), s2 = 16 * bj + acc_col(l);
-                const float v = accT[t / L::NW][e];
+                const float v = accT[t / L::NW][e] * dec[e];
                 if (kk) AkkF[r * LCF + s2] = s2 < r ? bsv[e] * v : 0.f;
                 else AqkF[r * LCF + s2] = s2 <= r ? v : 0.f;
             }

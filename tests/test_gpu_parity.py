@@ -129,7 +129,6 @@ ONE_REF_MIXED = {
     "bf16_c32": (scaled(KDA16, B=1, T=200, H=3, Hg=3, chunk=32, gate_mult=4.0, dht_std=0.1, seed=53), 64.0),
     "f16_c32": (scaled(KDA16, B=1, T=200, H=3, Hg=3, chunk=32, io_dtype=torch.float16, gate_mult=0.5,
                        dht_std=0.1, seed=53), 8.0),
-    "f16_c32_gdn_gqa": (scaled(GDN, B=1, T=200, H=4, Hg=2, gate_mult=1.0, seed=59), 8.0),
     "f32_c32": (scaled(TINY, T=130, chunk=32, gate_mult=4.0, h0_std=0.1, dht_std=0.1, seed=57), 64.0),
 }
 
@@ -142,6 +141,16 @@ def test_prep_one_reference_bound_mixed(name):
     (chunk, head) items of both kinds, at both chunk sizes."""
     w, guard = ONE_REF_MIXED[name]
     fast, slow = tu.one_reference_split(w, guard)
+    assert fast > 0 and slow > 0, (fast, slow)
+    _check(tu.parity(w), tu.tolerance(w))
+
+
+def test_gdn_scalar_prep_across_the_operand_bound():
+    """Scalar gate: the preparation kernel forms Aqk / Akk as plain products
+    times the decay for every chunk, including chunks whose gate range is past
+    the bound that sends per-channel chunks to the per-boundary route."""
+    w = scaled(GDN, B=1, T=200, H=4, Hg=2, gate_mult=1.0, seed=59)
+    fast, slow = tu.one_reference_split(w, 8.0)
     assert fast > 0 and slow > 0, (fast, slow)
     _check(tu.parity(w), tu.tolerance(w))
 
