@@ -320,8 +320,8 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
     if constexpr (SCALAR) {
         // one gate per row: every wave scans the chunk's C gates across its
         // lanes (lane = row; rows past the end add 0, so they take G_last) and
-        // writes its pieces of the cumsum G and of 2^g broadcast over the
-        // columns
+        // writes its pieces of the cumsum G (and, for the per-block route, of
+        // 2^g) broadcast over the columns
         static_assert(C <= 64, "one row per lane");
         const int ll = tid & 63;
         const float gr = ll < len ? gsc : 0.f;
@@ -334,9 +334,12 @@ __global__ __launch_bounds__(128 * (C / 16)) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int i = 0; i < NGP; ++i) {
             const int e = tid + i * NT, r = e / (D / 4), d0 = (e % (D / 4)) * 4;
-            const float Gv = __shfl(G, r), ex = fast_exp2(__shfl(gr, r));
+            const float Gv = __shfl(G, r);
             *reinterpret_cast<f32x4*>(Gs + r * LF + d0) = f32x4{Gv, Gv, Gv, Gv};
-            *reinterpret_cast<f32x4*>(At + r * LF + d0) = f32x4{ex, ex, ex, ex};
+            if constexpr (!L::FAST) {   // only the per-block route reads 2^g
+                const float ex = fast_exp2(__shfl(gr, r));
+                *reinterpret_cast<f32x4*>(At + r * LF + d0) = f32x4{ex, ex, ex, ex};
+            }
         }
     } else {
 #pragma unroll
