@@ -231,9 +231,10 @@ WIDE = {
 }
 
 
-# Sequences of more than 128 chunks on 32-column sweep tiles at chunk 64: the
-# sweep refills its operand registers part by part within each step there;
-# every element compared, at every (io, K) form of that sweep.
+# Sequences of more than 128 chunks on 32-column sweep tiles at chunk 64,
+# every element compared: with K = 64 or fp32 io the register-set sweep
+# refills its operands part by part within each step there; with 16-bit io at
+# K = 128 the loader-wave sweep walks the same long sequences.
 SPREAD = {
     "bf16_d128": scaled(KDA16, B=1, T=64 * 134 + 9, H=2, Hg=2, h0_std=0.1, dht_std=0.1, seed=71),
     "f16_d128": scaled(KDA16, B=1, T=64 * 130, H=2, Hg=1, io_dtype=torch.float16, gate_mult=0.25, dht_std=0.1,
