@@ -1,5 +1,6 @@
 // gdr_sweep_ws.hpp -- the two state sweeps with loader waves, for 16-bit
-// operands, C = 64, D = 128 and 32-column V tiles.
+// operands at D = 128: C = 64 with 32-column V tiles, C = 32 with 64-column
+// tiles.
 //
 // Same recurrences, block order and workspace layouts as gdr_sweep (forward:
 // X_c = u_c - w_c h_c, h_{c+1} = Diag(2^G_last) h_c + k~_c^T X_c; reverse:
@@ -14,10 +15,11 @@
 //   into LDS with 16-byte direct-to-LDS loads (no registers on the way) and
 //   do nothing else, so their memory counter holds only those loads.
 // Measured against gdr_sweep's register sets: headline sweep 121.1 -> 117.7
-// us, 1024 chunks per sequence 1739 -> 1704 us. (Loader waves that also
-// stored h and X / T were no faster than the register sets: their waits for
-// the next chunk's operands then also waited for those stores. A third
-// buffer for the update's operands, two steps ahead, gained nothing more.)
+// us, 1024 chunks per sequence 1739 -> 1704 us; GDN GQA workload (C = 32,
+// 64-column tiles) 889 -> 876 us. (Loader waves that also stored h and X / T
+// were no faster than the register sets: their waits for the next chunk's
+// operands then also waited for those stores. A third buffer for the
+// update's operands, two steps ahead, gained nothing more.)
 //
 // Two operand buffers, each split by when a step has finished with its part:
 //   early: the chunk-row product's operands (w / k~ fragments, the update's
@@ -35,7 +37,8 @@ namespace gdr {
 
 template <typename T, int C, int D, int BV>
 struct SweepWs {
-    static_assert(sizeof(T) == 2 && BV == 32 && D == 128 && C == 64, "loader-wave sweep: 16-bit, C 64, D 128, 32 columns");
+    static_assert(sizeof(T) == 2 && D == 128 && ((C == 64 && BV == 32) || (C == 32 && BV == 64)),
+                  "loader-wave sweep: 16-bit, D 128, C 64 with 32 columns or C 32 with 64");
     using S = SweepTiles<T, C, D, BV>;
     static constexpr int LS = D + pad<T>();   // state^T rows [BV][LS]
     static constexpr int LX = C + pad<T>();   // X^T / -T^T rows [BV][LX]
@@ -47,8 +50,12 @@ struct SweepWs {
     static constexpr int DO = A3 + D * C * 2;          // rev: do rows [C][BV], 16-byte pieces swizzled
     static constexpr int GL = DO + C * BV * 2;         // 2^G_last [D] fp32
     static constexpr int BUF = GL + D * 4;
-    // loads per loader wave in the early part (forward, reverse)
-    static constexpr int N_EARLY_F = 4 + 4 + 1, N_EARLY_R = 4 + 4;
+    // 1 KB blocks of a C x D operand per loader wave; loads per loader wave in
+    // the early part (forward, reverse)
+    static constexpr int NBW = C * D / 2048;
+    static_assert(BV * C == 2048 && C * BV / 8 == 256, "u^T tile: 4 blocks; do: 256 pieces");
+    static constexpr int N_EARLY_F = 2 * NBW + 1, N_EARLY_R = 2 * NBW;
+    static constexpr int PPR = BV / 8;   // 16-byte pieces per do row
 };
 
 // 16 bytes per lane from global memory to LDS (lane l writes lds + 16 l; the
@@ -66,18 +73,24 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// do rows [C][32] in LDS as 16-byte pieces: piece pc of row r at slot
-// 4 r + (pc ^ 2 ((r >> 1) & 1)), so the transposed reads of four consecutive
-// rows (two pieces each) cover all 32 banks once
-__device__ __forceinline__ int do_slot(int r, int pc) { return 4 * r + (pc ^ (((r >> 1) & 1) << 1)); }
+// do rows [C][BV] in LDS as 16-byte pieces, XOR-swizzled by row so that the
+// transposed reads of four consecutive rows (two pieces each) cover all 32
+// banks once: 32 columns (64-byte rows, two rows per bank window) piece pc of
+// row r at 4 r + (pc ^ 2 ((r >> 1) & 1)); 64 columns (128-byte rows) at
+// 8 r + (pc ^ 2 (r & 3))
+template <int BV>
+__device__ __forceinline__ int do_slot(int r, int pc) {
+    if constexpr (BV == 32) return 4 * r + (pc ^ (((r >> 1) & 1) << 1));
+    else return 8 * r + (pc ^ ((r & 3) << 1));
+}
 
 // do^T fragment (v columns i0 + (l & 15), rows k0 + 8 (l >> 4) + 0..7) from
 // those swizzled rows: two transposed loads, as frag_ks
-template <typename T>
+template <typename T, int BV>
 __device__ __forceinline__ typename Mfma<T>::frag frag_do_ws(const T* rows, int i0, int k0, int l) {
     auto piece = [&](int kk) {
         const int r = kk + ((l & 15) >> 2), c = i0 + 4 * (l & 3);
-        const T* q = rows + do_slot(r, c >> 3) * 8 + (c & 7);
+        const T* q = rows + do_slot<BV>(r, c >> 3) * 8 + (c & 7);
         return __builtin_bit_cast(
             uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q)));
     };
@@ -152,7 +165,8 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
 #pragma unroll
                     for (int ct = 0; ct < SCT; ++ct) {
                         const int d = 16 * (w * S::SRW + i) + acc_row(0), c = 16 * ct + acc_col();
-                        store4<T>(sS + c * LS + d, st[i][ct][0], st[i][ct][1], st[i][ct][2], st[i][ct][3]);
+                        store4<T>(sS + c * LS + (d ^ sweep_swz<T, C, BV, D>(c)), st[i][ct][0], st[i][ct][1], st[i][ct][2],
+                                  st[i][ct][3]);
                     }
                 __syncthreads();
                 // 2. chunk-row product X = u - w h (fwd) / -T = -k~ dh (rev); all
@@ -165,7 +179,7 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
 #pragma unroll
                     for (int jj = 0; jj < S::XCT; ++jj)
 #pragma unroll
-                        for (int k2 = 0; k2 < D / KS; ++k2) bx[jj][k2] = frag_kc(sS, LS, 16 * S::xcol(w, jj), k2 * KS, l);
+                        for (int k2 = 0; k2 < D / KS; ++k2) bx[jj][k2] = frag_kc_swz<T, C, BV, D>(sS, LS, 16 * S::xcol(w, jj), k2 * KS, l);
 #pragma unroll
                     for (int i = 0; i < S::XRT; ++i)
 #pragma unroll
@@ -202,7 +216,7 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
                             float o[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) o[e] = DIR == 0 ? to_f32(uq[i][jj][e]) - acc[jj][e] : -acc[jj][e];
-                            store4<T>(sX + c * LX + r, o[0], o[1], o[2], o[3]);
+                            store4<T>(sX + c * LX + (r ^ sweep_swz<T, C, BV, C>(c)), o[0], o[1], o[2], o[3]);
                         }
                     }
                     __syncthreads();
@@ -214,9 +228,9 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
                     for (int ct = 0; ct < SCT; ++ct)
 #pragma unroll
                         for (int k2 = 0; k2 < C / KS; ++k2) {
-                            bxs[ct][k2] = frag_kc(sX, LX, 16 * ct, k2 * KS, l);
+                            bxs[ct][k2] = frag_kc_swz<T, C, BV, C>(sX, LX, 16 * ct, k2 * KS, l);
                             if constexpr (DIR == 1)
-                                bdo[ct][k2] = frag_do_ws(reinterpret_cast<const T*>(ob + W::DO), 16 * ct, k2 * KS, l);
+                                bdo[ct][k2] = frag_do_ws<T, BV>(reinterpret_cast<const T*>(ob + W::DO), 16 * ct, k2 * KS, l);
                         }
                     if constexpr (DIR == 1) {
                         const T* A3 = reinterpret_cast<const T*>(ob + W::A3);
@@ -252,25 +266,54 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
                     }
                 }
                 {   // the incoming state and X (T) of this chunk to the workspace,
-                    // read back from LDS while the update's MFMAs run (row-major
-                    // pieces of 8 columns through transposed loads, as gdr_sweep)
+                    // read back from LDS while the update's MFMAs run, row-major
+                    // pieces of 8 columns: through transposed loads at 32 columns,
+                    // through 16-bit reads of the swizzled buffers at 64 (as gdr_sweep)
                     const int it = chunk_it(k);
                     const size_t jh = (size_t)(c0 + it) * p.H + h;
                     T* gS = static_cast<T*>(DIR == 0 ? p.hbuf : p.dhbuf) + jh * D * D;
-#pragma unroll
-                    for (int t2 = 0; t2 < 2; ++t2) {
-                        const int dt = w + 4 * t2;
-                        const uint64_t a = ks_tr4_bits(sS, LS, 16 * dt, 0, 8, l);
-                        const uint64_t b = ks_tr4_bits(sS, LS, 16 * dt, 4, 8, l);
-                        const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
-                        st16(gS + tiled_index<D, BV>(16 * dt + (l & 15), v0, 8 * (l >> 4)), v);
-                    }
                     T* gX = static_cast<T*>(DIR == 0 ? p.xbuf : p.tbuf) + jh * C * D;
-                    constexpr uint64_t kNeg = DIR == 0 ? 0 : 0x8000800080008000ull;
-                    const uint64_t a = ks_tr4_bits(sX, LX, 16 * w, 0, 8, l) ^ kNeg;
-                    const uint64_t b = ks_tr4_bits(sX, LX, 16 * w, 4, 8, l) ^ kNeg;
-                    const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
-                    st16(gX + tiled_index<C, BV>(16 * w + (l & 15), v0, 8 * (l >> 4)), v);
+                    if constexpr (BV == 32) {
+#pragma unroll
+                        for (int t2 = 0; t2 < 2; ++t2) {
+                            const int dt = w + 4 * t2;
+                            const uint64_t a = ks_tr4_bits(sS, LS, 16 * dt, 0, 8, l);
+                            const uint64_t b = ks_tr4_bits(sS, LS, 16 * dt, 4, 8, l);
+                            const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
+                            st16(gS + tiled_index<D, BV>(16 * dt + (l & 15), v0, 8 * (l >> 4)), v);
+                        }
+                        constexpr uint64_t kNeg = DIR == 0 ? 0 : 0x8000800080008000ull;
+                        const uint64_t a = ks_tr4_bits(sX, LX, 16 * w, 0, 8, l) ^ kNeg;
+                        const uint64_t b = ks_tr4_bits(sX, LX, 16 * w, 4, 8, l) ^ kNeg;
+                        const Vec16 v = {{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)}};
+                        st16(gX + tiled_index<C, BV>(16 * w + (l & 15), v0, 8 * (l >> 4)), v);
+                    } else {
+                        constexpr int V8 = 16 / sizeof(T), NPS = D * BV / V8, NPX = C * BV / V8;
+                        static_assert(NPS % 256 == 0 && NPX % 256 == 0, "whole rounds of the compute threads");
+#pragma unroll
+                        for (int pi = 0; pi < NPS / 256; ++pi) {
+                            const int e = (int)threadIdx.x + 256 * pi;
+                            const int d = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                            Vec16 v;
+                            T* vp = reinterpret_cast<T*>(&v);
+#pragma unroll
+                            for (int q = 0; q < V8; ++q) vp[q] = sS[(c + q) * LS + (d ^ sweep_swz<T, C, BV, D>(c + q))];
+                            st16(gS + tiled_index<D, BV>(d, v0, c), v);
+                        }
+#pragma unroll
+                        for (int pi = 0; pi < NPX / 256; ++pi) {
+                            const int e = (int)threadIdx.x + 256 * pi;
+                            const int r = e / (BV / V8), c = (e % (BV / V8)) * V8;
+                            Vec16 v;
+                            T* vp = reinterpret_cast<T*>(&v);
+#pragma unroll
+                            for (int q = 0; q < V8; ++q) {
+                                const T x = sX[(c + q) * LX + (r ^ sweep_swz<T, C, BV, C>(c + q))];
+                                vp[q] = DIR == 0 ? x : from_f32<T>(-to_f32(x));
+                            }
+                            st16(gX + tiled_index<C, BV>(r, v0, c), v);
+                        }
+                    }
                 }
             }
         }
@@ -303,9 +346,9 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
         const T* A1g = static_cast<const T*>(DIR == 0 ? p.w : p.kt) + jh * C * D;
         const T* A2g = static_cast<const T*>(DIR == 0 ? p.kt : p.w) + jh * C * D;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) dma16(A1g + (lw * 4 + b) * 512 + l * 8, ob + W::A1 + (lw * 4 + b) * 1024);
+        for (int b = 0; b < W::NBW; ++b) dma16(A1g + (lw * W::NBW + b) * 512 + l * 8, ob + W::A1 + (lw * W::NBW + b) * 1024);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) dma16(A2g + (lw * 4 + b) * 512 + l * 8, ob + W::A2 + (lw * 4 + b) * 1024);
+        for (int b = 0; b < W::NBW; ++b) dma16(A2g + (lw * W::NBW + b) * 512 + l * 8, ob + W::A2 + (lw * W::NBW + b) * 1024);
         if constexpr (DIR == 0) {
             const T* Ug = static_cast<const T*>(p.uT) + jh * D * C + (v0 / 16) * (C / 16) * 256;
             dma16(Ug + lw * 512 + l * 8, ob + W::U + lw * 1024);
@@ -317,10 +360,11 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
         if constexpr (DIR == 1) {
             const T* A3g = static_cast<const T*>(p.qsT) + jh * D * C;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) dma16(A3g + (lw * 4 + b) * 512 + l * 8, ob + W::A3 + (lw * 4 + b) * 1024);
+            for (int b = 0; b < W::NBW; ++b) dma16(A3g + (lw * W::NBW + b) * 512 + l * 8, ob + W::A3 + (lw * W::NBW + b) * 1024);
             // do: this lane's LDS slot s holds piece pc of row r; rows past the
             // sequence end read its last row and are zeroed once landed
-            const int s = lw * 64 + l, r = s >> 2, pc = (s & 3) ^ (((r >> 1) & 1) << 1);
+            const int s = lw * 64 + l, r = s / W::PPR, pc0 = s % W::PPR;
+            const int pc = do_slot<BV>(r, pc0) - W::PPR * r;   // the slot map is an involution within a row
             const int len = min(C, slen - it * C);
             const int rr = min(r, len - 1);
             dma16(static_cast<const T*>(p.dout) + ((size_t)(stok0 + it * C + rr) * p.H + h) * D + v0 + 8 * pc,
@@ -336,7 +380,7 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
             if (k < nch) {
                 const int it = chunk_it(k);
                 const int len = min(C, slen - it * C);
-                const int s = lw * 64 + l, r = s >> 2;
+                const int s = lw * 64 + l, r = s / W::PPR;
                 if (r >= len) st16(ob + W::DO + s * 16, Vec16{});
             }
         }
@@ -367,6 +411,7 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
 // the block order of gdr_sweep.
 template <typename T, int C, int D, int BV>
 __global__ __launch_bounds__(512) void gdr_sweep_ws(Params p) {
+    static_assert(kTileV % BV == 0 || BV % kTileV == 0, "sweep V tiles and stored tiles nest");
     using W = SweepWs<T, C, D, BV>;
     __shared__ __attribute__((aligned(16))) char lds[2 * W::BUF + 2 * BV * (W::LS + W::LX) * (int)sizeof(T)];
     constexpr int NV = D / BV;
