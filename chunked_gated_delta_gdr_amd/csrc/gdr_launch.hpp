@@ -77,7 +77,7 @@ hipError_t launch_front(const Params& p, hipStream_t stream, hipEvent_t const* e
     if (wide) {
         // refills spread over the step (measured: C = 64 with one set of
         // operands in flight 400 -> 363 us varlen; C = 32 878 -> 866 us GDN GQA)
-        if constexpr (sizeof(T) == 2 && C == 32 && D == 128)   // loader waves (GDN GQA sweep 889 -> 876 us)
+        if constexpr (sizeof(T) == 2 && D == 128)   // loader waves (GDN GQA sweep 889 -> 876 us, varlen 363 -> 350 us)
             gdr_sweep_ws<T, C, D, kSweepBVW><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(512), 0, stream>>>(p);
         else
             gdr_sweep<T, C, D, kSweepBVW, true><<<dim3(p.dirs * p.N * p.H * (D / kSweepBVW)), dim3(256), 0, stream>>>(p);

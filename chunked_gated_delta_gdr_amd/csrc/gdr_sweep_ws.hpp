@@ -1,6 +1,6 @@
 // gdr_sweep_ws.hpp -- the two state sweeps with loader waves, for 16-bit
-// operands at D = 128: C = 64 with 32-column V tiles, C = 32 with 64-column
-// tiles.
+// operands at D = 128: C = 64 with 32- or 64-column V tiles, C = 32 with
+// 64-column tiles.
 //
 // Same recurrences, block order and workspace layouts as gdr_sweep (forward:
 // X_c = u_c - w_c h_c, h_{c+1} = Diag(2^G_last) h_c + k~_c^T X_c; reverse:
@@ -16,7 +16,8 @@
 //   do nothing else, so their memory counter holds only those loads.
 // Measured against gdr_sweep's register sets: headline sweep 121.1 -> 117.7
 // us, 1024 chunks per sequence 1739 -> 1704 us; GDN GQA workload (C = 32,
-// 64-column tiles) 889 -> 876 us. (Loader waves that also stored h and X / T
+// 64-column tiles) 889 -> 876 us; varlen workload (C = 64, 64-column tiles)
+// 363 -> 350 us. (Loader waves that also stored h and X / T
 // were no faster than the register sets: their waits for the next chunk's
 // operands then also waited for those stores. A third buffer for the
 // update's operands, two steps ahead, gained nothing more.)
@@ -37,8 +38,8 @@ namespace gdr {
 
 template <typename T, int C, int D, int BV>
 struct SweepWs {
-    static_assert(sizeof(T) == 2 && D == 128 && ((C == 64 && BV == 32) || (C == 32 && BV == 64)),
-                  "loader-wave sweep: 16-bit, D 128, C 64 with 32 columns or C 32 with 64");
+    static_assert(sizeof(T) == 2 && D == 128 && ((C == 64 && (BV == 32 || BV == 64)) || (C == 32 && BV == 64)),
+                  "loader-wave sweep: 16-bit, D 128, C 64 with 32 or 64 columns, C 32 with 64");
     using S = SweepTiles<T, C, D, BV>;
     static constexpr int LS = D + pad<T>();   // state^T rows [BV][LS]
     static constexpr int LX = C + pad<T>();   // X^T / -T^T rows [BV][LX]
@@ -53,9 +54,16 @@ struct SweepWs {
     // 1 KB blocks of a C x D operand per loader wave; loads per loader wave in
     // the early part (forward, reverse)
     static constexpr int NBW = C * D / 2048;
-    static_assert(BV * C == 2048 && C * BV / 8 == 256, "u^T tile: 4 blocks; do: 256 pieces");
-    static constexpr int N_EARLY_F = 2 * NBW + 1, N_EARLY_R = 2 * NBW;
+    static constexpr int NUW = BV * C / 2048;     // 1 KB blocks of the u^T tile per loader wave
+    static constexpr int NDW = C * BV / 8 / 256;  // do pieces per loader-wave lane
+    static_assert(NUW * 2048 == BV * C && NDW * 2048 == C * BV, "whole blocks per loader wave");
+    static constexpr int N_EARLY_F = 2 * NBW + NUW, N_EARLY_R = 2 * NBW;
     static constexpr int PPR = BV / 8;   // 16-byte pieces per do row
+    // X / T single-buffered at C = 64 with 64 columns (to fit the LDS): every
+    // read of step k's X is done before any wave passes step k+1's first
+    // barrier, after which the next X is written
+    static constexpr bool SX1 = C == 64 && BV == 64;
+    static constexpr int TOTAL = 2 * BUF + (2 * BV * LS + (SX1 ? 1 : 2) * BV * LX) * 2;
 };
 
 // 16 bytes per lane from global memory to LDS (lane l writes lds + 16 l; the
@@ -125,7 +133,7 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
     T* const sS0 = reinterpret_cast<T*>(lds + 2 * W::BUF);
     T* const sS1 = sS0 + BV * LS;
     T* const sX0 = sS1 + BV * LS;
-    T* const sX1 = sX0 + BV * LX;
+    T* const sX1 = W::SX1 ? sX0 : sX0 + BV * LX;
     char* const ob0 = lds;
     char* const ob1 = lds + W::BUF;
     // the wave's role must be a uniform branch: both roles hold barriers
@@ -351,7 +359,8 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
         for (int b = 0; b < W::NBW; ++b) dma16(A2g + (lw * W::NBW + b) * 512 + l * 8, ob + W::A2 + (lw * W::NBW + b) * 1024);
         if constexpr (DIR == 0) {
             const T* Ug = static_cast<const T*>(p.uT) + jh * D * C + (v0 / 16) * (C / 16) * 256;
-            dma16(Ug + lw * 512 + l * 8, ob + W::U + lw * 1024);
+#pragma unroll
+            for (int b = 0; b < W::NUW; ++b) dma16(Ug + (lw * W::NUW + b) * 512 + l * 8, ob + W::U + (lw * W::NUW + b) * 1024);
         }
     };
     auto late = [&](int k, char* ob) __attribute__((always_inline)) {
@@ -363,12 +372,15 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
             for (int b = 0; b < W::NBW; ++b) dma16(A3g + (lw * W::NBW + b) * 512 + l * 8, ob + W::A3 + (lw * W::NBW + b) * 1024);
             // do: this lane's LDS slot s holds piece pc of row r; rows past the
             // sequence end read its last row and are zeroed once landed
-            const int s = lw * 64 + l, r = s / W::PPR, pc0 = s % W::PPR;
-            const int pc = do_slot<BV>(r, pc0) - W::PPR * r;   // the slot map is an involution within a row
             const int len = min(C, slen - it * C);
-            const int rr = min(r, len - 1);
-            dma16(static_cast<const T*>(p.dout) + ((size_t)(stok0 + it * C + rr) * p.H + h) * D + v0 + 8 * pc,
-                  ob + W::DO + lw * 1024);
+#pragma unroll
+            for (int b = 0; b < W::NDW; ++b) {
+                const int s = (lw * W::NDW + b) * 64 + l, r = s / W::PPR, pc0 = s % W::PPR;
+                const int pc = do_slot<BV>(r, pc0) - W::PPR * r;   // the slot map is an involution within a row
+                const int rr = min(r, len - 1);
+                dma16(static_cast<const T*>(p.dout) + ((size_t)(stok0 + it * C + rr) * p.H + h) * D + v0 + 8 * pc,
+                      ob + W::DO + (lw * W::NDW + b) * 1024);
+            }
         }
         const float* Gg = p.glast + jh * D;
         if (l < 8) dma16(Gg + (lw * 8 + l) * 4, ob + W::GL + lw * 128);
@@ -380,8 +392,11 @@ __device__ __forceinline__ void sweep_run_ws(const Params& p, int n, int h, int 
             if (k < nch) {
                 const int it = chunk_it(k);
                 const int len = min(C, slen - it * C);
-                const int s = lw * 64 + l, r = s / W::PPR;
-                if (r >= len) st16(ob + W::DO + s * 16, Vec16{});
+#pragma unroll
+                for (int b = 0; b < W::NDW; ++b) {
+                    const int s = (lw * W::NDW + b) * 64 + l, r = s / W::PPR;
+                    if (r >= len) st16(ob + W::DO + s * 16, Vec16{});
+                }
             }
         }
     };
@@ -413,7 +428,7 @@ template <typename T, int C, int D, int BV>
 __global__ __launch_bounds__(512) void gdr_sweep_ws(Params p) {
     static_assert(kTileV % BV == 0 || BV % kTileV == 0, "sweep V tiles and stored tiles nest");
     using W = SweepWs<T, C, D, BV>;
-    __shared__ __attribute__((aligned(16))) char lds[2 * W::BUF + 2 * BV * (W::LS + W::LX) * (int)sizeof(T)];
+    __shared__ __attribute__((aligned(16))) char lds[W::TOTAL];
     constexpr int NV = D / BV;
     const int nh = p.N * p.H, per_dir = NV * nh;
     const int rd = blockIdx.x / per_dir;
