@@ -252,6 +252,38 @@ def test_long_sequence_spread_refills(name):
     _check(tu.parity(w), tu.tolerance(w), name)
 
 
+WIDE_VARLEN = {
+    # (base workload, io dtype, chunk, q/k heads): 8 sequences x 8 value heads
+    # fill 2 x 8 x 8 x 4 = 512 >= 2 x 256 32-column tiles, so the sweep takes
+    # 64-column tiles (the loader-wave sweep at 16-bit K = 128)
+    "bf16_kda_c64": (KDA16, torch.bfloat16, 64, 8),
+    "f16_gdn_gqa_c32": (GDN, torch.float16, 32, 4),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_VARLEN))
+def test_wide_sweep_tiles_varlen_short_and_empty(name):
+    """64-column sweep tiles over packed sequences of 0, 1, one-chunk and
+    ragged multi-chunk lengths (fewer chunks than the operands requested
+    ahead, and empty ones): every output element compared with the oracle,
+    and the empty sequences pass dht through to dh0."""
+    base, io, chunk, hg = WIDE_VARLEN[name]
+    lens = [0, 197, 1, 0, 64, 200, 33, 0]
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens), 0).to(torch.int32)
+    w = scaled(base, B=1, T=int(cu[-1]), H=8, Hg=hg, n_seqs=1, chunk=chunk, io_dtype=io, seed=83)
+    inp = make_inputs(w)
+    gen = torch.Generator().manual_seed(83)
+    inp["cu_seqlens"] = cu
+    inp["h0"] = torch.randn(len(lens), w.H, w.K, w.V, generator=gen) * 0.1
+    inp["dht"] = torch.randn(len(lens), w.H, w.K, w.V, generator=gen) * 0.1
+    gpu = tu.run_gpu(inp)
+    _check(tu.rel_errors(gpu, tu.run_oracle(inp), tu.real_token_mask(inp)), tu.tolerance(w), name)
+    for n, ln in enumerate(lens):
+        if ln == 0:
+            assert torch.equal(gpu["dh0"][n], inp["dht"][n]), n
+
+
 @pytest.mark.parametrize("name", list(WIDE))
 def test_wide_sweep_tiles(name):
     w = WIDE[name]
